@@ -1,0 +1,192 @@
+/*
+ * Scalar CPU oracle for the BitNet b1.58 BitLinear layer.  TEST
+ * INFRASTRUCTURE ONLY: see oracle.h for who may load it, the method's source
+ * (transformers "BitNet" page, sections "Model details" and "BitNetConfig")
+ * and the packed format.
+ *
+ * Build: gcc -O2 -fno-tree-vectorize -ffp-contract=off -fPIC -shared
+ * (x86-64 SSE arithmetic: binary32 operations are correctly rounded and no
+ * multiply-add is fused).
+ */
+#include "oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* "Model details" / Quantization: weights are scaled by their absmean.
+ * The page does not fix the granularity; one scale per weight tensor. */
+float orc_absmean_scale(const float* W, int64_t N, int64_t K) {
+    double total = 0.0;
+    for (int64_t n = 0; n < N; ++n) {
+        double row = 0.0;
+        for (int64_t k = 0; k < K; ++k) row += fabs((double)W[n * K + k]);
+        total += row;
+    }
+    float mean = (float)(total / (double)(N * K));
+    /* floor keeps the divide below finite for an all-zero tensor */
+    if (!(mean >= 1e-5f)) mean = 1e-5f;
+    return mean;
+}
+
+/* "Model details" / Quantization: ternary {-1, 0, +1} from W / absmean,
+ * rounded to the nearest integer (ties to even) and clipped. */
+void orc_ternarize(const float* W, int64_t N, int64_t K, float gamma, int8_t* q) {
+    for (int64_t i = 0; i < N * K; ++i) {
+        float t = W[i] / gamma;
+        float r = rintf(t);
+        if (r > 1.0f) r = 1.0f;
+        if (r < -1.0f) r = -1.0f;
+        q[i] = (int8_t)r;
+    }
+}
+
+/* Position of weight k inside its row: byte 4*(k/16) + k%4, bit 2*((k/4)%4). */
+static int64_t packed_byte(int64_t k) { return 4 * (k / 16) + (k % 4); }
+static int packed_shift(int64_t k) { return (int)(2 * ((k / 4) % 4)); }
+
+int orc_pack(const int8_t* q, int64_t N, int64_t K, uint8_t* packed) {
+    if (K % 16 != 0) return -1;
+    const int64_t row_bytes = K / 4;
+    memset(packed, 0, (size_t)(N * row_bytes));
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t k = 0; k < K; ++k) {
+            int v = q[n * K + k];
+            if (v < -1 || v > 1) return -1;
+            unsigned code = (unsigned)(v + 1);
+            packed[n * row_bytes + packed_byte(k)] |= (uint8_t)(code << packed_shift(k));
+        }
+    }
+    return 0;
+}
+
+int orc_unpack(const uint8_t* packed, int64_t N, int64_t K, int8_t* q) {
+    if (K % 16 != 0) return -1;
+    const int64_t row_bytes = K / 4;
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t k = 0; k < K; ++k) {
+            unsigned code = (packed[n * row_bytes + packed_byte(k)] >> packed_shift(k)) & 3u;
+            if (code == 3u) return -1;
+            q[n * K + k] = (int8_t)((int)code - 1);
+        }
+    }
+    return 0;
+}
+
+/* "Model details" / Quantization: activations to 8-bit integers by absmax,
+ * one scale per token.  Range [-127, 127] so that the largest entry of every
+ * token maps to exactly +-127. */
+void orc_quant_act(const float* X, int64_t M, int64_t K,
+                   int8_t* xq, float* gamma_x, int32_t* rowsum) {
+    for (int64_t m = 0; m < M; ++m) {
+        const float* x = X + m * K;
+        float amax = 0.0f;
+        for (int64_t k = 0; k < K; ++k) {
+            float a = fabsf(x[k]);
+            if (a > amax) amax = a;
+        }
+        float g = amax;
+        if (!(g >= 1e-5f)) g = 1e-5f;
+        float s = 127.0f / g;
+        int32_t sum = 0;
+        for (int64_t k = 0; k < K; ++k) {
+            float r = rintf(x[k] * s);
+            if (r > 127.0f) r = 127.0f;
+            if (r < -127.0f) r = -127.0f;
+            xq[m * K + k] = (int8_t)r;
+            sum += (int32_t)r;
+        }
+        gamma_x[m] = g;
+        if (rowsum) rowsum[m] = sum;
+    }
+}
+
+/* "Model details": subln normalisation, no bias in normalisation layers;
+ * "BitNetConfig": rms_norm_eps.  Root-mean-square normalisation with a gain. */
+void orc_rmsnorm(const float* V, int64_t M, int64_t K, const float* gain,
+                 float eps, float* Z) {
+    for (int64_t m = 0; m < M; ++m) {
+        const float* v = V + m * K;
+        double ss = 0.0;
+        for (int64_t k = 0; k < K; ++k) ss += (double)v[k] * (double)v[k];
+        double ms = ss / (double)K;
+        float r = (float)(1.0 / sqrt(ms + (double)eps));
+        for (int64_t k = 0; k < K; ++k) {
+            float t = v[k] * r;
+            Z[m * K + k] = gain ? t * gain[k] : t;
+        }
+    }
+}
+
+/* W1.58A8 contraction: int8 activations times ternary weights, int32 sum. */
+void orc_int_matmul(const int8_t* xq, int64_t M, int64_t K,
+                    const int8_t* q, int64_t N, int32_t* acc) {
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t n = 0; n < N; ++n) {
+            int32_t s = 0;
+            for (int64_t k = 0; k < K; ++k)
+                s += (int32_t)xq[m * K + k] * (int32_t)q[n * K + k];
+            acc[m * N + n] = s;
+        }
+    }
+}
+
+/* Undo both scales: x ~ xq * gamma_x / 127 and w ~ q * gamma_w. */
+void orc_dequant(const int32_t* acc, int64_t M, int64_t N,
+                 const float* gamma_x, float gamma_w, float* Y) {
+    for (int64_t m = 0; m < M; ++m) {
+        float d = (gamma_x[m] * gamma_w) / 127.0f;
+        for (int64_t n = 0; n < N; ++n) Y[m * N + n] = (float)acc[m * N + n] * d;
+    }
+}
+
+/* "Model details": squared ReLU activation in the feed-forward layers. */
+void orc_relu2(float* Y, int64_t count) {
+    for (int64_t i = 0; i < count; ++i) {
+        float r = Y[i] > 0.0f ? Y[i] : 0.0f;
+        Y[i] = r * r;
+    }
+}
+
+void orc_add(float* H, const float* Y, int64_t count) {
+    for (int64_t i = 0; i < count; ++i) H[i] = H[i] + Y[i];
+}
+
+void orc_ffn_layer(float* H, int64_t M, int64_t Hd, int64_t F,
+                   const float* pre_gain, float pre_eps,
+                   const int8_t* q_up, float gamma_up,
+                   const float* sub_gain, float sub_eps,
+                   const int8_t* q_down, float gamma_down,
+                   int residual,
+                   float* y1_out, int8_t* xq2_out, float* g2_out) {
+    float* u = (float*)malloc(sizeof(float) * (size_t)(M * Hd));
+    int8_t* xq1 = (int8_t*)malloc((size_t)(M * Hd));
+    float* g1 = (float*)malloc(sizeof(float) * (size_t)M);
+    int32_t* acc1 = (int32_t*)malloc(sizeof(int32_t) * (size_t)(M * F));
+    float* y1 = (float*)malloc(sizeof(float) * (size_t)(M * F));
+    float* z = (float*)malloc(sizeof(float) * (size_t)(M * F));
+    int8_t* xq2 = (int8_t*)malloc((size_t)(M * F));
+    float* g2 = (float*)malloc(sizeof(float) * (size_t)M);
+    int32_t* acc2 = (int32_t*)malloc(sizeof(int32_t) * (size_t)(M * Hd));
+    float* y2 = (float*)malloc(sizeof(float) * (size_t)(M * Hd));
+
+    if (pre_gain) orc_rmsnorm(H, M, Hd, pre_gain, pre_eps, u);
+    else memcpy(u, H, sizeof(float) * (size_t)(M * Hd));
+    orc_quant_act(u, M, Hd, xq1, g1, NULL);
+    orc_int_matmul(xq1, M, Hd, q_up, F, acc1);
+    orc_dequant(acc1, M, F, g1, gamma_up, y1);
+    orc_relu2(y1, M * F);
+    orc_rmsnorm(y1, M, F, sub_gain, sub_eps, z);
+    orc_quant_act(z, M, F, xq2, g2, NULL);
+    orc_int_matmul(xq2, M, F, q_down, Hd, acc2);
+    orc_dequant(acc2, M, Hd, g2, gamma_down, y2);
+    if (residual) orc_add(H, y2, M * Hd);
+    else memcpy(H, y2, sizeof(float) * (size_t)(M * Hd));
+
+    if (y1_out) memcpy(y1_out, y1, sizeof(float) * (size_t)(M * F));
+    if (xq2_out) memcpy(xq2_out, xq2, (size_t)(M * F));
+    if (g2_out) memcpy(g2_out, g2, sizeof(float) * (size_t)M);
+
+    free(u); free(xq1); free(g1); free(acc1); free(y1);
+    free(z); free(xq2); free(g2); free(acc2); free(y2);
+}
