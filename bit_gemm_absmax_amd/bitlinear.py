@@ -1,0 +1,264 @@
+"""Python binding of libbitlinear (the C ABI in include/bitlinear.h).
+
+Argument marshalling only: every step of the BitLinear path runs in the HIP
+kernels of the library.  Tensors are torch CUDA (HIP) tensors; calls enqueue
+on torch's current stream and do not synchronise.  If the library is not
+built, every call raises :class:`BitLinearError`; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libbitlinear.so")
+
+BL_OK = 0
+BL_ERR_NULL = -1
+BL_ERR_SHAPE = -2
+BL_ERR_ALIGN = -3
+BL_ERR_WORKSPACE = -4
+BL_ERR_HIP = -5
+BL_ERR_UNSUPPORTED = -6
+
+BL_QUANT_RMSNORM = 0x1
+BL_EPI_RELU2 = 0x1
+BL_EPI_RESIDUAL = 0x2
+BL_EPI_SUBLN_QUANT = 0x4
+BL_FFN_PRE_NORM = 0x1
+BL_FFN_RESIDUAL = 0x2
+
+RMS_EPS = 1e-5  # rms_norm_eps of the BitNet config
+
+SYMBOLS = (
+    "bitlinear_status_string", "bitlinear_last_error", "bitlinear_abi_version",
+    "bitlinear_pack_workspace_bytes", "bitlinear_pack_weights", "bitlinear_quant_act",
+    "bitlinear_forward_workspace_bytes", "bitlinear_forward",
+    "bitnet_ffn_workspace_bytes", "bitnet_ffn_forward",
+)
+
+
+class BitLinearError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"[{status}] {message}")
+        self.status = status
+
+
+class Epilogue(ctypes.Structure):
+    _fields_ = [("flags", ctypes.c_uint32), ("residual", ctypes.c_void_p),
+                ("norm_gain", ctypes.c_void_p), ("norm_eps", ctypes.c_float),
+                ("out_q", ctypes.c_void_p), ("out_q_scale", ctypes.c_void_p),
+                ("out_q_rowsum", ctypes.c_void_p)]
+
+
+class FFNLayer(ctypes.Structure):
+    _fields_ = [("pre_norm_gain", ctypes.c_void_p), ("up", ctypes.c_void_p),
+                ("up_scale", ctypes.c_void_p), ("gate", ctypes.c_void_p),
+                ("gate_scale", ctypes.c_void_p), ("sub_norm_gain", ctypes.c_void_p),
+                ("down", ctypes.c_void_p), ("down_scale", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH):
+    """Load libbitlinear.so and declare its C signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise BitLinearError(BL_ERR_UNSUPPORTED,
+                             f"{path} is not built (python -m bit_gemm_absmax_amd.build)")
+    lib = ctypes.CDLL(path)
+    P, I64, U32, F, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint32, ctypes.c_float, ctypes.c_size_t
+    I = ctypes.c_int
+    lib.bitlinear_status_string.argtypes = [I]
+    lib.bitlinear_status_string.restype = ctypes.c_char_p
+    lib.bitlinear_last_error.argtypes = []
+    lib.bitlinear_last_error.restype = ctypes.c_char_p
+    lib.bitlinear_abi_version.argtypes = []
+    lib.bitlinear_abi_version.restype = I
+    lib.bitlinear_pack_workspace_bytes.argtypes = [I64, I64]
+    lib.bitlinear_pack_workspace_bytes.restype = SZ
+    lib.bitlinear_pack_weights.argtypes = [P, I64, I64, P, P, P, SZ, P]
+    lib.bitlinear_pack_weights.restype = I
+    lib.bitlinear_quant_act.argtypes = [P, I64, I64, U32, P, F, P, P, P, P]
+    lib.bitlinear_quant_act.restype = I
+    lib.bitlinear_forward_workspace_bytes.argtypes = [I64, I64, I64, U32]
+    lib.bitlinear_forward_workspace_bytes.restype = SZ
+    lib.bitlinear_forward.argtypes = [P, P, P, I64, I64, P, P, I64, ctypes.POINTER(Epilogue),
+                                      P, P, P, SZ, P]
+    lib.bitlinear_forward.restype = I
+    lib.bitnet_ffn_workspace_bytes.argtypes = [I64, I64, I64]
+    lib.bitnet_ffn_workspace_bytes.restype = SZ
+    lib.bitnet_ffn_forward.argtypes = [ctypes.POINTER(FFNLayer), ctypes.c_int32, P, I64, I64, I64,
+                                       U32, F, P, SZ, P]
+    lib.bitnet_ffn_forward.restype = I
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != BL_OK:
+        lib = load()
+        msg = lib.bitlinear_last_error().decode() or lib.bitlinear_status_string(status).decode()
+        raise BitLinearError(status, msg)
+
+
+def _p(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device=None):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t: torch.Tensor, dtype, ndim: int, name: str):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {t.dim()}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _workspace(nbytes: int, device) -> Optional[torch.Tensor]:
+    if nbytes == 0:
+        return None
+    return torch.empty(int(nbytes), dtype=torch.uint8, device=device)
+
+
+def pack_weights(W: torch.Tensor):
+    """Absmean-ternarise and pack fp32 W [N][K] -> (packed u8 [N][K/4], w_scale f32 [1])."""
+    lib = load()
+    _need(W, torch.float32, 2, "W")
+    N, K = W.shape
+    packed = torch.empty((N, K // 4), dtype=torch.uint8, device=W.device)
+    w_scale = torch.empty(1, dtype=torch.float32, device=W.device)
+    ws = _workspace(lib.bitlinear_pack_workspace_bytes(N, K), W.device)
+    _check(lib.bitlinear_pack_weights(_p(W), N, K, _p(packed), _p(w_scale), _p(ws),
+                                      0 if ws is None else ws.numel(), _stream(W.device)))
+    return packed, w_scale
+
+
+def quant_act(X: torch.Tensor, rmsnorm: bool = False, norm_gain: Optional[torch.Tensor] = None,
+              eps: float = RMS_EPS, out=None):
+    """Per-token absmax int8 of X [M][K] (optionally after RMSNorm) ->
+    (Xq int8 [M][K], x_scale f32 [M], x_rowsum i32 [M])."""
+    lib = load()
+    _need(X, torch.float32, 2, "X")
+    M, K = X.shape
+    if out is None:
+        out = (torch.empty((M, K), dtype=torch.int8, device=X.device),
+               torch.empty(M, dtype=torch.float32, device=X.device),
+               torch.empty(M, dtype=torch.int32, device=X.device))
+    xq, xs, rs = out
+    if norm_gain is not None:
+        _need(norm_gain, torch.float32, 1, "norm_gain")
+    _check(lib.bitlinear_quant_act(_p(X), M, K, BL_QUANT_RMSNORM if rmsnorm else 0, _p(norm_gain),
+                                   float(eps), _p(xq), _p(xs), _p(rs), _stream(X.device)))
+    return xq, xs, rs
+
+
+def forward(xq: torch.Tensor, x_scale: torch.Tensor, packed: torch.Tensor, w_scale: torch.Tensor,
+            x_rowsum: Optional[torch.Tensor] = None, relu2: bool = False,
+            residual: Optional[torch.Tensor] = None, subln: bool = False,
+            norm_gain: Optional[torch.Tensor] = None, eps: float = RMS_EPS,
+            want_y: bool = True, want_acc: bool = False, y_out: Optional[torch.Tensor] = None):
+    """BitLinear forward.  Returns a dict with the requested outputs:
+    'y' (f32 [M][N]), 'acc' (i32 [M][N]) and, with subln, 'q', 'q_scale', 'q_rowsum'."""
+    lib = load()
+    _need(xq, torch.int8, 2, "xq")
+    _need(packed, torch.uint8, 2, "packed")
+    M, K = xq.shape
+    N = packed.shape[0]
+    if packed.shape[1] * 4 != K:
+        raise ValueError(f"packed has {packed.shape[1]} bytes per row, expected K/4 = {K // 4}")
+    dev = xq.device
+    flags = 0
+    epi = Epilogue()
+    res = {}
+    if relu2:
+        flags |= BL_EPI_RELU2
+    if residual is not None:
+        _need(residual, torch.float32, 2, "residual")
+        flags |= BL_EPI_RESIDUAL
+        epi.residual = residual.data_ptr()
+    if subln:
+        flags |= BL_EPI_SUBLN_QUANT
+        res["q"] = torch.empty((M, N), dtype=torch.int8, device=dev)
+        res["q_scale"] = torch.empty(M, dtype=torch.float32, device=dev)
+        res["q_rowsum"] = torch.empty(M, dtype=torch.int32, device=dev)
+        epi.out_q = res["q"].data_ptr()
+        epi.out_q_scale = res["q_scale"].data_ptr()
+        epi.out_q_rowsum = res["q_rowsum"].data_ptr()
+        epi.norm_gain = None if norm_gain is None else norm_gain.data_ptr()
+        epi.norm_eps = float(eps)
+    epi.flags = flags
+    y = None
+    if want_y or not subln:
+        y = y_out if y_out is not None else torch.empty((M, N), dtype=torch.float32, device=dev)
+        res["y"] = y
+    acc = torch.empty((M, N), dtype=torch.int32, device=dev) if want_acc else None
+    if acc is not None:
+        res["acc"] = acc
+    ws = _workspace(lib.bitlinear_forward_workspace_bytes(M, K, N, flags), dev)
+    _check(lib.bitlinear_forward(_p(xq), _p(x_scale), _p(x_rowsum), M, K, _p(packed), _p(w_scale),
+                                 N, ctypes.byref(epi), _p(y), _p(acc), _p(ws),
+                                 0 if ws is None else ws.numel(), _stream(dev)))
+    return res
+
+
+def make_layers(layers: Sequence[dict]):
+    """Host array of FFN layer descriptors from dicts of device tensors
+    (keys: up, up_scale, down, down_scale, optional pre_norm_gain, sub_norm_gain)."""
+    arr = (FFNLayer * len(layers))()
+    for i, L in enumerate(layers):
+        arr[i].pre_norm_gain = None if L.get("pre_norm_gain") is None else L["pre_norm_gain"].data_ptr()
+        arr[i].up = L["up"].data_ptr()
+        arr[i].up_scale = L["up_scale"].data_ptr()
+        arr[i].gate = None if L.get("gate") is None else L["gate"].data_ptr()
+        arr[i].gate_scale = None if L.get("gate_scale") is None else L["gate_scale"].data_ptr()
+        arr[i].sub_norm_gain = None if L.get("sub_norm_gain") is None else L["sub_norm_gain"].data_ptr()
+        arr[i].down = L["down"].data_ptr()
+        arr[i].down_scale = L["down_scale"].data_ptr()
+    return arr
+
+
+class FFNStack:
+    """Reusable launcher for bitnet_ffn_forward: holds the layer descriptors
+    and a workspace sized for up to ``max_m`` tokens."""
+
+    def __init__(self, layers: Sequence[dict], H: int, F: int, max_m: int, device,
+                 pre_norm: bool = True, residual: bool = True, eps: float = RMS_EPS):
+        self.lib = load()
+        self._keep = list(layers)
+        self.arr = make_layers(layers)
+        self.n = len(layers)
+        self.H, self.F = H, F
+        self.flags = (BL_FFN_PRE_NORM if pre_norm else 0) | (BL_FFN_RESIDUAL if residual else 0)
+        self.eps = float(eps)
+        self.ws = _workspace(self.lib.bitnet_ffn_workspace_bytes(max_m, H, F), device)
+
+    def __call__(self, hidden: torch.Tensor) -> torch.Tensor:
+        _need(hidden, torch.float32, 2, "hidden")
+        M = hidden.shape[0]
+        _check(self.lib.bitnet_ffn_forward(self.arr, self.n, _p(hidden), M, self.H, self.F, self.flags,
+                                           self.eps, _p(self.ws), 0 if self.ws is None else self.ws.numel(),
+                                           _stream(hidden.device)))
+        return hidden
+
+
+def ffn_forward(layers: Sequence[dict], hidden: torch.Tensor, pre_norm: bool = True,
+                residual: bool = True, eps: float = RMS_EPS) -> torch.Tensor:
+    """Run the FFN stack in place on hidden [M][H]; returns hidden."""
+    M, H = hidden.shape
+    F = layers[0]["up"].shape[0] if layers else 64
+    return FFNStack(layers, H, F, max(M, 1), hidden.device, pre_norm, residual, eps)(hidden)

@@ -1,0 +1,55 @@
+// Internal declarations shared by the HIP translation units of libbitlinear.
+// Not part of the public ABI (include/bitlinear.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace bl {
+
+// Fused epilogue description handed to the contraction kernels by value.
+struct Epi {
+    uint32_t flags;          // BL_EPI_RELU2 | BL_EPI_RESIDUAL (SUBLN is host-side)
+    const float* residual;   // [M][N] or nullptr
+};
+
+constexpr uint32_t kEpiRelu2 = 0x1u;
+constexpr uint32_t kEpiResidual = 0x2u;
+
+// ---- launchers (return hipError_t of the launch) ----------------------------
+
+// Weight packing: partial binary64 sums of |W| into `partial` (count returned
+// by pack_partial_blocks), then ternarise + pack.
+int pack_partial_blocks(int64_t count);
+hipError_t launch_pack(const float* W, int64_t N, int64_t K, uint8_t* packed,
+                       float* w_scale, double* partial, hipStream_t s);
+
+// Per-row absmax quantisation with optional RMSNorm (gain may be null).
+hipError_t launch_quant(const float* X, int64_t M, int64_t K, bool rmsnorm,
+                        const float* gain, float eps, int8_t* Xq, float* scale,
+                        int32_t* rowsum, hipStream_t s);
+bool quant_supported(int64_t K);
+
+// rowsum[m] = sum_k Xq[m][k]
+hipError_t launch_rowsum(const int8_t* Xq, int64_t M, int64_t K, int32_t* rowsum,
+                         hipStream_t s);
+
+// Decode GEMV (v_dot4) for M <= 4.
+bool gemv_supported(int64_t M, int64_t K);
+hipError_t launch_gemv(const int8_t* Xq, const float* xs, const int32_t* rs, int64_t M,
+                       int64_t K, const uint8_t* packed, const float* ws, int64_t N, Epi epi,
+                       float* Y, int32_t* acc_out, hipStream_t s);
+
+// int8 MFMA GEMM for any M.
+hipError_t launch_gemm(const int8_t* Xq, const float* xs, const int32_t* rs, int64_t M,
+                       int64_t K, const uint8_t* packed, const float* ws, int64_t N, Epi epi,
+                       float* Y, int32_t* acc_out, hipStream_t s);
+
+// Contraction + dequant epilogue, choosing the kernel from M.  rowsum must be valid (not null).
+hipError_t launch_contract(const int8_t* Xq, const float* x_scale,
+                           const int32_t* rowsum, int64_t M, int64_t K,
+                           const uint8_t* packed, const float* w_scale, int64_t N,
+                           Epi epi, float* Y, int32_t* acc_out, hipStream_t s);
+
+}  // namespace bl

@@ -1,0 +1,107 @@
+// Weight packer: absmean ternarisation and 2-bit packing of latent fp32
+// weights (transformers "BitNet" page, "Model details" / Quantization:
+// ternary {-1, 0, +1} weights by absmean quantisation; "Model variants":
+// packed 1.58-bit weights for deployment).
+//
+// Two launches, both streaming W once from HBM:
+//   1. k_absmean_partial: each block sums |W| in binary64 over a grid-stride
+//      slice and writes one partial.
+//   2. k_ternary_pack: every block re-reduces the partials in the same fixed
+//      order (a few KB from L2, identical result in every block), forms
+//      gamma_w = max((float)(sum / (N*K)), 1e-5), and turns each group of 16
+//      weights into one 32-bit word of 2-bit codes.
+// The partial count depends only on N*K, so the binary64 summation order,
+// and hence gamma_w, is the same on every run.
+#include "bl_device.h"
+#include "bl_internal.h"
+
+namespace bl {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kMaxPartials = 1024;
+
+__global__ __launch_bounds__(kThreads) void k_absmean_partial(const float4* __restrict__ W,
+                                                              int64_t n4,
+                                                              double* __restrict__ partial) {
+    __shared__ double slot[kThreads / kWave];
+    double s = 0.0;
+    const int64_t stride = (int64_t)gridDim.x * kThreads;
+    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n4; i += stride) {
+        const float4 v = W[i];
+        s += fabs((double)v.x);
+        s += fabs((double)v.y);
+        s += fabs((double)v.z);
+        s += fabs((double)v.w);
+    }
+    s = block_sum<kThreads / kWave>(s, slot);
+    if (threadIdx.x == 0) partial[blockIdx.x] = s;
+}
+
+// code = clamp(rint(w / gamma), -1, 1) + 1, with one correctly rounded divide
+// and round-half-to-even (v_rndne_f32).
+__device__ __forceinline__ uint32_t ternary_code(float w, float gamma) {
+    float r = rintf(w / gamma);
+    r = r > 1.0f ? 1.0f : r;
+    r = r < -1.0f ? -1.0f : r;
+    return (uint32_t)((int)r + 1);
+}
+
+__global__ __launch_bounds__(kThreads) void k_ternary_pack(const float4* __restrict__ W,
+                                                           int64_t nwords,
+                                                           const double* __restrict__ partial,
+                                                           int nparts, double count,
+                                                           uint32_t* __restrict__ packed,
+                                                           float* __restrict__ w_scale) {
+    __shared__ double slot[kThreads / kWave];
+    double s = 0.0;
+    for (int i = threadIdx.x; i < nparts; i += kThreads) s += partial[i];
+    s = block_sum<kThreads / kWave>(s, slot);
+    float gamma = (float)(s / count);
+    if (!(gamma >= 1e-5f)) gamma = 1e-5f;
+    if (blockIdx.x == 0 && threadIdx.x == 0) *w_scale = gamma;
+
+    const int64_t stride = (int64_t)gridDim.x * kThreads;
+    for (int64_t w = (int64_t)blockIdx.x * kThreads + threadIdx.x; w < nwords; w += stride) {
+        float4 v[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[j] = W[4 * w + j];
+        uint32_t word = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            // float4 j holds weights 4j + b (b = 0..3) of the group: byte b, bits 2j.
+            word |= ternary_code(v[j].x, gamma) << (2 * j);
+            word |= ternary_code(v[j].y, gamma) << (8 + 2 * j);
+            word |= ternary_code(v[j].z, gamma) << (16 + 2 * j);
+            word |= ternary_code(v[j].w, gamma) << (24 + 2 * j);
+        }
+        packed[w] = word;
+    }
+}
+
+}  // namespace
+
+int pack_partial_blocks(int64_t count) {
+    const int64_t per_block = (int64_t)kThreads * 4 * 16;  // 16 float4 per thread
+    int64_t g = (count + per_block - 1) / per_block;
+    if (g < 1) g = 1;
+    if (g > kMaxPartials) g = kMaxPartials;
+    return (int)g;
+}
+
+hipError_t launch_pack(const float* W, int64_t N, int64_t K, uint8_t* packed,
+                       float* w_scale, double* partial, hipStream_t s) {
+    const int64_t count = N * K;
+    const int g = pack_partial_blocks(count);
+    hipLaunchKernelGGL(k_absmean_partial, dim3(g), dim3(kThreads), 0, s,
+                       reinterpret_cast<const float4*>(W), count / 4, partial);
+    const int64_t nwords = count / 16;
+    int64_t blocks = (nwords + kThreads - 1) / kThreads;
+    if (blocks > 8192) blocks = 8192;
+    hipLaunchKernelGGL(k_ternary_pack, dim3((unsigned)blocks), dim3(kThreads), 0, s,
+                       reinterpret_cast<const float4*>(W), nwords, partial, g,
+                       (double)count, reinterpret_cast<uint32_t*>(packed), w_scale);
+    return hipGetLastError();
+}
+
+}  // namespace bl

@@ -1,0 +1,219 @@
+/*
+ * bitlinear.h -- C ABI of the MI355X (gfx950) BitLinear W1.58A8 library.
+ *
+ * The layer is the one described on the transformers "BitNet" documentation
+ * page, section "Model details":
+ *   - Quantization: 1.58-bit weights and 8-bit activations (W1.58A8); weights
+ *     are made ternary {-1, 0, +1} by absmean quantisation, activations become
+ *     8-bit integers by per-token absmax quantisation.
+ *   - Architecture: BitLinear layers, squared ReLU (ReLU^2) in the feed-forward
+ *     layers, subln normalisation, no bias in linear or normalisation layers.
+ * Section "BitNetConfig" gives rms_norm_eps = 1e-05 and the model shapes
+ * (hidden 2560, intermediate 6912, 30 layers); section "Model variants" names
+ * packed 1.58-bit weights for deployment without giving a layout.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * Pointers.  Every array argument is a DEVICE pointer (hipMalloc'd or from a
+ * framework allocator) unless marked "host".  The caller owns all memory; no
+ * call allocates device memory.  Scratch comes from a caller-supplied
+ * workspace whose size the matching *_workspace_bytes() query returns.
+ *
+ * Layouts.  Row-major, no padding:
+ *   W       fp32 [N][K]     latent weights, out x in (y = x . W^T)
+ *   packed  u8   [N][K/4]   2-bit codes c = q + 1; inside a row, weights come
+ *                           in groups of 16 forming one little-endian 32-bit
+ *                           word; weight k = 16g + 4j + b is stored in byte
+ *                           4g + b at bits 2j..2j+1.  Code 3 never occurs.
+ *   X       fp32 [M][K]     activations, one row per token
+ *   Xq      int8 [M][K]     quantised activations, in [-127, 127]
+ *   Y       fp32 [M][N]     outputs
+ *
+ * Scales.  w_scale is one fp32 per weight tensor (the absmean, gamma_w);
+ * x_scale is one fp32 per token (the absmax, gamma_x).  Both are floored at
+ * 1e-5.  Dequantisation is y = acc * ((gamma_x * gamma_w) / 127).
+ *
+ * Shapes.  K must be a positive multiple of 64; N >= 1; M >= 0 (M == 0 is an
+ * empty batch: validated, then nothing is launched).  Limits: M*K, M*N and
+ * N*K below 2^31.
+ *
+ * Alignment.  W, X, Xq, packed, Y, acc and residual need 16-byte alignment;
+ * scale, rowsum and gain arrays need 4-byte alignment; the workspace needs
+ * 256-byte alignment.
+ *
+ * Streams.  Every call enqueues its kernels on the caller's stream and
+ * returns without synchronising.  Results are deterministic: the same inputs
+ * give bit-identical outputs on every run (no floating-point atomics).
+ *
+ * Errors.  Calls return BL_OK (0) or a negative bl_status.  Arguments are
+ * validated before anything is launched, so a rejected call has no effect.
+ * bitlinear_last_error() returns a thread-local message describing the last
+ * failure on the calling thread.  Non-finite inputs are outside the contract
+ * and are not checked.
+ */
+#ifndef BITLINEAR_H
+#define BITLINEAR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum bl_status {
+    BL_OK = 0,
+    BL_ERR_NULL = -1,        /* a required pointer is NULL */
+    BL_ERR_SHAPE = -2,       /* bad M, N or K (see Shapes) */
+    BL_ERR_ALIGN = -3,       /* a pointer is not aligned as required */
+    BL_ERR_WORKSPACE = -4,   /* workspace missing or smaller than required */
+    BL_ERR_HIP = -5,         /* HIP runtime reported an error (launch, device) */
+    BL_ERR_UNSUPPORTED = -6  /* valid request this build does not implement */
+};
+
+/* Static description of a status code (never NULL). */
+const char* bitlinear_status_string(int status);
+
+/* Thread-local description of the last failure on this thread ("" if none). */
+const char* bitlinear_last_error(void);
+
+/* ABI version of this header, (major << 16) | minor. */
+int bitlinear_abi_version(void);
+#define BITLINEAR_ABI_VERSION ((1 << 16) | 0)
+
+/* ------------------------------------------------------------------------
+ * Weight packing ("Model details" / Quantization: absmean ternary weights).
+ *
+ *   gamma_w   = max(mean_{n,k} |W[n][k]|, 1e-5)   one scale for the tensor;
+ *               the sum runs in binary64 and is rounded once to binary32
+ *   q[n][k]   = clamp(rint(W[n][k] / gamma_w), -1, 1)   (ties to even)
+ *   packed    = 2-bit codes q + 1 in the layout above
+ *
+ * W        in   fp32 [N][K]
+ * packed   out  u8 [N][K/4]
+ * w_scale  out  fp32 [1], gamma_w
+ * ws       scratch of bitlinear_pack_workspace_bytes(N, K) bytes
+ * Offline step: run once per weight tensor.
+ * ---------------------------------------------------------------------- */
+size_t bitlinear_pack_workspace_bytes(int64_t N, int64_t K);
+int bitlinear_pack_weights(const float* W, int64_t N, int64_t K,
+                           uint8_t* packed, float* w_scale,
+                           void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Activation quantisation ("Model details" / Quantization: per-token absmax
+ * 8-bit activations), optionally preceded by RMSNorm with a gain and no bias
+ * ("Model details" / Architecture; eps from "BitNetConfig").
+ *
+ * With BL_QUANT_RMSNORM in flags, each row is first normalised:
+ *   r = (float)(1 / sqrt(sum_k (double)x^2 / K + (double)norm_eps))
+ *   z = (x * r) * gain[k]           (gain NULL means all ones)
+ * and then, for each row (z = x without the flag):
+ *   gamma_x = max(max_k |z|, 1e-5);  s = 127 / gamma_x
+ *   Xq[k]   = clamp(rint(z[k] * s), -127, 127)      (ties to even)
+ *   rowsum  = sum_k Xq[k]
+ *
+ * X         in   fp32 [M][K]
+ * norm_gain in   fp32 [K] or NULL (ignored without BL_QUANT_RMSNORM)
+ * Xq        out  int8 [M][K]
+ * x_scale   out  fp32 [M], gamma_x
+ * x_rowsum  out  int32 [M], may be NULL
+ * ---------------------------------------------------------------------- */
+#define BL_QUANT_RMSNORM 0x1u
+int bitlinear_quant_act(const float* X, int64_t M, int64_t K, uint32_t flags,
+                        const float* norm_gain, float norm_eps,
+                        int8_t* Xq, float* x_scale, int32_t* x_rowsum,
+                        hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * BitLinear forward: the W1.58A8 contraction with int32 accumulation and the
+ * dequantising epilogue ("Model details" / Quantization), with optional fused
+ * squared ReLU, residual add and subln requantisation ("Model details" /
+ * Architecture).
+ *
+ *   acc[m][n] = sum_k Xq[m][k] * q[n][k]                  (exact int32)
+ *   y[m][n]   = (float)acc[m][n] * ((x_scale[m] * w_scale) / 127)
+ *   BL_EPI_RELU2:       y = max(y, 0)^2
+ *   BL_EPI_RESIDUAL:    y = y + residual[m][n]
+ *   BL_EPI_SUBLN_QUANT: out_q, out_q_scale, out_q_rowsum = the
+ *                       bitlinear_quant_act of y with BL_QUANT_RMSNORM,
+ *                       gain norm_gain (NULL = ones), eps norm_eps.
+ *
+ * Xq         in  int8 [M][K]
+ * x_scale    in  fp32 [M]
+ * x_rowsum   in  int32 [M] = sum_k Xq[m][k], or NULL (then computed inside)
+ * packed     in  u8 [N][K/4], from bitlinear_pack_weights
+ * w_scale    in  fp32 [1]
+ * epi        in  host pointer to a bl_epilogue, or NULL for plain dequant
+ * Y          out fp32 [M][N]; may be NULL only with BL_EPI_SUBLN_QUANT.
+ *                With BL_EPI_RESIDUAL, Y may equal residual (in place); any
+ *                other overlap between outputs and inputs is not allowed.
+ * acc_out    out int32 [M][N], the exact accumulators, or NULL
+ * ws         scratch of bitlinear_forward_workspace_bytes(M, K, N, flags)
+ * ---------------------------------------------------------------------- */
+#define BL_EPI_RELU2       0x1u
+#define BL_EPI_RESIDUAL    0x2u
+#define BL_EPI_SUBLN_QUANT 0x4u
+
+typedef struct bl_epilogue {
+    uint32_t flags;          /* BL_EPI_* bits */
+    const float* residual;   /* [M][N] for BL_EPI_RESIDUAL */
+    const float* norm_gain;  /* [N] or NULL (ones) for BL_EPI_SUBLN_QUANT */
+    float norm_eps;          /* RMSNorm eps for BL_EPI_SUBLN_QUANT (1e-5) */
+    int8_t* out_q;           /* [M][N] requantised output */
+    float* out_q_scale;      /* [M] its absmax scales */
+    int32_t* out_q_rowsum;   /* [M] its row sums, or NULL */
+} bl_epilogue;
+
+size_t bitlinear_forward_workspace_bytes(int64_t M, int64_t K, int64_t N,
+                                         uint32_t epi_flags);
+int bitlinear_forward(const int8_t* Xq, const float* x_scale,
+                      const int32_t* x_rowsum, int64_t M, int64_t K,
+                      const uint8_t* packed, const float* w_scale, int64_t N,
+                      const bl_epilogue* epi, float* Y, int32_t* acc_out,
+                      void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * BitNet feed-forward stack: for each layer in order, on hidden [M][H]
+ * ("Model details" / Architecture: BitLinear FFN with ReLU^2 and subln, no
+ * bias; "BitNetConfig": hidden 2560, intermediate 6912, 30 layers):
+ *
+ *   u  = BL_FFN_PRE_NORM ? RMSNorm(hidden; pre_norm_gain) : hidden
+ *   xq = absmax-quant(u)
+ *   y1 = ReLU^2(BitLinear(xq; up))                          [M][F]
+ *   x2 = absmax-quant(RMSNorm(y1; sub_norm_gain))           subln
+ *   y2 = BitLinear(x2; down)                                [M][H]
+ *   hidden = BL_FFN_RESIDUAL ? hidden + y2 : y2
+ *
+ * layers     in  host array of n_layers descriptors holding device pointers
+ * hidden     in/out fp32 [M][H]
+ * norm_eps   eps of both RMSNorms (1e-5)
+ * ws         scratch of bitnet_ffn_workspace_bytes(M, H, F)
+ * Gated blocks (gate != NULL) return BL_ERR_UNSUPPORTED.
+ * ---------------------------------------------------------------------- */
+#define BL_FFN_PRE_NORM 0x1u
+#define BL_FFN_RESIDUAL 0x2u
+
+typedef struct bitnet_ffn_layer {
+    const float* pre_norm_gain;  /* [H] or NULL (ones) */
+    const uint8_t* up;           /* [F][H/4] packed */
+    const float* up_scale;       /* [1] */
+    const uint8_t* gate;         /* must be NULL */
+    const float* gate_scale;     /* must be NULL */
+    const float* sub_norm_gain;  /* [F] or NULL (ones) */
+    const uint8_t* down;         /* [H][F/4] packed */
+    const float* down_scale;     /* [1] */
+} bitnet_ffn_layer;
+
+size_t bitnet_ffn_workspace_bytes(int64_t M, int64_t H, int64_t F);
+int bitnet_ffn_forward(const bitnet_ffn_layer* layers, int32_t n_layers,
+                       float* hidden, int64_t M, int64_t H, int64_t F,
+                       uint32_t flags, float norm_eps,
+                       void* ws, size_t ws_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* BITLINEAR_H */

@@ -1,0 +1,148 @@
+"""Host-side checks of the C ABI: the library loads, exports every function
+include/bitlinear.h declares, and rejects bad arguments before launching
+anything.  No call here reaches a kernel launch, so these run without a GPU."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from bit_gemm_absmax_amd import bitlinear as bl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bitlinear.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?[\s\*](\w+)\s*\(", text, flags=re.M)
+    return sorted(set(n for n in names if n.startswith(("bitlinear_", "bitnet_"))))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(bl.LIB_PATH):
+        from bit_gemm_absmax_amd import build
+        build.build()
+    return bl.load()
+
+
+def test_header_declares_the_four_calls():
+    names = declared_functions()
+    for n in ("bitlinear_pack_weights", "bitlinear_quant_act", "bitlinear_forward", "bitnet_ffn_forward"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", bl.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(re.findall(r" T (\w+)$", out, flags=re.M))
+    for name in declared_functions():
+        assert name in exported, name
+        assert getattr(lib, name) is not None
+    assert set(bl.SYMBOLS) == set(declared_functions())
+
+
+def test_version_and_status_strings(lib):
+    assert lib.bitlinear_abi_version() == (1 << 16)
+    for s in range(-6, 1):
+        assert lib.bitlinear_status_string(s)
+    assert lib.bitlinear_status_string(-99) == b"unknown status"
+
+
+def test_workspace_queries(lib):
+    assert lib.bitlinear_pack_workspace_bytes(6912, 2560) >= 8 * 1024
+    assert lib.bitlinear_pack_workspace_bytes(0, 64) == 0
+    assert lib.bitlinear_forward_workspace_bytes(4096, 2560, 6912, 0) >= 4096 * 4
+    with_y = lib.bitlinear_forward_workspace_bytes(4096, 2560, 6912, bl.BL_EPI_SUBLN_QUANT)
+    assert with_y >= 4096 * 6912 * 4
+    ffn = lib.bitnet_ffn_workspace_bytes(32, 2560, 6912)
+    assert ffn >= 32 * 2560 + 32 * 6912 * 5
+    assert lib.bitnet_ffn_workspace_bytes(0, 2560, 6912) == 0
+
+
+# Fake, aligned, never-dereferenced device addresses: every call below fails
+# validation (or has M == 0) before anything touches them.
+A = ctypes.c_void_p(1 << 20)
+B = ctypes.c_void_p(2 << 20)
+C = ctypes.c_void_p(3 << 20)
+D = ctypes.c_void_p(4 << 20)
+MIS = ctypes.c_void_p((5 << 20) + 4)
+
+
+def test_pack_validation(lib):
+    f = lib.bitlinear_pack_weights
+    assert f(None, 4, 64, B, C, D, 1 << 20, None) == bl.BL_ERR_NULL
+    assert b"required" in lib.bitlinear_last_error()
+    assert f(A, 0, 64, B, C, D, 1 << 20, None) == bl.BL_ERR_SHAPE
+    assert f(A, 4, 96, B, C, D, 1 << 20, None) == bl.BL_ERR_SHAPE
+    assert f(A, 4, 0, B, C, D, 1 << 20, None) == bl.BL_ERR_SHAPE
+    assert f(MIS, 4, 64, B, C, D, 1 << 20, None) == bl.BL_ERR_ALIGN
+    assert f(A, 4, 64, B, C, None, 0, None) == bl.BL_ERR_WORKSPACE
+    assert f(A, 4, 64, B, C, D, 16, None) == bl.BL_ERR_WORKSPACE
+    assert f(A, 4, 64, B, C, MIS, 1 << 20, None) == bl.BL_ERR_ALIGN
+
+
+def test_quant_validation(lib):
+    f = lib.bitlinear_quant_act
+    assert f(None, 1, 64, 0, None, 1e-5, B, C, D, None) == bl.BL_ERR_NULL
+    assert f(A, 1, 64, 0x8, None, 1e-5, B, C, D, None) == bl.BL_ERR_UNSUPPORTED
+    assert f(A, -1, 64, 0, None, 1e-5, B, C, D, None) == bl.BL_ERR_SHAPE
+    assert f(A, 1, 100, 0, None, 1e-5, B, C, D, None) == bl.BL_ERR_SHAPE
+    assert f(A, 1, 65536, 0, None, 1e-5, B, C, D, None) == bl.BL_ERR_UNSUPPORTED
+    assert f(MIS, 1, 64, 0, None, 1e-5, B, C, D, None) == bl.BL_ERR_ALIGN
+    # empty batch: validated, nothing launched
+    assert f(A, 0, 64, 0, None, 1e-5, B, C, D, None) == bl.BL_OK
+    assert lib.bitlinear_last_error() == b""
+
+
+def test_forward_validation(lib):
+    f = lib.bitlinear_forward
+    E = bl.Epilogue
+    nul = ctypes.POINTER(E)()
+    assert f(None, B, None, 1, 64, C, D, 8, nul, A, None, None, 0, None) == bl.BL_ERR_NULL
+    assert f(A, B, None, 1, 64, C, D, 8, nul, None, None, None, 0, None) == bl.BL_ERR_NULL
+    assert f(A, B, None, 1, 63, C, D, 8, nul, A, None, None, 0, None) == bl.BL_ERR_SHAPE
+    assert f(A, B, None, 1, 64, C, D, 0, nul, A, None, None, 0, None) == bl.BL_ERR_SHAPE
+    assert f(A, B, None, -2, 64, C, D, 8, nul, A, None, None, 0, None) == bl.BL_ERR_SHAPE
+    assert f(A, B, None, 1, 64, C, D, 8, nul, MIS, None, None, 0, None) == bl.BL_ERR_ALIGN
+    # missing workspace when the row sums must be computed
+    assert f(A, B, None, 1, 64, C, D, 8, nul, A, None, None, 0, None) == bl.BL_ERR_WORKSPACE
+    e = E(flags=bl.BL_EPI_RESIDUAL)
+    assert f(A, B, D, 1, 64, C, D, 8, ctypes.byref(e), A, None, None, 0, None) == bl.BL_ERR_NULL
+    e = E(flags=bl.BL_EPI_SUBLN_QUANT)
+    assert f(A, B, D, 1, 64, C, D, 64, ctypes.byref(e), A, None, None, 0, None) == bl.BL_ERR_NULL
+    e = E(flags=bl.BL_EPI_SUBLN_QUANT, out_q=A.value, out_q_scale=B.value)
+    assert f(A, B, D, 1, 64, C, D, 72, ctypes.byref(e), A, None, None, 0, None) == bl.BL_ERR_SHAPE
+    e = E(flags=0x40)
+    assert f(A, B, D, 1, 64, C, D, 8, ctypes.byref(e), A, None, None, 0, None) == bl.BL_ERR_UNSUPPORTED
+    # empty batch with everything else valid
+    assert f(A, B, D, 0, 64, C, D, 8, nul, A, None, None, 0, None) == bl.BL_OK
+
+
+def test_ffn_validation(lib):
+    f = lib.bitnet_ffn_forward
+    L = (bl.FFNLayer * 1)()
+    L[0].up, L[0].up_scale, L[0].down, L[0].down_scale = A.value, B.value, C.value, D.value
+    assert f(L, 1, None, 1, 64, 64, 3, 1e-5, None, 0, None) == bl.BL_ERR_NULL
+    assert f(None, 1, A, 1, 64, 64, 3, 1e-5, None, 0, None) == bl.BL_ERR_NULL
+    assert f(L, -1, A, 1, 64, 64, 3, 1e-5, None, 0, None) == bl.BL_ERR_SHAPE
+    assert f(L, 1, A, 1, 64, 96, 3, 1e-5, None, 0, None) == bl.BL_ERR_SHAPE
+    assert f(L, 1, A, 1, 64, 64, 0x10, 1e-5, None, 0, None) == bl.BL_ERR_UNSUPPORTED
+    assert f(L, 1, A, 1, 64, 64, 3, 1e-5, None, 0, None) == bl.BL_ERR_WORKSPACE
+    G = (bl.FFNLayer * 1)()
+    ctypes.memmove(G, L, ctypes.sizeof(L))
+    G[0].gate = A.value
+    assert f(G, 1, A, 1, 64, 64, 3, 1e-5, None, 0, None) == bl.BL_ERR_UNSUPPORTED
+    Z = (bl.FFNLayer * 1)()
+    assert f(Z, 1, A, 1, 64, 64, 3, 1e-5, None, 0, None) == bl.BL_ERR_NULL
+    assert f(L, 0, A, 1, 64, 64, 3, 1e-5, None, 0, None) == bl.BL_OK
+    assert f(L, 1, A, 0, 64, 64, 3, 1e-5, None, 0, None) == bl.BL_OK
+
+
+def test_binding_raises_on_bad_tensor():
+    import torch
+    with pytest.raises((ValueError, TypeError)):
+        bl.pack_weights(torch.zeros(4, 64))  # CPU tensor: rejected before any C call
