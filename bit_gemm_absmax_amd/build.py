@@ -59,6 +59,10 @@ def build(verbose: bool = False) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
+    # dlopen resolves every symbol now: a kernel whose host stub the
+    # compiler failed to emit shows up here instead of on the GPU machine.
+    import ctypes
+    ctypes.CDLL(tmp)
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB}")

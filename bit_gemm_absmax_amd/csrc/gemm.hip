@@ -2,14 +2,16 @@
 // (transformers "BitNet" page, "Model details" / Quantization: W1.58A8; with
 // thousands of tokens the product is a dense contraction).
 //
-// Tiling: a workgroup computes a BM x BN tile of acc with WM x WN waves, each
-// owning a (BM/WM) x (BN/WN) sub-tile of 16x16 MFMA fragments
-// (v_mfma_i32_16x16x64_i8).  Per k-step of 64:
-//   - the int8 activation tile [BM][64] goes HBM -> LDS;
-//   - the packed weight tile [BN][16 bytes] goes HBM -> LDS (4x smaller than
-//     int8), and each wave expands its own 32-bit words into int8 codes in
-//     registers: one shift + mask per 4 weights, producing 16 consecutive k
-//     in order, which is exactly a 16-byte MFMA operand.
+// Tiling.  A workgroup of WM x WN waves computes a BM x BN tile of acc; each
+// wave owns a (BM/WM) x (BN/WN) block of 16x16 fragments and issues
+// v_mfma_i32_16x16x64_i8, one per fragment pair and 64-k step.
+// Weights stay packed (2 bits) all the way into LDS, 4x less traffic than
+// int8; each wave expands its 32-bit words to int8 codes in registers: a
+// shift and a mask per 4 weights give 16 consecutive k in order, which is one
+// 16-byte MFMA operand, matching the 16 activation bytes of the same k.
+// Tile order is XCD-aware: workgroups are dealt round-robin to the 8 XCDs,
+// so consecutive tile indices are remapped to land on the same XCD and share
+// its L2.
 // The MFMA accumulates codes (q + 1); the epilogue subtracts the token's
 // activation row sum, dequantises and applies the fused ReLU^2 / residual.
 #include "bl_device.h"
@@ -20,29 +22,101 @@ namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 
-template <int BM, int BN, int WM, int WN>
-__global__ __launch_bounds__(WM* WN* kWave) void k_gemm(
+constexpr int kXcds = 8;
+
+// Pipeline: k advances 128 per stage and NBUF stages ring through LDS,
+// filled by direct global->LDS loads (global_load_lds_dwordx4) issued NBUF-1
+// stages ahead, so several stages of L2/HBM latency overlap the MFMAs.
+// A DMA instruction writes 64 lanes x 16 bytes contiguously; the global
+// address each lane fetches is chosen so that:
+//   - activations: one instruction covers 8 rows x 128 bytes (whole cache
+//     lines); inside a row the 16-byte chunk c lands at slot c ^ (row % 8),
+//     so the 16 rows of an MFMA fragment read at one k hit distinct banks;
+//   - weights: one instruction covers 32 rows x both 16-byte chunks of the
+//     stage, chunk-major, so a fragment read (word g of 16 rows) is one
+//     contiguous 256-byte span.
+// Rows past M or N are clamped to the last row for loading (never stored).
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8] left at max).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+template <int PER_STAGE, int MAXS>
+__device__ __forceinline__ void wait_stages(int n) {
+    // n stages (PER_STAGE loads each) may stay in flight; n <= MAXS
+    if constexpr (MAXS >= 3) if (n >= 3) { wait_vmcnt<3 * PER_STAGE>(); return; }
+    if constexpr (MAXS >= 2) if (n == 2) { wait_vmcnt<2 * PER_STAGE>(); return; }
+    if constexpr (MAXS >= 1) if (n == 1) { wait_vmcnt<1 * PER_STAGE>(); return; }
+    wait_vmcnt<0>();
+}
+
+constexpr int kBK = 128;             // k per stage
+constexpr int kAChunks = kBK / 16;   // 16-byte activation chunks per row per stage
+
+// Issue one stage of direct global->LDS loads for this wave.
+//   activations: A_BLKS instructions, block j = rows 8j..8j+7 of the tile;
+//   weights: one instruction, rows 32*wave..+31, both 64-k chunks.
+template <int A_BLKS>
+__device__ __forceinline__ void issue_stage(const int8_t* Xq, int M, int K, int m0, int lane, int wave,
+                                            const uint4* Wp, int N, int C, int n0, int8_t* base,
+                                            int a_stage, int st) {
+    const int r8 = lane >> 3;                  // row inside the 8-row block
+    const int chunk = (lane & 7) ^ r8;         // global chunk this lane fetches
+#pragma unroll
+    for (int i = 0; i < A_BLKS; ++i) {
+        const int blk = wave * A_BLKS + i;
+        int m = m0 + blk * 8 + r8;
+        m = m < M ? m : M - 1;
+        int k = st * kBK + chunk * 16;
+        k = k < K ? k : k - 64;                // K % 128 == 64: the unused half re-reads valid bytes
+        __builtin_amdgcn_global_load_lds(Xq + (int64_t)m * K + k, base + blk * 1024, 16, 0, 0);
+    }
+    int n = n0 + wave * 32 + (lane & 31);
+    n = n < N ? n : N - 1;
+    int kc = st * 2 + (lane >> 5);
+    kc = kc < C ? kc : C - 1;                  // K % 128 == 64: the last half stage repeats a chunk
+    __builtin_amdgcn_global_load_lds(Wp + (int64_t)n * C + kc, base + a_stage + wave * 1024, 16, 0, 0);
+}
+
+template <int BM, int BN, int WM, int WN, int NBUF>
+__global__ __launch_bounds__(WM* WN* kWave, 1) void k_gemm_pipe(
     const int8_t* __restrict__ Xq, const float* __restrict__ x_scale,
     const int32_t* __restrict__ rowsum, int M, int K, const uint4* __restrict__ Wp,
     const float* __restrict__ w_scale, int N, Epi epi, float* Y,
     int32_t* __restrict__ acc_out) {
-    constexpr int NT = WM * WN * kWave;
-    constexpr int TM = BM / WM;
-    constexpr int TN = BN / WN;
-    constexpr int FM = TM / 16;
-    constexpr int FN = TN / 16;
-    constexpr int APITCH = 80;  // bytes per LDS row of A: 64 + 16 to spread banks
-    __shared__ __align__(16) int8_t sA[BM * APITCH];
-    __shared__ __align__(16) uint32_t sB[BN * 4];
+    constexpr int NW = WM * WN;
+    constexpr int TM = BM / WM, TN = BN / WN, FM = TM / 16, FN = TN / 16;
+    constexpr int A_STAGE = BM * kBK;             // bytes
+    constexpr int B_STAGE = NW * 1024;            // bytes: 32 packed rows x 32 bytes per wave
+    constexpr int STAGE = A_STAGE + B_STAGE;
+    constexpr int A_BLKS = (BM / 8) / NW;         // 1 KB activation blocks per wave
+    constexpr int LOADS = A_BLKS + 1;             // DMA instructions per wave per stage
+    static_assert((BM / 8) % NW == 0, "activation blocks must split evenly over waves");
+    static_assert(BN <= NW * 32, "each wave loads 32 weight rows");
+    static_assert(TM % 16 == 0 && TN % 16 == 0, "whole fragments");
+    __shared__ __align__(1024) int8_t smem[NBUF * STAGE];
 
-    const int tid = threadIdx.x;
-    const int lane = tid % kWave;
-    const int wave = tid / kWave;
+    const int lane = threadIdx.x % kWave;
+    const int wave = threadIdx.x / kWave;
     const int wm = wave / WN;
     const int wn = wave % WN;
-    const int m0 = blockIdx.y * BM;
-    const int n0 = blockIdx.x * BN;
+
+    const int tiles_n = (N + BN - 1) / BN;
+    const int ntiles = gridDim.x;
+    const int b = blockIdx.x;
+    int t = b;
+    if (ntiles % kXcds == 0) t = (b % kXcds) * (ntiles / kXcds) + b / kXcds;
+    const int m0 = (t / tiles_n) * BM;
+    const int n0 = (t % tiles_n) * BN;
     const int C = K / 64;
+    const int nst = (K + kBK - 1) / kBK;
+
+    const int fr = lane & 15;
+    const int fg = lane >> 4;
 
     v4i acc[FM][FN];
 #pragma unroll
@@ -50,38 +124,50 @@ __global__ __launch_bounds__(WM* WN* kWave) void k_gemm(
 #pragma unroll
         for (int j = 0; j < FN; ++j) acc[i][j] = v4i{0, 0, 0, 0};
 
-    for (int kc = 0; kc < C; ++kc) {
-        for (int i = tid; i < BM * 4; i += NT) {
-            const int row = i / 4, c16 = i % 4;
-            const int m = m0 + row;
-            uint4 v = make_uint4(0u, 0u, 0u, 0u);
-            if (m < M) v = *reinterpret_cast<const uint4*>(Xq + (int64_t)m * K + kc * 64 + c16 * 16);
-            *reinterpret_cast<uint4*>(sA + row * APITCH + c16 * 16) = v;
-        }
-        for (int i = tid; i < BN; i += NT) {
-            const int n = n0 + i;
-            uint4 v = make_uint4(0u, 0u, 0u, 0u);
-            if (n < N) v = Wp[(int64_t)n * C + kc];
-            *reinterpret_cast<uint4*>(sB + i * 4) = v;
-        }
-        __syncthreads();
+    constexpr int P = NBUF - 1;
+#pragma unroll
+    for (int p = 0; p < P; ++p)
+        if (p < nst) issue_stage<A_BLKS>(Xq, M, K, m0, lane, wave, Wp, N, C, n0, smem + p * STAGE, A_STAGE, p);
 
-        v4i a[FM];
+    // a fragment row's activation bytes: row R, chunk c at R/8 block, slot c ^ (R % 8)
+    for (int st = 0; st < nst; ++st) {
+        const int ahead = nst - 1 - st;
+        wait_stages<LOADS, P - 1>(ahead < P - 1 ? ahead : P - 1);
+        // Execution barrier only: this wave's share of stage st is in LDS
+        // (vmcnt above), and after the barrier every wave's share is; a
+        // fenced __syncthreads would also drain the later stages' loads.
+        __builtin_amdgcn_s_barrier();
+        if (st + P < nst)
+            issue_stage<A_BLKS>(Xq, M, K, m0, lane, wave, Wp, N, C, n0, smem + ((st + P) % NBUF) * STAGE,
+                                A_STAGE, st + P);
+
+        const int8_t* sa = smem + (st % NBUF) * STAGE;
+        const uint32_t* sb = reinterpret_cast<const uint32_t*>(sa + A_STAGE);
+        const int ksteps = (st * kBK + 64 < K) ? 2 : 1;
 #pragma unroll
-        for (int fm = 0; fm < FM; ++fm) {
-            const int row = wm * TM + fm * 16 + (lane % 16);
-            a[fm] = *reinterpret_cast<const v4i*>(sA + row * APITCH + 16 * (lane / 16));
+        for (int s = 0; s < 2; ++s) {
+            if (s == 1 && ksteps == 1) break;
+            v4i a[FM];
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm) {
+                const int R = wm * TM + fm * 16 + fr;
+                const int slot = (4 * s + fg) ^ (R & 7);
+                a[fm] = *reinterpret_cast<const v4i*>(sa + (R >> 3) * 1024 + (R & 7) * 128 + slot * 16);
+            }
+            uint32_t wq[FN];
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn) {
+                const int col = wn * TN + fn * 16 + fr;
+                wq[fn] = sb[(col >> 5) * 256 + s * 128 + (col & 31) * 4 + fg];
+            }
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn) {
+                const v4i bv = v4i{codes4(wq[fn], 0), codes4(wq[fn], 1), codes4(wq[fn], 2), codes4(wq[fn], 3)};
+#pragma unroll
+                for (int fm = 0; fm < FM; ++fm)
+                    acc[fm][fn] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[fm], bv, acc[fm][fn], 0, 0, 0);
+            }
         }
-#pragma unroll
-        for (int fn = 0; fn < FN; ++fn) {
-            const int col = wn * TN + fn * 16 + (lane % 16);
-            const uint32_t w = sB[col * 4 + lane / 16];
-            const v4i b = v4i{codes4(w, 0), codes4(w, 1), codes4(w, 2), codes4(w, 3)};
-#pragma unroll
-            for (int fm = 0; fm < FM; ++fm)
-                acc[fm][fn] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[fm], b, acc[fm][fn], 0, 0, 0);
-        }
-        __syncthreads();
     }
 
     const float ws = *w_scale;
@@ -89,19 +175,19 @@ __global__ __launch_bounds__(WM* WN* kWave) void k_gemm(
     for (int fm = 0; fm < FM; ++fm) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int m = m0 + wm * TM + fm * 16 + 4 * (lane / 16) + r;
+            const int m = m0 + wm * TM + fm * 16 + 4 * fg + r;
             if (m >= M) continue;
             const int rsum = rowsum[m];
             const float d = (x_scale[m] * ws) / 127.0f;
 #pragma unroll
             for (int fn = 0; fn < FN; ++fn) {
-                const int n = n0 + wn * TN + fn * 16 + (lane % 16);
+                const int n = n0 + wn * TN + fn * 16 + fr;
                 if (n >= N) continue;
                 const int av = acc[fm][fn][r] - rsum;
                 float y = (float)av * d;
                 if (epi.flags & kEpiRelu2) {
-                    const float t = y > 0.0f ? y : 0.0f;
-                    y = t * t;
+                    const float tt = y > 0.0f ? y : 0.0f;
+                    y = tt * tt;
                 }
                 const int64_t o = (int64_t)m * N + n;
                 if (epi.flags & kEpiResidual) y = y + epi.residual[o];
@@ -112,16 +198,31 @@ __global__ __launch_bounds__(WM* WN* kWave) void k_gemm(
     }
 }
 
+template <int BM, int BN, int WM, int WN, int NBUF>
+hipError_t launch_pipe(const int8_t* Xq, const float* xs, const int32_t* rs, int64_t M, int64_t K,
+                       const uint8_t* packed, const float* ws, int64_t N, Epi epi, float* Y,
+                       int32_t* acc_out, hipStream_t s) {
+    const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+    hipLaunchKernelGGL((k_gemm_pipe<BM, BN, WM, WN, NBUF>), dim3((unsigned)tiles), dim3(WM * WN * kWave),
+                       0, s, Xq, xs, rs, (int)M, (int)K, reinterpret_cast<const uint4*>(packed), ws,
+                       (int)N, epi, Y, acc_out);
+    return hipGetLastError();
+}
+
 }  // namespace
 
+// Tile choice: 256-row tiles with 256 columns, or 160 columns when N is a
+// multiple of 160 and not of 256 (2560 -> 16 tiles of 160, one per CU row of
+// work); 128-row tiles for mid-size M.
 hipError_t launch_gemm(const int8_t* Xq, const float* xs, const int32_t* rs, int64_t M, int64_t K,
                        const uint8_t* packed, const float* ws, int64_t N, Epi epi, float* Y,
                        int32_t* acc_out, hipStream_t s) {
-    constexpr int BM = 128, BN = 128;
-    const dim3 grid((unsigned)((N + BN - 1) / BN), (unsigned)((M + BM - 1) / BM));
-    hipLaunchKernelGGL((k_gemm<BM, BN, 2, 2>), grid, dim3(256), 0, s, Xq, xs, rs, (int)M, (int)K,
-                       reinterpret_cast<const uint4*>(packed), ws, (int)N, epi, Y, acc_out);
-    return hipGetLastError();
+    if (M > 128) {
+        if (N % 256 != 0 && N % 160 == 0)
+            return launch_pipe<256, 160, 4, 2, 3>(Xq, xs, rs, M, K, packed, ws, N, epi, Y, acc_out, s);
+        return launch_pipe<256, 256, 4, 2, 3>(Xq, xs, rs, M, K, packed, ws, N, epi, Y, acc_out, s);
+    }
+    return launch_pipe<128, 128, 2, 2, 3>(Xq, xs, rs, M, K, packed, ws, N, epi, Y, acc_out, s);
 }
 
 hipError_t launch_contract(const int8_t* Xq, const float* x_scale, const int32_t* rowsum,

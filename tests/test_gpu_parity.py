@@ -114,7 +114,7 @@ def run_forward(X, W, **kw):
 
 
 @pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 8, 17, 64, 130])
-@pytest.mark.parametrize("K,N", [(256, 512), (192, 100), (2560, 200), (6912, 72)])
+@pytest.mark.parametrize("K,N", [(256, 512), (192, 100), (2560, 200), (6912, 72), (64, 96), (128, 130), (320, 160)])
 def test_forward_small(M, K, N):
     log(f"[forward] M={M} K={K} N={N}")
     rng = np.random.default_rng(M * 31 + K + N)
