@@ -37,21 +37,22 @@ constexpr int kXcds = 8;
 //     contiguous 256-byte span.
 // Rows past M or N are clamped to the last row for loading (never stored).
 
-// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
-// vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8] left at max).
+// s_waitcnt on the vector-memory counter (at most N loads in flight) and
+// the LDS counter (all LDS reads returned); gfx9 encoding: vmcnt bits [3:0]
+// and [15:14], expcnt [6:4] left at max, lgkmcnt [11:8] = 0.
 template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
+__device__ __forceinline__ void wait_vm_lgkm0() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4));
 }
 
 template <int PER_STAGE, int MAXS>
 __device__ __forceinline__ void wait_stages(int n) {
     // n stages (PER_STAGE loads each) may stay in flight; n <= MAXS
-    if constexpr (MAXS >= 3) if (n >= 3) { wait_vmcnt<3 * PER_STAGE>(); return; }
-    if constexpr (MAXS >= 2) if (n == 2) { wait_vmcnt<2 * PER_STAGE>(); return; }
-    if constexpr (MAXS >= 1) if (n == 1) { wait_vmcnt<1 * PER_STAGE>(); return; }
-    wait_vmcnt<0>();
+    if constexpr (MAXS >= 3) if (n >= 3) { wait_vm_lgkm0<3 * PER_STAGE>(); return; }
+    if constexpr (MAXS >= 2) if (n == 2) { wait_vm_lgkm0<2 * PER_STAGE>(); return; }
+    if constexpr (MAXS >= 1) if (n == 1) { wait_vm_lgkm0<1 * PER_STAGE>(); return; }
+    wait_vm_lgkm0<0>();
 }
 
 constexpr int kBK = 128;             // k per stage
@@ -59,8 +60,8 @@ constexpr int kAChunks = kBK / 16;   // 16-byte activation chunks per row per st
 
 // Issue one stage of direct global->LDS loads for this wave.
 //   activations: A_BLKS instructions, block j = rows 8j..8j+7 of the tile;
-//   weights: one instruction, rows 32*wave..+31, both 64-k chunks.
-template <int A_BLKS>
+//   weights: B_INS instructions, each 32 rows x both 64-k chunks.
+template <int A_BLKS, int B_INS>
 __device__ __forceinline__ void issue_stage(const int8_t* Xq, int M, int K, int m0, int lane, int wave,
                                             const uint4* Wp, int N, int C, int n0, int8_t* base,
                                             int a_stage, int st) {
@@ -75,15 +76,19 @@ __device__ __forceinline__ void issue_stage(const int8_t* Xq, int M, int K, int 
         k = k < K ? k : k - 64;                // K % 128 == 64: the unused half re-reads valid bytes
         __builtin_amdgcn_global_load_lds(Xq + (int64_t)m * K + k, base + blk * 1024, 16, 0, 0);
     }
-    int n = n0 + wave * 32 + (lane & 31);
-    n = n < N ? n : N - 1;
     int kc = st * 2 + (lane >> 5);
     kc = kc < C ? kc : C - 1;                  // K % 128 == 64: the last half stage repeats a chunk
-    __builtin_amdgcn_global_load_lds(Wp + (int64_t)n * C + kc, base + a_stage + wave * 1024, 16, 0, 0);
+#pragma unroll
+    for (int i = 0; i < B_INS; ++i) {
+        const int blk = wave * B_INS + i;
+        int n = n0 + blk * 32 + (lane & 31);
+        n = n < N ? n : N - 1;
+        __builtin_amdgcn_global_load_lds(Wp + (int64_t)n * C + kc, base + a_stage + blk * 1024, 16, 0, 0);
+    }
 }
 
-template <int BM, int BN, int WM, int WN, int NBUF>
-__global__ __launch_bounds__(WM* WN* kWave, 1) void k_gemm_pipe(
+template <int BM, int BN, int WM, int WN, int NBUF, int OCC>
+__global__ __launch_bounds__(WM* WN* kWave, OCC) void k_gemm_pipe(
     const int8_t* __restrict__ Xq, const float* __restrict__ x_scale,
     const int32_t* __restrict__ rowsum, int M, int K, const uint4* __restrict__ Wp,
     const float* __restrict__ w_scale, int N, Epi epi, float* Y,
@@ -91,12 +96,12 @@ __global__ __launch_bounds__(WM* WN* kWave, 1) void k_gemm_pipe(
     constexpr int NW = WM * WN;
     constexpr int TM = BM / WM, TN = BN / WN, FM = TM / 16, FN = TN / 16;
     constexpr int A_STAGE = BM * kBK;             // bytes
-    constexpr int B_STAGE = NW * 1024;            // bytes: 32 packed rows x 32 bytes per wave
+    constexpr int B_INS = (BN + 32 * NW - 1) / (32 * NW);  // weight DMAs per wave (32 rows each)
+    constexpr int B_STAGE = B_INS * NW * 1024;    // bytes: 32 packed rows x 32 bytes per DMA
     constexpr int STAGE = A_STAGE + B_STAGE;
     constexpr int A_BLKS = (BM / 8) / NW;         // 1 KB activation blocks per wave
-    constexpr int LOADS = A_BLKS + 1;             // DMA instructions per wave per stage
+    constexpr int LOADS = A_BLKS + B_INS;         // DMA instructions per wave per stage
     static_assert((BM / 8) % NW == 0, "activation blocks must split evenly over waves");
-    static_assert(BN <= NW * 32, "each wave loads 32 weight rows");
     static_assert(TM % 16 == 0 && TN % 16 == 0, "whole fragments");
     __shared__ __align__(1024) int8_t smem[NBUF * STAGE];
 
@@ -118,6 +123,23 @@ __global__ __launch_bounds__(WM* WN* kWave, 1) void k_gemm_pipe(
     const int fr = lane & 15;
     const int fg = lane >> 4;
 
+    // Epilogue operands, loaded now so their latency hides under the main
+    // loop: lane l holds rows (wave row 0 + 64 h + l)'s row sum and dequant
+    // factor; the epilogue fetches them per row with a cross-lane read.
+    constexpr int RPL = (TM + kWave - 1) / kWave;
+    int row_rs[RPL];
+    float row_d[RPL];
+    {
+        const float wsc = *w_scale;
+#pragma unroll
+        for (int h = 0; h < RPL; ++h) {
+            int m = m0 + wm * TM + h * kWave + lane;
+            m = m < M ? m : M - 1;
+            row_rs[h] = rowsum[m];
+            row_d[h] = (x_scale[m] * wsc) / 127.0f;
+        }
+    }
+
     v4i acc[FM][FN];
 #pragma unroll
     for (int i = 0; i < FM; ++i)
@@ -127,83 +149,159 @@ __global__ __launch_bounds__(WM* WN* kWave, 1) void k_gemm_pipe(
     constexpr int P = NBUF - 1;
 #pragma unroll
     for (int p = 0; p < P; ++p)
-        if (p < nst) issue_stage<A_BLKS>(Xq, M, K, m0, lane, wave, Wp, N, C, n0, smem + p * STAGE, A_STAGE, p);
+        if (p < nst) issue_stage<A_BLKS, B_INS>(Xq, M, K, m0, lane, wave, Wp, N, C, n0, smem + p * STAGE, A_STAGE, p);
 
-    // a fragment row's activation bytes: row R, chunk c at R/8 block, slot c ^ (R % 8)
-    for (int st = 0; st < nst; ++st) {
-        const int ahead = nst - 1 - st;
-        wait_stages<LOADS, P - 1>(ahead < P - 1 ? ahead : P - 1);
-        // Execution barrier only: this wave's share of stage st is in LDS
-        // (vmcnt above), and after the barrier every wave's share is; a
-        // fenced __syncthreads would also drain the later stages' loads.
-        __builtin_amdgcn_s_barrier();
-        if (st + P < nst)
-            issue_stage<A_BLKS>(Xq, M, K, m0, lane, wave, Wp, N, C, n0, smem + ((st + P) % NBUF) * STAGE,
-                                A_STAGE, st + P);
-
+    // Fragments of one 64-k step: activation rows R (block R/8, slot
+    // (4s + fg) ^ (R % 8)) and the packed weight word g of 16 rows.
+    auto load_frags = [&](int st, int s, v4i (&a)[FM], uint32_t (&wq)[FN]) {
         const int8_t* sa = smem + (st % NBUF) * STAGE;
         const uint32_t* sb = reinterpret_cast<const uint32_t*>(sa + A_STAGE);
-        const int ksteps = (st * kBK + 64 < K) ? 2 : 1;
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            if (s == 1 && ksteps == 1) break;
-            v4i a[FM];
+        for (int fm = 0; fm < FM; ++fm) {
+            const int R = wm * TM + fm * 16 + fr;
+            const int slot = (4 * s + fg) ^ (R & 7);
+            a[fm] = *reinterpret_cast<const v4i*>(sa + (R >> 3) * 1024 + (R & 7) * 128 + slot * 16);
+        }
 #pragma unroll
-            for (int fm = 0; fm < FM; ++fm) {
-                const int R = wm * TM + fm * 16 + fr;
-                const int slot = (4 * s + fg) ^ (R & 7);
-                a[fm] = *reinterpret_cast<const v4i*>(sa + (R >> 3) * 1024 + (R & 7) * 128 + slot * 16);
-            }
-            uint32_t wq[FN];
+        for (int fn = 0; fn < FN; ++fn) {
+            const int col = wn * TN + fn * 16 + fr;
+            wq[fn] = sb[(col >> 5) * 256 + s * 128 + (col & 31) * 4 + fg];
+        }
+    };
+    auto mma = [&](const v4i (&a)[FM], const uint32_t (&wq)[FN]) {
 #pragma unroll
-            for (int fn = 0; fn < FN; ++fn) {
-                const int col = wn * TN + fn * 16 + fr;
-                wq[fn] = sb[(col >> 5) * 256 + s * 128 + (col & 31) * 4 + fg];
-            }
+        for (int fn = 0; fn < FN; ++fn) {
+            const v4i bv = v4i{codes4(wq[fn], 0), codes4(wq[fn], 1), codes4(wq[fn], 2), codes4(wq[fn], 3)};
 #pragma unroll
-            for (int fn = 0; fn < FN; ++fn) {
-                const v4i bv = v4i{codes4(wq[fn], 0), codes4(wq[fn], 1), codes4(wq[fn], 2), codes4(wq[fn], 3)};
+            for (int fm = 0; fm < FM; ++fm)
+                acc[fm][fn] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[fm], bv, acc[fm][fn], 0, 0, 0);
+        }
+    };
+    // Stage st is ready in LDS for every wave: this wave's loads have landed
+    // (vmcnt) and the execution barrier waits for the others.  The same wait
+    // drains this wave's LDS reads, so once all waves pass the barrier no
+    // read of the previous stage's buffer is pending and the DMA issued right
+    // after may overwrite it.
+    auto stage_ready = [&](int st) {
+        const int ahead = nst - 1 - st;
+        wait_stages<LOADS, P - 1>(ahead < P - 1 ? ahead : P - 1);
+        __builtin_amdgcn_s_barrier();
+    };
+
+    // Full stages: both 64-k steps, branch-free, so the second step's
+    // fragment reads are in flight while the first step's MFMAs run.  The
+    // last stage is peeled (it may hold a single 64-k step).
+    for (int st = 0; st + 1 < nst; ++st) {
+        stage_ready(st);
+        if (st + P < nst)
+            issue_stage<A_BLKS, B_INS>(Xq, M, K, m0, lane, wave, Wp, N, C, n0,
+                                       smem + ((st + P) % NBUF) * STAGE, A_STAGE, st + P);
+        v4i a0[FM], a1[FM];
+        uint32_t w0[FN], w1[FN];
+        load_frags(st, 0, a0, w0);
+        __builtin_amdgcn_sched_barrier(0);
+        // second step's reads ride inside the first step's MFMA stream:
+        // per weight fragment, its unpack, then MFMAs with reads between
+        load_frags(st, 1, a1, w1);
+        mma(a0, w0);
 #pragma unroll
-                for (int fm = 0; fm < FM; ++fm)
-                    acc[fm][fn] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[fm], bv, acc[fm][fn], 0, 0, 0);
-            }
+        for (int g = 0; g < FN; ++g) {
+            __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);   // VALU: unpack
+            __builtin_amdgcn_sched_group_barrier(0x008, FM / 2, 0);  // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, (FM + FN + FN - 1) / FN, 0);  // DS read
+            __builtin_amdgcn_sched_group_barrier(0x008, FM - FM / 2, 0);  // MFMA
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        mma(a1, w1);
+    }
+    {
+        const int st = nst - 1;
+        stage_ready(st);
+        v4i a[FM];
+        uint32_t w[FN];
+        load_frags(st, 0, a, w);
+        mma(a, w);
+        if (st * kBK + 64 < K) {
+            load_frags(st, 1, a, w);
+            mma(a, w);
         }
     }
 
-    const float ws = *w_scale;
+    // Epilogue.  acc holds 4 consecutive rows of one column per lane, so
+    // direct stores would write 64-byte pieces of 4 rows.  Instead each wave
+    // stages 16 rows x TN of finished values (dequant, ReLU^2) in LDS, with a
+    // row pitch of TN + 4 floats (the minimum, 2-way, conflict for the
+    // 64-lane writes), then writes whole rows with 16-byte stores, adding the
+    // residual there.  The main loop's buffers are free after the barrier.
+    __syncthreads();
+    constexpr int PITCH = TN + 4;
+    float* stage = reinterpret_cast<float*>(smem) + wave * 16 * PITCH;
+    static_assert(NW * 16 * PITCH * 4 <= NBUF * STAGE, "epilogue staging fits the LDS ring");
+    static_assert(TN % 4 == 0, "16-byte row stores");
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int m = m0 + wm * TM + fm * 16 + 4 * fg + r;
-            if (m >= M) continue;
-            const int rsum = rowsum[m];
-            const float d = (x_scale[m] * ws) / 127.0f;
+            const int ri = fm * 16 + 4 * fg + r;     // row inside the wave tile
+            const int m = m0 + wm * TM + ri;
+            const int rsum = __shfl(row_rs[fm / 4], ri % kWave, kWave);
+            const float d = __shfl(row_d[fm / 4], ri % kWave, kWave);
 #pragma unroll
             for (int fn = 0; fn < FN; ++fn) {
-                const int n = n0 + wn * TN + fn * 16 + fr;
-                if (n >= N) continue;
                 const int av = acc[fm][fn][r] - rsum;
                 float y = (float)av * d;
                 if (epi.flags & kEpiRelu2) {
                     const float tt = y > 0.0f ? y : 0.0f;
                     y = tt * tt;
                 }
-                const int64_t o = (int64_t)m * N + n;
-                if (epi.flags & kEpiResidual) y = y + epi.residual[o];
-                if (Y != nullptr) Y[o] = y;
-                if (acc_out != nullptr) acc_out[o] = av;
+                stage[(4 * fg + r) * PITCH + fn * 16 + fr] = y;
+                const int n = n0 + wn * TN + fn * 16 + fr;
+                if (acc_out != nullptr && m < M && n < N) acc_out[(int64_t)m * N + n] = av;
             }
         }
+        // the wave reads back only its own rows: no workgroup barrier needed,
+        // the LDS counter orders this wave's writes before its reads
+        constexpr int VPR = TN / 4;                  // 16-byte vectors per row
+#pragma unroll
+        for (int i = lane; i < 16 * VPR; i += kWave) {
+            const int rr = i / VPR, cv = i % VPR;
+            const int m = m0 + wm * TM + fm * 16 + rr;
+            const int n = n0 + wn * TN + cv * 4;
+            float4 v = *reinterpret_cast<const float4*>(&stage[rr * PITCH + cv * 4]);
+            if (m < M && Y != nullptr) {
+                const int64_t o = (int64_t)m * N + n;
+                if (n + 3 < N && (N % 4) == 0) {
+                    if (epi.flags & kEpiResidual) {
+                        const float4 res = *reinterpret_cast<const float4*>(epi.residual + o);
+                        v.x = v.x + res.x;
+                        v.y = v.y + res.y;
+                        v.z = v.z + res.z;
+                        v.w = v.w + res.w;
+                    }
+                    *reinterpret_cast<float4*>(Y + o) = v;
+                } else {
+                    const float e[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        if (n + q < N) {
+                            float yq = e[q];
+                            if (epi.flags & kEpiResidual) yq = yq + epi.residual[o + q];
+                            Y[o + q] = yq;
+                        }
+                    }
+                }
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(0xC07F);          // lgkmcnt(0): reads done before the next fm reuses the rows
     }
 }
 
-template <int BM, int BN, int WM, int WN, int NBUF>
+template <int BM, int BN, int WM, int WN, int NBUF, int OCC>
 hipError_t launch_pipe(const int8_t* Xq, const float* xs, const int32_t* rs, int64_t M, int64_t K,
                        const uint8_t* packed, const float* ws, int64_t N, Epi epi, float* Y,
                        int32_t* acc_out, hipStream_t s) {
     const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-    hipLaunchKernelGGL((k_gemm_pipe<BM, BN, WM, WN, NBUF>), dim3((unsigned)tiles), dim3(WM * WN * kWave),
+    hipLaunchKernelGGL((k_gemm_pipe<BM, BN, WM, WN, NBUF, OCC>), dim3((unsigned)tiles), dim3(WM * WN * kWave),
                        0, s, Xq, xs, rs, (int)M, (int)K, reinterpret_cast<const uint4*>(packed), ws,
                        (int)N, epi, Y, acc_out);
     return hipGetLastError();
@@ -219,10 +317,10 @@ hipError_t launch_gemm(const int8_t* Xq, const float* xs, const int32_t* rs, int
                        int32_t* acc_out, hipStream_t s) {
     if (M > 128) {
         if (N % 256 != 0 && N % 160 == 0)
-            return launch_pipe<256, 160, 4, 2, 3>(Xq, xs, rs, M, K, packed, ws, N, epi, Y, acc_out, s);
-        return launch_pipe<256, 256, 4, 2, 3>(Xq, xs, rs, M, K, packed, ws, N, epi, Y, acc_out, s);
+            return launch_pipe<256, 160, 4, 2, 3, 1>(Xq, xs, rs, M, K, packed, ws, N, epi, Y, acc_out, s);
+        return launch_pipe<256, 256, 4, 2, 3, 1>(Xq, xs, rs, M, K, packed, ws, N, epi, Y, acc_out, s);
     }
-    return launch_pipe<128, 128, 2, 2, 3>(Xq, xs, rs, M, K, packed, ws, N, epi, Y, acc_out, s);
+    return launch_pipe<128, 128, 2, 2, 3, 1>(Xq, xs, rs, M, K, packed, ws, N, epi, Y, acc_out, s);
 }
 
 hipError_t launch_contract(const int8_t* Xq, const float* x_scale, const int32_t* rowsum,
