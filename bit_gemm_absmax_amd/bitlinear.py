@@ -37,6 +37,7 @@ SYMBOLS = (
     "bitlinear_status_string", "bitlinear_last_error", "bitlinear_abi_version",
     "bitlinear_pack_workspace_bytes", "bitlinear_pack_weights", "bitlinear_quant_act",
     "bitlinear_forward_workspace_bytes", "bitlinear_forward",
+    "bitlinear_quant_forward_workspace_bytes", "bitlinear_quant_forward",
     "bitnet_ffn_workspace_bytes", "bitnet_ffn_forward",
 )
 
@@ -92,6 +93,11 @@ def load(path: str = LIB_PATH):
     lib.bitlinear_forward.argtypes = [P, P, P, I64, I64, P, P, I64, ctypes.POINTER(Epilogue),
                                       P, P, P, SZ, P]
     lib.bitlinear_forward.restype = I
+    lib.bitlinear_quant_forward_workspace_bytes.argtypes = [I64, I64, I64]
+    lib.bitlinear_quant_forward_workspace_bytes.restype = SZ
+    lib.bitlinear_quant_forward.argtypes = [P, I64, I64, U32, P, F, P, P, I64, ctypes.POINTER(Epilogue),
+                                            P, P, SZ, P]
+    lib.bitlinear_quant_forward.restype = I
     lib.bitnet_ffn_workspace_bytes.argtypes = [I64, I64, I64]
     lib.bitnet_ffn_workspace_bytes.restype = SZ
     lib.bitnet_ffn_forward.argtypes = [ctypes.POINTER(FFNLayer), ctypes.c_int32, P, I64, I64, I64,
@@ -216,6 +222,44 @@ def forward(xq: torch.Tensor, x_scale: torch.Tensor, packed: torch.Tensor, w_sca
     return res
 
 
+class QuantForward:
+    """Reusable launcher for bitlinear_quant_forward (fp32 rows -> int8 ->
+    BitLinear -> epilogue) holding its workspace for up to ``max_m`` rows."""
+
+    def __init__(self, packed: torch.Tensor, w_scale: torch.Tensor, max_m: int, rmsnorm: bool = False,
+                 norm_gain: Optional[torch.Tensor] = None, eps: float = RMS_EPS, relu2: bool = False):
+        self.lib = load()
+        _need(packed, torch.uint8, 2, "packed")
+        self.packed, self.w_scale = packed, w_scale
+        self.N, self.K = packed.shape[0], packed.shape[1] * 4
+        self.qflags = BL_QUANT_RMSNORM if rmsnorm else 0
+        self.gain, self.eps, self.relu2 = norm_gain, float(eps), relu2
+        self.ws = _workspace(self.lib.bitlinear_quant_forward_workspace_bytes(max_m, self.K, self.N),
+                             packed.device)
+
+    def __call__(self, X: torch.Tensor, residual: Optional[torch.Tensor] = None,
+                 y_out: Optional[torch.Tensor] = None) -> torch.Tensor:
+        _need(X, torch.float32, 2, "X")
+        M = X.shape[0]
+        y = y_out if y_out is not None else torch.empty((M, self.N), dtype=torch.float32, device=X.device)
+        epi = Epilogue()
+        epi.flags = (BL_EPI_RELU2 if self.relu2 else 0) | (BL_EPI_RESIDUAL if residual is not None else 0)
+        if residual is not None:
+            epi.residual = residual.data_ptr()
+        _check(self.lib.bitlinear_quant_forward(_p(X), M, self.K, self.qflags, _p(self.gain), self.eps,
+                                                _p(self.packed), _p(self.w_scale), self.N, ctypes.byref(epi),
+                                                _p(y), _p(self.ws), 0 if self.ws is None else self.ws.numel(),
+                                                _stream(X.device)))
+        return y
+
+
+def quant_forward(X: torch.Tensor, packed: torch.Tensor, w_scale: torch.Tensor, rmsnorm: bool = False,
+                  norm_gain: Optional[torch.Tensor] = None, eps: float = RMS_EPS, relu2: bool = False,
+                  residual: Optional[torch.Tensor] = None, y_out: Optional[torch.Tensor] = None):
+    """Quantise fp32 X [M][K] and apply the BitLinear in one call; returns Y [M][N]."""
+    return QuantForward(packed, w_scale, X.shape[0], rmsnorm, norm_gain, eps, relu2)(X, residual, y_out)
+
+
 def make_layers(layers: Sequence[dict]):
     """Host array of FFN layer descriptors from dicts of device tensors
     (keys: up, up_scale, down, down_scale, optional pre_norm_gain, sub_norm_gain)."""
@@ -254,6 +298,7 @@ class FFNStack:
                                            self.eps, _p(self.ws), 0 if self.ws is None else self.ws.numel(),
                                            _stream(hidden.device)))
         return hidden
+
 
 
 def ffn_forward(layers: Sequence[dict], hidden: torch.Tensor, pre_norm: bool = True,

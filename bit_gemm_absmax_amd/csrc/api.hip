@@ -212,6 +212,61 @@ int bitlinear_forward(const int8_t* Xq, const float* x_scale, const int32_t* x_r
     return ok();
 }
 
+// ---------------------------------------------------------------- fused quant + forward
+
+size_t bitlinear_quant_forward_workspace_bytes(int64_t M, int64_t K, int64_t N) {
+    (void)N;
+    if (M < 1 || K < 1) return 0;
+    Carver c(nullptr);
+    c.take<int8_t>((size_t)(M * K));
+    c.take<float>((size_t)M);
+    c.take<int32_t>((size_t)M);
+    return c.off;
+}
+
+int bitlinear_quant_forward(const float* X, int64_t M, int64_t K, uint32_t quant_flags, const float* norm_gain,
+                            float norm_eps, const uint8_t* packed, const float* w_scale, int64_t N,
+                            const bl_epilogue* epi, float* Y, void* ws, size_t ws_bytes, hipStream_t stream) {
+    const uint32_t flags = epi ? epi->flags : 0u;
+    if (!X || !packed || !w_scale || !Y)
+        return fail(BL_ERR_NULL, "quant_forward: X, packed, w_scale and Y are required");
+    if (quant_flags & ~BL_QUANT_RMSNORM)
+        return fail(BL_ERR_UNSUPPORTED, "quant_forward: unknown quant flags 0x%x", quant_flags);
+    if (flags & ~(BL_EPI_RELU2 | BL_EPI_RESIDUAL))
+        return fail(BL_ERR_UNSUPPORTED, "quant_forward: epilogue flags 0x%x not supported", flags);
+    if ((flags & BL_EPI_RESIDUAL) && !epi->residual)
+        return fail(BL_ERR_NULL, "quant_forward: BL_EPI_RESIDUAL needs epi->residual");
+    if (M < 0) return fail(BL_ERR_SHAPE, "quant_forward: M = %lld must be >= 0", (long long)M);
+    if (N < 1) return fail(BL_ERR_SHAPE, "quant_forward: N = %lld must be >= 1", (long long)N);
+    if (int r = check_k(K, "quant_forward: K")) return r;
+    if (!bl::quant_supported(K))
+        return fail(BL_ERR_UNSUPPORTED, "quant_forward: K = %lld above 32768", (long long)K);
+    if (M * K >= kLimit || M * N >= kLimit || N * K >= kLimit * 4)
+        return fail(BL_ERR_SHAPE, "quant_forward: sizes exceed 2^31 elements");
+    if (!aligned(X, 16) || !aligned(packed, 16) || !aligned(Y, 16) || !aligned(w_scale, 4) ||
+        !aligned(norm_gain, 16) || ((flags & BL_EPI_RESIDUAL) && !aligned(epi->residual, 16)))
+        return fail(BL_ERR_ALIGN, "quant_forward: X, packed, Y, gain, residual need 16-byte alignment");
+    const bool fused = bl::decode_supported(M, K, N);
+    if (int r = check_workspace(ws, ws_bytes, M == 0 || fused ? 0 : bitlinear_quant_forward_workspace_bytes(M, K, N)))
+        return r;
+    if (M == 0) return ok();
+    const bool rms = (quant_flags & BL_QUANT_RMSNORM) != 0;
+    const uint32_t kflags = flags & (BL_EPI_RELU2 | BL_EPI_RESIDUAL);
+    const float* residual = (flags & BL_EPI_RESIDUAL) ? epi->residual : nullptr;
+    if (fused)
+        return hip_status(bl::launch_decode_bitlinear(X, M, K, rms, rms ? norm_gain : nullptr, norm_eps, packed,
+                                                      w_scale, N, kflags, residual, Y, stream),
+                          "quant_forward: fused decode kernel");
+    Carver c(ws);
+    int8_t* xq = c.take<int8_t>((size_t)(M * K));
+    float* xs = c.take<float>((size_t)M);
+    int32_t* rs = c.take<int32_t>((size_t)M);
+    hipError_t e = bl::launch_quant(X, M, K, rms, rms ? norm_gain : nullptr, norm_eps, xq, xs, rs, stream);
+    if (e != hipSuccess) return hip_status(e, "quant_forward: quant");
+    e = bl::launch_contract(xq, xs, rs, M, K, packed, w_scale, N, bl::Epi{kflags, residual}, Y, nullptr, stream);
+    return hip_status(e, "quant_forward: contraction");
+}
+
 // ---------------------------------------------------------------- FFN stack
 
 size_t bitnet_ffn_workspace_bytes(int64_t M, int64_t H, int64_t F) {
@@ -258,6 +313,21 @@ int bitnet_ffn_forward(const bitnet_ffn_layer* layers, int32_t n_layers, float* 
     int32_t* rs2 = c.take<int32_t>((size_t)M);
     const bool pre = (flags & BL_FFN_PRE_NORM) != 0;
     const bool res = (flags & BL_FFN_RESIDUAL) != 0;
+
+    // Few tokens: two launches per layer, each quantising its own input rows.
+    if (bl::decode_supported(M, H, F) && bl::decode_supported(M, F, H)) {
+        for (int32_t l = 0; l < n_layers; ++l) {
+            const bitnet_ffn_layer& L = layers[l];
+            hipError_t e = bl::launch_decode_bitlinear(hidden, M, H, pre, L.pre_norm_gain, norm_eps, L.up,
+                                                       L.up_scale, F, bl::kEpiRelu2, nullptr, y1, stream);
+            if (e != hipSuccess) return hip_status(e, "ffn: decode up");
+            e = bl::launch_decode_bitlinear(y1, M, F, true, L.sub_norm_gain, norm_eps, L.down, L.down_scale, H,
+                                            res ? bl::kEpiResidual : 0u, res ? hidden : nullptr, hidden, stream);
+            if (e != hipSuccess) return hip_status(e, "ffn: decode down");
+        }
+        return ok();
+    }
+
     for (int32_t l = 0; l < n_layers; ++l) {
         const bitnet_ffn_layer& L = layers[l];
         hipError_t e = bl::launch_quant(hidden, M, H, pre, pre ? L.pre_norm_gain : nullptr, norm_eps,

@@ -30,12 +30,16 @@ hipError_t launch_quant(const float* X, int64_t M, int64_t K, bool rmsnorm,
                         const float* gain, float eps, int8_t* Xq, float* scale,
                         int32_t* rowsum, hipStream_t s);
 bool quant_supported(int64_t K);
+// Workgroup size used to quantise a row of length K (256 up to 4096, 512 up
+// to 16384, else 1024); every kernel that quantises rows uses this size, so
+// all of them reduce in the same order.
+int quant_threads(int64_t K);
 
 // rowsum[m] = sum_k Xq[m][k]
 hipError_t launch_rowsum(const int8_t* Xq, int64_t M, int64_t K, int32_t* rowsum,
                          hipStream_t s);
 
-// Decode GEMV (v_dot4) for M <= 4.
+// Skinny MFMA contraction for decode / batched decode, M <= 64.
 bool gemv_supported(int64_t M, int64_t K);
 hipError_t launch_gemv(const int8_t* Xq, const float* xs, const int32_t* rs, int64_t M,
                        int64_t K, const uint8_t* packed, const float* ws, int64_t N, Epi epi,
@@ -51,5 +55,13 @@ hipError_t launch_contract(const int8_t* Xq, const float* x_scale,
                            const int32_t* rowsum, int64_t M, int64_t K,
                            const uint8_t* packed, const float* w_scale, int64_t N,
                            Epi epi, float* Y, int32_t* acc_out, hipStream_t s);
+
+// Few-token BitLinear from fp32 rows: every workgroup quantises the rows
+// itself (optional RMSNorm with gain), then contracts its slice of output
+// rows; epilogue ReLU^2 / residual (Y may alias residual).
+bool decode_supported(int64_t M, int64_t K, int64_t N);
+hipError_t launch_decode_bitlinear(const float* X, int64_t M, int64_t K, bool rmsnorm, const float* gain,
+                                   float eps, const uint8_t* packed, const float* w_scale, int64_t N,
+                                   uint32_t epi, const float* residual, float* Y, hipStream_t s);
 
 }  // namespace bl

@@ -1,156 +1,250 @@
-// Decode contraction for a few tokens (M <= 4): a bandwidth-bound GEMV over
-// the packed ternary weights (transformers "BitNet" page, "Model details" /
-// Quantization: W1.58A8, int8 activations times ternary weights).
+// Skinny contraction for decode and batched decode (M <= 64 tokens)
+// (transformers "BitNet" page, "Model details" / Quantization: W1.58A8,
+// int8 activations times ternary weights).  The work is a stream of packed
+// weights against a few KB of activations, so it is laid out for memory
+// parallelism and a short tail after the data lands:
 //
-// Layout of the work: each row of packed weights is K/64 chunks of 16 bytes
-// (64 weights).  G lanes share a row; lane g of the group takes chunks
-// g, g + G, ...  Every lane first issues all of its 16-byte weight loads
-// (coalesced: the G lanes of a row read G consecutive chunks), then the
-// workgroup stages the int8 activation rows in LDS while those loads are in
-// flight, then each 32-bit weight word is expanded with one shift and one
-// mask per 4 weights into int8 codes 0..2 and fed to v_dot4 against four
-// activations.  The code offset is removed once per output:
-//   sum_k (q+1) * x  -  sum_k x  =  sum_k q * x.
-// The G partial sums meet in an xor-butterfly inside the wave; integer sums
-// are exact, so the result does not depend on that order.
+//   - a workgroup owns 16 output rows (one MFMA column tile); its NW waves
+//     split K, and every lane issues all of its 16-byte weight loads before
+//     doing anything else;
+//   - the contraction runs on v_mfma_i32_16x16x64_i8 with the token rows as
+//     the 16-row A operand: rows past M are don't-care (their outputs are
+//     dropped), so one instruction serves 1..16 tokens and up to four M
+//     tiles reuse the same weight registers; the MFMA does the k-reduction,
+//     and expanding 16 weights costs one shift + mask per 4;
+//   - lane (n, g) holds the whole 64-weight chunk 4s + g of row n (one 16-byte
+//     load) and feeds its four 32-bit words to four MFMAs; the activation
+//     operand of lane (m, g) is the matching 16 bytes of row m, so both
+//     operands follow the same permutation of k and the sum is unchanged;
+//   - per-wave partial tiles meet in LDS in a fixed wave order (exact integer
+//     sums), then the epilogue subtracts the row sum of the code offset,
+//     dequantises and applies ReLU^2 / residual.
+//
+// Two prologues: int8 rows read straight from global memory (L2-resident,
+// shared by all workgroups), or -- for M <= 4 -- fp32 rows that every
+// workgroup quantises itself into LDS (the same quant_row_* as the
+// standalone quantiser, so the same int8 values), which removes the
+// quantiser launch from the decode chain.
 #include "bl_device.h"
 #include "bl_internal.h"
 
 namespace bl {
 namespace {
 
-constexpr int kGemvThreads = 256;
+typedef int v4i __attribute__((ext_vector_type(4)));
 
-template <int MT, int NCH>
-__global__ __launch_bounds__(kGemvThreads) void k_gemv(
-    const int8_t* __restrict__ Xq, const float* __restrict__ x_scale,
-    const int32_t* __restrict__ rowsum, int K, const uint4* __restrict__ Wp,
-    const float* __restrict__ w_scale, int N, int G, Epi epi, float* Y,
-    int32_t* __restrict__ acc_out) {
-    extern __shared__ uint4 sx[];  // MT rows of K int8
+constexpr int kRowDepth = 8;  // float4 per thread of an fp32 activation row (K <= 8192 at 256 threads)
+
+template <int MTILES, int NWV, int QMAX, bool F32IN>
+__global__ __launch_bounds__(NWV* kWave) void k_skinny(
+    const float* __restrict__ X, const int8_t* __restrict__ Xq, const float* __restrict__ x_scale,
+    const int32_t* __restrict__ x_rowsum, int M, int K, int rmsnorm, const float* __restrict__ gain,
+    float eps, const uint4* __restrict__ Wp, const float* __restrict__ w_scale, int N, uint32_t epi_flags,
+    const float* residual, float* Y, int32_t* __restrict__ acc_out) {
+    constexpr int NT = NWV * kWave;
+    extern __shared__ __align__(16) int8_t lds[];
+    __shared__ double dslot[NWV];
+    __shared__ float fslot[NWV];
+    __shared__ int islot[NWV];
+    __shared__ float gx[16 * MTILES];
+    __shared__ int rsx[16 * MTILES];
+
     const int lane = threadIdx.x % kWave;
     const int wave = threadIdx.x / kWave;
-    const int rows_per_wave = kWave / G;
-    const int n = (blockIdx.x * (kGemvThreads / kWave) + wave) * rows_per_wave + lane / G;
-    const int gl = lane % G;
-    const int C = K / 64;
+    const int fr = lane & 15;      // column (output row) of the tile / activation row of the A operand
+    const int fg = lane >> 4;      // k group
+    const int n0 = blockIdx.x * 16;
+    const int C = K / 64;          // 64-weight chunks per row
+    const int nq = (C + 3) / 4;    // chunk quads
 
-    uint4 w[NCH];
+    // ---- loads first: the first fp32 activation row, then every weight chunk
+    float4 v[F32IN ? kRowDepth : 1];
+    if constexpr (F32IN) quant_row_load<NT, kRowDepth>(X, K, v);
+    uint4 w[QMAX];
+    {
+        const int n = n0 + fr;
 #pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-        const int c = gl + i * G;
-        w[i] = (n < N && c < C) ? Wp[(int64_t)n * C + c] : make_uint4(0u, 0u, 0u, 0u);
+        for (int i = 0; i < QMAX; ++i) {
+            const int s = wave + i * NWV;
+            const int c = 4 * s + fg;
+            w[i] = (s < nq && c < C && n < N) ? Wp[(int64_t)n * C + c] : make_uint4(0u, 0u, 0u, 0u);
+        }
     }
 
-    const uint4* xg = reinterpret_cast<const uint4*>(Xq);
-    for (int i = threadIdx.x; i < MT * K / 16; i += kGemvThreads) sx[i] = xg[i];
-    __syncthreads();
-
-    int acc[MT];
+    // ---- activation rows: quantised here (fp32 input) or read as int8
+    const int8_t* arow[MTILES];
+    if constexpr (F32IN) {
+        int8_t* xq = lds;  // [M][K]
 #pragma unroll
-    for (int m = 0; m < MT; ++m) acc[m] = 0;
-
+        for (int m = 0; m < 4; ++m) {
+            if (m < M) {
+                if (m > 0) quant_row_load<NT, kRowDepth>(X + (int64_t)m * K, K, v);
+                const QuantRow q = quant_row_finish<NT, kRowDepth>(v, K, rmsnorm != 0, gain, eps, xq + m * K,
+                                                                   dslot, fslot, islot, true);
+                if (threadIdx.x == 0) {
+                    gx[m] = q.gamma;
+                    rsx[m] = q.rowsum;
+                }
+            }
+        }
+        __syncthreads();
+        arow[0] = xq + (fr < M ? fr : M - 1) * K;
+    } else {
+        if (threadIdx.x < M) {
+            gx[threadIdx.x] = x_scale[threadIdx.x];
+            rsx[threadIdx.x] = x_rowsum[threadIdx.x];
+        }
 #pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-        const int c = gl + i * G;
-        if (c < C) {
+        for (int t = 0; t < MTILES; ++t) {
+            const int m = 16 * t + fr;
+            arow[t] = Xq + (int64_t)(m < M ? m : M - 1) * K;
+        }
+    }
+
+    // ---- contraction
+    v4i acc[MTILES];
+#pragma unroll
+    for (int t = 0; t < MTILES; ++t) acc[t] = v4i{0, 0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < QMAX; ++i) {
+        const int s = wave + i * NWV;
+        if (s < nq) {
+            const int koff = 64 * (4 * s + fg);
+            const bool kin = (4 * s + fg) < C;
             const uint32_t wd[4] = {w[i].x, w[i].y, w[i].z, w[i].w};
 #pragma unroll
             for (int d = 0; d < 4; ++d) {
-                const int c0 = codes4(wd[d], 0);
-                const int c1 = codes4(wd[d], 1);
-                const int c2 = codes4(wd[d], 2);
-                const int c3 = codes4(wd[d], 3);
+                const v4i b = v4i{codes4(wd[d], 0), codes4(wd[d], 1), codes4(wd[d], 2), codes4(wd[d], 3)};
 #pragma unroll
-                for (int m = 0; m < MT; ++m) {
-                    const uint4 xv = sx[(m * K + 64 * c + 16 * d) / 16];
-                    int a = acc[m];
-                    a = __builtin_amdgcn_sdot4(c0, (int)xv.x, a, false);
-                    a = __builtin_amdgcn_sdot4(c1, (int)xv.y, a, false);
-                    a = __builtin_amdgcn_sdot4(c2, (int)xv.z, a, false);
-                    a = __builtin_amdgcn_sdot4(c3, (int)xv.w, a, false);
-                    acc[m] = a;
+                for (int t = 0; t < MTILES; ++t) {
+                    const v4i a = kin ? *reinterpret_cast<const v4i*>(arow[t] + koff + 16 * d) : v4i{0, 0, 0, 0};
+                    acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, acc[t], 0, 0, 0);
                 }
             }
         }
     }
 
-    for (int mask = G / 2; mask >= 1; mask >>= 1) {
+    // ---- per-wave partial tiles -> LDS in wave order -> epilogue
+    int* red = reinterpret_cast<int*>(lds + (F32IN ? ((4 * K + 15) / 16) * 16 : 0));  // [NWV][16*MTILES][16]
+    constexpr int ROWS = 16 * MTILES;
+    __syncthreads();
 #pragma unroll
-        for (int m = 0; m < MT; ++m) acc[m] += __shfl_xor(acc[m], mask, kWave);
-    }
-
-    if (n >= N) return;
+    for (int t = 0; t < MTILES; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int m = 16 * t + 4 * fg + r;
+            if (m < M) red[(wave * ROWS + m) * 16 + fr] = acc[t][r];
+        }
+    __syncthreads();
     const float ws = *w_scale;
+    for (int i = threadIdx.x; i < M * 16; i += NT) {
+        const int m = i / 16, col = i % 16;
+        const int n = n0 + col;
+        if (n < N) {
+            int a = 0;
 #pragma unroll
-    for (int m = 0; m < MT; ++m) {
-        if (gl == (m % G)) {
-            const int a = acc[m] - rowsum[m];
-            const float d = (x_scale[m] * ws) / 127.0f;
+            for (int q = 0; q < NWV; ++q) a += red[(q * ROWS + m) * 16 + col];
+            a -= rsx[m];
+            const float d = (gx[m] * ws) / 127.0f;
             float y = (float)a * d;
-            if (epi.flags & kEpiRelu2) {
-                const float r = y > 0.0f ? y : 0.0f;
-                y = r * r;
+            if (epi_flags & kEpiRelu2) {
+                const float tt = y > 0.0f ? y : 0.0f;
+                y = tt * tt;
             }
             const int64_t o = (int64_t)m * N + n;
-            if (epi.flags & kEpiResidual) y = y + epi.residual[o];
+            if (epi_flags & kEpiResidual) y = y + residual[o];
             if (Y != nullptr) Y[o] = y;
             if (acc_out != nullptr) acc_out[o] = a;
         }
     }
 }
 
-template <int MT>
-hipError_t launch_mt(int nch, const int8_t* Xq, const float* xs, const int32_t* rs, int64_t K,
-                     const uint8_t* packed, const float* ws, int64_t N, int G, Epi epi, float* Y,
-                     int32_t* acc_out, hipStream_t s) {
-    const int rows_per_block = (kGemvThreads / kWave) * (kWave / G);
-    const unsigned blocks = (unsigned)((N + rows_per_block - 1) / rows_per_block);
-    const size_t lds = (size_t)MT * (size_t)K;
-#define BL_GCASE(C)                                                                         \
-    case C:                                                                                 \
-        hipLaunchKernelGGL((k_gemv<MT, C>), dim3(blocks), dim3(kGemvThreads), lds, s, Xq, xs, \
-                           rs, (int)K, reinterpret_cast<const uint4*>(packed), ws, (int)N, G, \
-                           epi, Y, acc_out);                                                \
-        break;
-    switch (nch) {
-        BL_GCASE(1)
-        BL_GCASE(2)
-        BL_GCASE(3)
-        BL_GCASE(4)
-        BL_GCASE(5)
-        BL_GCASE(6)
-        BL_GCASE(7)
-        BL_GCASE(8)
-        default:
-            return hipErrorInvalidValue;
-    }
-#undef BL_GCASE
+struct Plan {
+    int nw, qmax;
+};
+
+// Waves per workgroup and weight loads per lane from the chunk-quad count.
+bool plan(int64_t K, Plan& p) {
+    const int64_t nq = (K / 64 + 3) / 4;
+    p.nw = quant_threads(K) / kWave;  // 4 waves up to K = 4096, then 8 (same size as the quantiser)
+    if (p.nw > 8) p.nw = 8;
+    const int64_t per = (nq + p.nw - 1) / p.nw;
+    if (per <= 2) p.qmax = 2;
+    else if (per <= 4) p.qmax = 4;
+    else if (per <= 8) p.qmax = 8;
+    else return false;
+    return true;
+}
+
+template <int MT, int NWV, int Q, bool F>
+hipError_t go(const float* X, const int8_t* Xq, const float* xs, const int32_t* rs, int64_t M, int64_t K, bool rms,
+              const float* gain, float eps, const uint8_t* packed, const float* ws, int64_t N, uint32_t epi,
+              const float* residual, float* Y, int32_t* acc_out, hipStream_t s) {
+    const unsigned blocks = (unsigned)((N + 15) / 16);
+    const size_t red = (size_t)NWV * 16 * MT * 16 * sizeof(int);
+    const size_t lds = (F ? ((4 * (size_t)K + 15) / 16) * 16 : 0) + red;
+    hipLaunchKernelGGL((k_skinny<MT, NWV, Q, F>), dim3(blocks), dim3(NWV * kWave), lds, s, X, Xq, xs, rs, (int)M,
+                       (int)K, rms ? 1 : 0, gain, eps, reinterpret_cast<const uint4*>(packed), ws, (int)N, epi,
+                       residual, Y, acc_out);
     return hipGetLastError();
+}
+
+template <int MT, bool F>
+hipError_t go_mt(const Plan& p, const float* X, const int8_t* Xq, const float* xs, const int32_t* rs, int64_t M,
+                 int64_t K, bool rms, const float* gain, float eps, const uint8_t* packed, const float* ws,
+                 int64_t N, uint32_t epi, const float* residual, float* Y, int32_t* acc_out, hipStream_t s) {
+#define BL_SK(NWV, Q)                                                                                     \
+    if (p.nw == NWV && p.qmax == Q)                                                                       \
+        return go<MT, NWV, Q, F>(X, Xq, xs, rs, M, K, rms, gain, eps, packed, ws, N, epi, residual, Y, acc_out, s);
+    BL_SK(4, 2)
+    BL_SK(4, 4)
+    BL_SK(8, 2)
+    BL_SK(8, 4)
+    BL_SK(8, 8)
+#undef BL_SK
+    return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-// Lanes per row: the smallest power of two that keeps every lane at <= 4
-// chunks, capped at a wave; chunks per lane follow.
 bool gemv_supported(int64_t M, int64_t K) {
-    return M >= 1 && M <= 4 && K <= 32768 && M * K <= 65536;
+    Plan p;
+    return M >= 1 && M <= 64 && K <= 32768 && plan(K, p);
 }
 
-hipError_t launch_gemv(const int8_t* Xq, const float* xs, const int32_t* rs, int64_t M,
-                       int64_t K, const uint8_t* packed, const float* ws, int64_t N, Epi epi,
-                       float* Y, int32_t* acc_out, hipStream_t s) {
-    const int64_t C = K / 64;
-    int G = 1;
-    while (G < 64 && G * 4 < C) G *= 2;
-    const int nch = (int)((C + G - 1) / G);
-    switch (M) {
-        case 1: return launch_mt<1>(nch, Xq, xs, rs, K, packed, ws, N, G, epi, Y, acc_out, s);
-        case 2: return launch_mt<2>(nch, Xq, xs, rs, K, packed, ws, N, G, epi, Y, acc_out, s);
-        case 3: return launch_mt<3>(nch, Xq, xs, rs, K, packed, ws, N, G, epi, Y, acc_out, s);
-        case 4: return launch_mt<4>(nch, Xq, xs, rs, K, packed, ws, N, G, epi, Y, acc_out, s);
+hipError_t launch_gemv(const int8_t* Xq, const float* xs, const int32_t* rs, int64_t M, int64_t K,
+                       const uint8_t* packed, const float* ws, int64_t N, Epi epi, float* Y, int32_t* acc_out,
+                       hipStream_t s) {
+    Plan p;
+    if (!plan(K, p)) return hipErrorInvalidValue;
+    const int mt = (int)((M + 15) / 16);
+    switch (mt) {
+        case 1: return go_mt<1, false>(p, nullptr, Xq, xs, rs, M, K, false, nullptr, 0.f, packed, ws, N, epi.flags,
+                                       epi.residual, Y, acc_out, s);
+        case 2: return go_mt<2, false>(p, nullptr, Xq, xs, rs, M, K, false, nullptr, 0.f, packed, ws, N, epi.flags,
+                                       epi.residual, Y, acc_out, s);
+        case 3: return go_mt<3, false>(p, nullptr, Xq, xs, rs, M, K, false, nullptr, 0.f, packed, ws, N, epi.flags,
+                                       epi.residual, Y, acc_out, s);
+        case 4: return go_mt<4, false>(p, nullptr, Xq, xs, rs, M, K, false, nullptr, 0.f, packed, ws, N, epi.flags,
+                                       epi.residual, Y, acc_out, s);
         default: return hipErrorInvalidValue;
     }
+}
+
+bool decode_supported(int64_t M, int64_t K, int64_t N) {
+    (void)N;
+    Plan p;
+    if (M < 1 || M > 4 || !plan(K, p) || quant_threads(K) != p.nw * kWave) return false;
+    return K <= (int64_t)4 * p.nw * kWave * kRowDepth;  // quant_row_*: kRowDepth float4 per thread
+}
+
+hipError_t launch_decode_bitlinear(const float* X, int64_t M, int64_t K, bool rmsnorm, const float* gain, float eps,
+                                   const uint8_t* packed, const float* w_scale, int64_t N, uint32_t epi,
+                                   const float* residual, float* Y, hipStream_t s) {
+    Plan p;
+    if (!plan(K, p)) return hipErrorInvalidValue;
+    return go_mt<1, true>(p, X, nullptr, nullptr, nullptr, M, K, rmsnorm, gain, eps, packed, w_scale, N, epi,
+                          residual, Y, nullptr, s);
 }
 
 }  // namespace bl

@@ -176,6 +176,29 @@ int bitlinear_forward(const int8_t* Xq, const float* x_scale,
                       void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * Fused quantise + BitLinear: bitlinear_quant_act followed by
+ * bitlinear_forward, from fp32 activation rows, with the same results as the
+ * two calls.  For a few tokens (M <= 4) it is one launch in which every
+ * workgroup quantises the rows itself; otherwise the two steps run in turn
+ * through the workspace.
+ *
+ * X           in  fp32 [M][K]
+ * quant_flags     BL_QUANT_RMSNORM or 0; norm_gain / norm_eps as in
+ *                 bitlinear_quant_act
+ * packed, w_scale, N  as in bitlinear_forward
+ * epi         in  host pointer or NULL; only BL_EPI_RELU2 and BL_EPI_RESIDUAL
+ *                 are accepted here (BL_ERR_UNSUPPORTED otherwise)
+ * Y           out fp32 [M][N]; may equal epi->residual (in place)
+ * ws          scratch of bitlinear_quant_forward_workspace_bytes(M, K, N)
+ * ---------------------------------------------------------------------- */
+size_t bitlinear_quant_forward_workspace_bytes(int64_t M, int64_t K, int64_t N);
+int bitlinear_quant_forward(const float* X, int64_t M, int64_t K, uint32_t quant_flags,
+                            const float* norm_gain, float norm_eps,
+                            const uint8_t* packed, const float* w_scale, int64_t N,
+                            const bl_epilogue* epi, float* Y,
+                            void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * BitNet feed-forward stack: for each layer in order, on hidden [M][H]
  * ("Model details" / Architecture: BitLinear FFN with ReLU^2 and subln, no
  * bias; "BitNetConfig": hidden 2560, intermediate 6912, 30 layers):
@@ -190,7 +213,8 @@ int bitlinear_forward(const int8_t* Xq, const float* x_scale,
  * layers     in  host array of n_layers descriptors holding device pointers
  * hidden     in/out fp32 [M][H]
  * norm_eps   eps of both RMSNorms (1e-5)
- * ws         scratch of bitnet_ffn_workspace_bytes(M, H, F)
+ * ws         scratch of bitnet_ffn_workspace_bytes(M, H, F); calls that
+ *            share one workspace must not overlap in time.
  * Gated blocks (gate != NULL) return BL_ERR_UNSUPPORTED.
  * ---------------------------------------------------------------------- */
 #define BL_FFN_PRE_NORM 0x1u

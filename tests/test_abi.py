@@ -146,3 +146,21 @@ def test_binding_raises_on_bad_tensor():
     import torch
     with pytest.raises((ValueError, TypeError)):
         bl.pack_weights(torch.zeros(4, 64))  # CPU tensor: rejected before any C call
+
+
+def test_quant_forward_validation(lib):
+    f = lib.bitlinear_quant_forward
+    E = bl.Epilogue
+    nul = ctypes.POINTER(E)()
+    assert f(None, 1, 64, 0, None, 1e-5, B, C, 8, nul, D, None, 0, None) == bl.BL_ERR_NULL
+    assert f(A, 1, 64, 0, None, 1e-5, B, C, 8, nul, None, None, 0, None) == bl.BL_ERR_NULL
+    assert f(A, 1, 64, 0x4, None, 1e-5, B, C, 8, nul, D, None, 0, None) == bl.BL_ERR_UNSUPPORTED
+    e = E(flags=bl.BL_EPI_SUBLN_QUANT)
+    assert f(A, 1, 64, 0, None, 1e-5, B, C, 8, ctypes.byref(e), D, None, 0, None) == bl.BL_ERR_UNSUPPORTED
+    e = E(flags=bl.BL_EPI_RESIDUAL)
+    assert f(A, 1, 64, 0, None, 1e-5, B, C, 8, ctypes.byref(e), D, None, 0, None) == bl.BL_ERR_NULL
+    assert f(A, 1, 96, 0, None, 1e-5, B, C, 8, nul, D, None, 0, None) == bl.BL_ERR_SHAPE
+    assert f(A, 1, 64, 0, None, 1e-5, B, C, 0, nul, D, None, 0, None) == bl.BL_ERR_SHAPE
+    assert f(A, 1, 64, 0, None, 1e-5, B, C, 8, nul, MIS, None, 0, None) == bl.BL_ERR_ALIGN
+    assert f(A, 0, 64, 0, None, 1e-5, B, C, 8, nul, D, None, 0, None) == bl.BL_OK
+    assert lib.bitlinear_quant_forward_workspace_bytes(64, 2560, 6912) >= 64 * 2560

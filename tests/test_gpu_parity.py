@@ -113,7 +113,7 @@ def run_forward(X, W, **kw):
     return out, ref, (xq, xs, rs, p, s, q, g)
 
 
-@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 8, 17, 64, 130])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 8, 17, 40, 64, 65, 130])
 @pytest.mark.parametrize("K,N", [(256, 512), (192, 100), (2560, 200), (6912, 72), (64, 96), (128, 130), (320, 160)])
 def test_forward_small(M, K, N):
     log(f"[forward] M={M} K={K} N={N}")
@@ -176,10 +176,46 @@ def test_forward_subln_requant(M, with_gain):
     assert_exact(host(o2["q"]), host(out["q"]), "subln without Y")
 
 
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 12])
+@pytest.mark.parametrize("K,N,rms,gain,relu2,res", [(2560, 6912, False, False, True, False),
+                                                     (6912, 2560, True, True, False, True),
+                                                     (256, 512, True, False, False, False),
+                                                     (640, 37, False, False, True, True)])
+def test_quant_forward(M, K, N, rms, gain, relu2, res):
+    """Fused quantise + BitLinear (one launch for M <= 4) against the oracle."""
+    log(f"[quant_forward] M={M} K={K} N={N} rms={rms} gain={gain} relu2={relu2} res={res}")
+    rng = np.random.default_rng(M * 7 + K + N)
+    X = synth.activations(rng, M, K, outliers=True)
+    W = synth.weights(rng, N, K)
+    g = synth.gains(rng, K) if gain else None
+    R = synth.activations(rng, M, N)
+    p, s, q, gw = check_pack(W, "quant_forward")
+    y = bl.quant_forward(dev(X), p, s, rmsnorm=rms, norm_gain=None if g is None else dev(g), relu2=relu2,
+                         residual=dev(R) if res else None)
+    z = oracle.rmsnorm(X, g) if rms else X
+    xq, gx, _ = oracle.quant_act(z)
+    want = oracle.dequant(oracle.int_matmul(xq, q), gx, gw)
+    if relu2:
+        want = oracle.relu2(want)
+    if res:
+        want = oracle.add(R, want)
+    assert_y_close(host(y), want, "quant_forward y")
+    # same values as the two-step path on the GPU
+    xq2, xs2, rs2 = bl.quant_act(dev(X), rmsnorm=rms, norm_gain=None if g is None else dev(g))
+    two = bl.forward(xq2, xs2, p, s, x_rowsum=rs2, relu2=relu2, residual=dev(R) if res else None)
+    assert_exact(host(y), host(two["y"]), "quant_forward vs quant_act + forward")
+    if res:  # in place
+        h = dev(R)
+        bl.quant_forward(dev(X), p, s, rmsnorm=rms, norm_gain=None if g is None else dev(g), relu2=relu2,
+                         residual=h, y_out=h)
+        assert_exact(host(h), host(y), "quant_forward in place")
+
+
 def test_gemv_row_equals_gemm_row():
-    """Token independence across kernels: M=1 (GEMV) equals row 0 of M=8 (GEMM)."""
+    """Token independence across kernels: M=1 (skinny decode kernel) equals
+    row 0 of M=80 (tiled GEMM)."""
     rng = np.random.default_rng(21)
-    X = synth.activations(rng, 8, 2560, outliers=True)
+    X = synth.activations(rng, 80, 2560, outliers=True)
     W = synth.weights(rng, 640, 2560)
     p, s = gpu_pack(W)
     xq, xs, rs = bl.quant_act(dev(X))
@@ -271,10 +307,16 @@ def test_ffn_block_small(M):
     h = h0
     for l in range(L):
         h, _ = layer_teacher_forced(h, gl[l], ol[l], M)
-    # the fused stack call runs the same kernels: bit-identical to the staged calls
+    # the stack call (fused decode kernels for M <= 4) gives exactly the
+    # staged calls' results: same quantiser reductions, exact integer sums
     hs = dev(h0)
-    bl.ffn_forward(gl, hs)
+    stack = bl.FFNStack(gl, H, F, M, DEV)
+    stack(hs)
     assert_exact(host(hs), h, "ffn stack vs staged calls")
+    # twice in a row on the same workspace: same result
+    hs2 = dev(h0)
+    stack(hs2)
+    assert_exact(host(hs2), h, "ffn stack, second call")
     # free running against the oracle stack (information, loose bound)
     ref = oracle.ffn_stack(h0, ol)
     assert np.abs(host(hs) - ref).max() <= 1e-3 * np.abs(ref).max()
@@ -390,7 +432,8 @@ def test_workload_ffn_stack(M):
     h0 = synth.ffn_stack_hidden(rng)[:M].copy()
     hs = dev(h0)
     log(f"[workload] ffn stack M={M}: running")
-    bl.ffn_forward(gl, hs)
+    stack = bl.FFNStack(gl, synth.HIDDEN, synth.FFN, M, DEV)
+    stack(hs)
     got = host(hs)
     rows = [0] if M == 1 else [0, 13, M - 1]
     h = h0[rows]
