@@ -10,63 +10,120 @@ namespace bl {
 
 constexpr int kWave = 64;
 
-// xor-butterfly: every lane ends with the same value, and because each step
-// adds the same two operands on both partner lanes, the result is the same
-// on every lane even for floating point.
-__device__ __forceinline__ double wave_sum(double v) {
-#pragma unroll
-    for (int m = kWave / 2; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
-    return v;
+// Raw buffer access.  A load whose byte offset is at or past the
+// descriptor's size returns zero in hardware, so bounds-checked loads need no
+// branch: every load issues unconditionally, and the in-order vmcnt counter
+// lets a kernel wait for an early load while later ones are still in flight
+// (a load under a divergent branch makes the compiler wait for everything).
+// Dword 3 = 0x00020000 selects 32-bit data format, which raw loads need to
+// be valid on gfx9-family parts.
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+constexpr uint32_t kOob = 0x80000000u;  // an offset past every descriptor used here
+
+__device__ __forceinline__ Rsrc make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
-__device__ __forceinline__ int wave_sum(int v) {
-#pragma unroll
-    for (int m = kWave / 2; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
-    return v;
+__device__ __forceinline__ uint4 buf_load16(Rsrc r, uint32_t off) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int m = kWave / 2; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, kWave));
-    return v;
+__device__ __forceinline__ float4 buf_load16f(Rsrc r, uint32_t off) {
+    return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ float buf_load4f(Rsrc r, uint32_t off) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+__device__ __forceinline__ int buf_load4i(Rsrc r, uint32_t off) {
+    return (int)__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
 }
 
-// Block reductions over NW waves through a small LDS array; the final sum
-// runs over the waves in index order.  All threads get the result.  The
-// caller must pass distinct `slot` arrays for back-to-back reductions or
-// separate them with a barrier (these helpers end with one).
+// Wave reductions.  Within each row of 16 lanes, four DPP steps pair lane i
+// with i^1, i^2 (quad permutes), 7-i (half mirror) and 15-i (mirror); after
+// the first two steps the four lanes of a quad agree, so each step combines
+// two equal groups and every lane computes the same two operands (in either
+// order: + and max are commutative), hence the same value.  The four row
+// values are then read into scalars and combined as (r0 + r1) + (r2 + r3).
+// The order depends only on lane numbers, so results are run-to-run
+// identical and the same in every kernel that calls these.
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppMirror = 0x140;
+
+template <int CTRL>
+__device__ __forceinline__ int dpp(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __builtin_bit_cast(float, dpp<CTRL>(__builtin_bit_cast(int, v)));
+}
+template <int CTRL>
+__device__ __forceinline__ double dpp(double v) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = (uint32_t)dpp<CTRL>((int)(uint32_t)u);
+    const uint32_t hi = (uint32_t)dpp<CTRL>((int)(uint32_t)(u >> 32));
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ int lane_read(int v, int l) { return __builtin_amdgcn_readlane(v, l); }
+__device__ __forceinline__ float lane_read(float v, int l) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+}
+__device__ __forceinline__ double lane_read(double v, int l) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, l);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), l);
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+template <typename T>
+__device__ __forceinline__ T wave_sum(T v) {
+    v = v + dpp<kDppXor1>(v);
+    v = v + dpp<kDppXor2>(v);
+    v = v + dpp<kDppHalfMirror>(v);
+    v = v + dpp<kDppMirror>(v);
+    return (lane_read(v, 0) + lane_read(v, 16)) + (lane_read(v, 32) + lane_read(v, 48));
+}
+__device__ __forceinline__ float wave_max(float v) {
+    v = fmaxf(v, dpp<kDppXor1>(v));
+    v = fmaxf(v, dpp<kDppXor2>(v));
+    v = fmaxf(v, dpp<kDppHalfMirror>(v));
+    v = fmaxf(v, dpp<kDppMirror>(v));
+    return fmaxf(fmaxf(lane_read(v, 0), lane_read(v, 16)), fmaxf(lane_read(v, 32), lane_read(v, 48)));
+}
+
+// Block reductions over NW waves through a small LDS array; the final
+// combine runs over the waves in index order, and all threads get the
+// result.  One barrier each and none at the end: a slot array may be used
+// again only after a further barrier (distinct arrays for back-to-back
+// reductions).
 template <int NW>
 __device__ __forceinline__ double block_sum(double v, double* slot) {
     v = wave_sum(v);
-    const int w = threadIdx.x / kWave;
-    if ((threadIdx.x % kWave) == 0) slot[w] = v;
+    if ((threadIdx.x % kWave) == 0) slot[threadIdx.x / kWave] = v;
     __syncthreads();
     double t = 0.0;
 #pragma unroll
     for (int i = 0; i < NW; ++i) t += slot[i];
-    __syncthreads();
     return t;
 }
 template <int NW>
 __device__ __forceinline__ int block_sum(int v, int* slot) {
     v = wave_sum(v);
-    const int w = threadIdx.x / kWave;
-    if ((threadIdx.x % kWave) == 0) slot[w] = v;
+    if ((threadIdx.x % kWave) == 0) slot[threadIdx.x / kWave] = v;
     __syncthreads();
     int t = 0;
 #pragma unroll
     for (int i = 0; i < NW; ++i) t += slot[i];
-    __syncthreads();
     return t;
 }
 template <int NW>
 __device__ __forceinline__ float block_max(float v, float* slot) {
     v = wave_max(v);
-    const int w = threadIdx.x / kWave;
-    if ((threadIdx.x % kWave) == 0) slot[w] = v;
+    if ((threadIdx.x % kWave) == 0) slot[threadIdx.x / kWave] = v;
     __syncthreads();
     float t = slot[0];
 #pragma unroll
     for (int i = 1; i < NW; ++i) t = fmaxf(t, slot[i]);
-    __syncthreads();
     return t;
 }
 
@@ -87,7 +144,6 @@ __device__ __forceinline__ void block_sum_max(double& v, float& mx, double* dslo
     for (int i = 0; i < NW; ++i) t += dslot[i];
 #pragma unroll
     for (int i = 1; i < NW; ++i) m = fmaxf(m, fslot[i]);
-    __syncthreads();
     v = t;
     mx = m;
 }
@@ -110,39 +166,40 @@ __device__ __forceinline__ int signed4(uint32_t w, int j) {
 // One token row of the activation quantiser, run by a whole workgroup of NT
 // threads: optional RMSNorm (binary64 sum of squares, r rounded once to
 // binary32, z = (x * r) * gain), then absmax int8 quantisation.  Thread t
-// owns float4 indices t + NT*i (i < NV), so K <= 4 * NT * NV.  Every kernel
-// uses these functions with the same NT for a given K, so the reduction
-// order (per-thread in i, then the wave butterfly, then the waves in index
-// order) and hence every result is the same in every kernel.  Without a
-// gain, max|x| is reduced together with the sum of squares: rounding is
-// monotonic, so max_k |fl(x_k * r)| equals fl(max_k |x_k| * r), the same
-// value a second pass would give.
+// owns float4 indices t + NT*i (i < NV), so K <= 4 * NT * NV; slots past the
+// row hold zeros, which change no sum or max, so any NV that covers the row
+// gives the same results.  Every kernel uses these functions with the same
+// NT for a given K, so the reduction order (per-thread in i, then the wave
+// reduction, then the waves in index order) and hence every result is the
+// same in every kernel.  Without a gain, max|x| is reduced together with the
+// sum of squares: rounding is monotonic, so max_k |fl(x_k * r)| equals
+// fl(max_k |x_k| * r), the same value a second pass would give.
 //
-// quant_row_load issues the row's loads (so a caller can put them ahead of
-// other traffic); quant_row_finish does the arithmetic and writes xq (global
-// memory or LDS), returning gamma and, if asked, the int8 row sum to all
-// threads.
-struct QuantRow {
-    float gamma;
-    int rowsum;
-};
-
+// quant_row_load issues the row's loads, and the gain's (zeros when there is
+// none), so a caller can put them ahead of other traffic; quant_row_finish
+// does the arithmetic, writes xq (global memory or LDS) and returns gamma to
+// all threads.  With rs_slot, lane 0 of each wave also writes the wave's
+// share of the int8 row sum to rs_slot[wave]: the caller adds the NT/64
+// entries after its next barrier.  Slot arrays follow block_sum's rule.
 template <int NT, int NV>
-__device__ __forceinline__ void quant_row_load(const float* __restrict__ x, int K, float4 (&v)[NV]) {
-    const int n4 = K / 4;
-    const float4* x4 = reinterpret_cast<const float4*>(x);
+__device__ __forceinline__ void quant_row_load_x(const float* x, int K, float4 (&v)[NV]) {
+    const Rsrc rx = make_rsrc(x, (uint32_t)K * 4u);
 #pragma unroll
-    for (int i = 0; i < NV; ++i) {
-        const int idx = threadIdx.x + i * NT;
-        v[i] = idx < n4 ? x4[idx] : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
+    for (int i = 0; i < NV; ++i) v[i] = buf_load16f(rx, (uint32_t)(threadIdx.x + i * NT) * 16u);
+}
+template <int NT, int NV>
+__device__ __forceinline__ void quant_row_load(const float* x, const float* gain, int K, float4 (&v)[NV],
+                                               float4 (&gv)[NV]) {
+    quant_row_load_x<NT, NV>(x, K, v);
+    const Rsrc rg = make_rsrc(gain, gain != nullptr ? (uint32_t)K * 4u : 0u);
+#pragma unroll
+    for (int i = 0; i < NV; ++i) gv[i] = buf_load16f(rg, (uint32_t)(threadIdx.x + i * NT) * 16u);
 }
 
 template <int NT, int NV>
-__device__ __forceinline__ QuantRow quant_row_finish(float4 (&v)[NV], int K, bool rmsnorm,
-                                                     const float* __restrict__ gain, float eps, int8_t* xq,
-                                                     double* dslot, float* fslot, int* islot,
-                                                     bool want_rowsum) {
+__device__ __forceinline__ float quant_row_finish(float4 (&v)[NV], const float4 (&gv)[NV], int K, bool rmsnorm,
+                                                  bool has_gain, float eps, int8_t* xq, double* dslot,
+                                                  float* fslot, float* fslot2, int* rs_slot) {
     constexpr int NW = NT / kWave;
     const int n4 = K / 4;
     float amax = 0.0f;
@@ -165,25 +222,22 @@ __device__ __forceinline__ QuantRow quant_row_finish(float4 (&v)[NV], int K, boo
         }
         block_sum_max<NW>(ss, amax, dslot, fslot);
         const float r = (float)(1.0 / sqrt(ss / (double)K + (double)eps));
-        const float4* g4 = reinterpret_cast<const float4*>(gain);
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
-            const int idx = threadIdx.x + i * NT;
             float4 t = v[i];
             t.x = t.x * r;
             t.y = t.y * r;
             t.z = t.z * r;
             t.w = t.w * r;
-            if (gain != nullptr && idx < n4) {
-                const float4 gg = g4[idx];
-                t.x = t.x * gg.x;
-                t.y = t.y * gg.y;
-                t.z = t.z * gg.z;
-                t.w = t.w * gg.w;
+            if (has_gain) {
+                t.x = t.x * gv[i].x;
+                t.y = t.y * gv[i].y;
+                t.z = t.z * gv[i].z;
+                t.w = t.w * gv[i].w;
             }
             v[i] = t;
         }
-        if (gain != nullptr) {
+        if (has_gain) {
             amax = 0.0f;
 #pragma unroll
             for (int i = 0; i < NV; ++i) {
@@ -192,7 +246,7 @@ __device__ __forceinline__ QuantRow quant_row_finish(float4 (&v)[NV], int K, boo
                 amax = fmaxf(amax, fabsf(v[i].z));
                 amax = fmaxf(amax, fabsf(v[i].w));
             }
-            g = block_max<NW>(amax, fslot);
+            g = block_max<NW>(amax, fslot2);
         } else {
             g = amax * r;
         }
@@ -206,23 +260,24 @@ __device__ __forceinline__ QuantRow quant_row_finish(float4 (&v)[NV], int K, boo
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
         const int idx = threadIdx.x + i * NT;
-        if (idx < n4) {
-            const float e[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
-            uint32_t packed = 0;
+        const float e[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+        uint32_t packed = 0;
 #pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                float t = rintf(e[b] * s);
-                t = t > 127.0f ? 127.0f : t;
-                t = t < -127.0f ? -127.0f : t;
-                const int qi = (int)t;
-                sum += qi;
-                packed |= ((uint32_t)qi & 0xFFu) << (8 * b);
-            }
-            q4[idx] = (int)packed;
+        for (int b = 0; b < 4; ++b) {
+            float t = rintf(e[b] * s);
+            t = t > 127.0f ? 127.0f : t;
+            t = t < -127.0f ? -127.0f : t;
+            const int qi = (int)t;
+            sum += qi;  // slots past the row hold 0 and add 0
+            packed |= ((uint32_t)qi & 0xFFu) << (8 * b);
         }
+        if (idx < n4) q4[idx] = (int)packed;
     }
-    if (want_rowsum) sum = block_sum<NW>(sum, islot);
-    return QuantRow{g, sum};
+    if (rs_slot != nullptr) {
+        sum = wave_sum(sum);
+        if ((threadIdx.x % kWave) == 0) rs_slot[threadIdx.x / kWave] = sum;
+    }
+    return g;
 }
 
 }  // namespace bl

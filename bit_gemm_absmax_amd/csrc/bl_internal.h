@@ -40,7 +40,7 @@ hipError_t launch_rowsum(const int8_t* Xq, int64_t M, int64_t K, int32_t* rowsum
                          hipStream_t s);
 
 // Skinny MFMA contraction for decode / batched decode, M <= 64.
-bool gemv_supported(int64_t M, int64_t K);
+bool gemv_supported(int64_t M, int64_t K, int64_t N);
 hipError_t launch_gemv(const int8_t* Xq, const float* xs, const int32_t* rs, int64_t M,
                        int64_t K, const uint8_t* packed, const float* ws, int64_t N, Epi epi,
                        float* Y, int32_t* acc_out, hipStream_t s);

@@ -326,7 +326,7 @@ hipError_t launch_gemm(const int8_t* Xq, const float* xs, const int32_t* rs, int
 hipError_t launch_contract(const int8_t* Xq, const float* x_scale, const int32_t* rowsum,
                            int64_t M, int64_t K, const uint8_t* packed, const float* w_scale,
                            int64_t N, Epi epi, float* Y, int32_t* acc_out, hipStream_t s) {
-    if (gemv_supported(M, K))
+    if (gemv_supported(M, K, N))
         return launch_gemv(Xq, x_scale, rowsum, M, K, packed, w_scale, N, epi, Y, acc_out, s);
     return launch_gemm(Xq, x_scale, rowsum, M, K, packed, w_scale, N, epi, Y, acc_out, s);
 }

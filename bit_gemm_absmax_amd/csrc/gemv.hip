@@ -33,21 +33,22 @@ namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 
-constexpr int kRowDepth = 8;  // float4 per thread of an fp32 activation row (K <= 8192 at 256 threads)
-
+// QMAX 16-byte weight chunks per lane; with fp32 input the activation row
+// takes QMAX float4 per thread as well (quant_row_*: K <= 4 * NT * QMAX,
+// which the plan below guarantees).
 template <int MTILES, int NWV, int QMAX, bool F32IN>
 __global__ __launch_bounds__(NWV* kWave) void k_skinny(
     const float* __restrict__ X, const int8_t* __restrict__ Xq, const float* __restrict__ x_scale,
     const int32_t* __restrict__ x_rowsum, int M, int K, int rmsnorm, const float* __restrict__ gain,
-    float eps, const uint4* __restrict__ Wp, const float* __restrict__ w_scale, int N, uint32_t epi_flags,
+    float eps, const uint8_t* __restrict__ Wp, const float* __restrict__ w_scale, int N, uint32_t epi_flags,
     const float* residual, float* Y, int32_t* __restrict__ acc_out) {
     constexpr int NT = NWV * kWave;
-    extern __shared__ __align__(16) int8_t lds[];
+    constexpr int ROWS = 16 * MTILES;
+    extern __shared__ __align__(16) int8_t lds[];  // [fp32 input: xq, M <= 4 rows of K] [partials]
     __shared__ double dslot[NWV];
-    __shared__ float fslot[NWV];
-    __shared__ int islot[NWV];
-    __shared__ float gx[16 * MTILES];
-    __shared__ int rsx[16 * MTILES];
+    __shared__ float fslot[NWV], fslot2[NWV];
+    __shared__ int islot[4][NWV];
+    __shared__ float gx[4];
 
     const int lane = threadIdx.x % kWave;
     const int wave = threadIdx.x / kWave;
@@ -56,44 +57,61 @@ __global__ __launch_bounds__(NWV* kWave) void k_skinny(
     const int n0 = blockIdx.x * 16;
     const int C = K / 64;          // 64-weight chunks per row
     const int nq = (C + 3) / 4;    // chunk quads
+    const float ws = *w_scale;
 
-    // ---- loads first: the first fp32 activation row, then every weight chunk
-    float4 v[F32IN ? kRowDepth : 1];
-    if constexpr (F32IN) quant_row_load<NT, kRowDepth>(X, K, v);
+    // ---- every load up front, in the order they are needed: the first fp32
+    // activation row (and the norm gain), the weights, then the epilogue's
+    // operands for this thread's first output.
+    float4 v[F32IN ? QMAX : 1], gv[F32IN ? QMAX : 1];
+    const bool has_gain = rmsnorm != 0 && gain != nullptr;
+    if constexpr (F32IN) {
+        quant_row_load<NT, QMAX>(X, has_gain ? gain : nullptr, K, v, gv);
+        __builtin_amdgcn_sched_barrier(0);  // keep these loads ahead of the weights'
+    }
     uint4 w[QMAX];
     {
-        const int n = n0 + fr;
+        const int rows = N - n0 < 16 ? N - n0 : 16;
+        const Rsrc rw = make_rsrc(Wp + (int64_t)n0 * (K / 4), (uint32_t)rows * (uint32_t)(K / 4));
 #pragma unroll
         for (int i = 0; i < QMAX; ++i) {
             const int s = wave + i * NWV;
             const int c = 4 * s + fg;
-            w[i] = (s < nq && c < C && n < N) ? Wp[(int64_t)n * C + c] : make_uint4(0u, 0u, 0u, 0u);
+            w[i] = buf_load16(rw, (s < nq && c < C) ? (uint32_t)(fr * C + c) * 16u : kOob);
         }
+    }
+    const bool e_first = (int)threadIdx.x < M * 16;
+    const int e_m = threadIdx.x / 16, e_n = n0 + (int)(threadIdx.x % 16);
+    const bool e_ok = e_first && e_n < N;
+    const float e_res = buf_load4f(make_rsrc(residual, (epi_flags & kEpiResidual) ? 0x7FFFFFFFu : 0u),
+                                   e_ok ? (uint32_t)((int64_t)e_m * N + e_n) * 4u : kOob);
+    float e_xs = 0.0f;
+    int e_rs = 0;
+    if constexpr (!F32IN) {
+        e_xs = buf_load4f(make_rsrc(x_scale, (uint32_t)M * 4u), e_first ? (uint32_t)e_m * 4u : kOob);
+        e_rs = buf_load4i(make_rsrc(x_rowsum, (uint32_t)M * 4u), e_first ? (uint32_t)e_m * 4u : kOob);
     }
 
     // ---- activation rows: quantised here (fp32 input) or read as int8
     const int8_t* arow[MTILES];
     if constexpr (F32IN) {
-        int8_t* xq = lds;  // [M][K]
+        int8_t* xq = lds;
+        // Row 0 unconditionally (the host launches with M >= 1): a guard
+        // would let the compiler sink its loads behind the weights'.
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-            if (m < M) {
-                if (m > 0) quant_row_load<NT, kRowDepth>(X + (int64_t)m * K, K, v);
-                const QuantRow q = quant_row_finish<NT, kRowDepth>(v, K, rmsnorm != 0, gain, eps, xq + m * K,
-                                                                   dslot, fslot, islot, true);
-                if (threadIdx.x == 0) {
-                    gx[m] = q.gamma;
-                    rsx[m] = q.rowsum;
+            if (m == 0 || m < M) {
+                if (m > 0) {
+                    __syncthreads();  // the reduction slots are reused
+                    quant_row_load_x<NT, QMAX>(X + (int64_t)m * K, K, v);
                 }
+                const float g = quant_row_finish<NT, QMAX>(v, gv, K, rmsnorm != 0, has_gain, eps, xq + m * K,
+                                                           dslot, fslot, fslot2, islot[m]);
+                if (threadIdx.x == 0) gx[m] = g;
             }
         }
         __syncthreads();
         arow[0] = xq + (fr < M ? fr : M - 1) * K;
     } else {
-        if (threadIdx.x < M) {
-            gx[threadIdx.x] = x_scale[threadIdx.x];
-            rsx[threadIdx.x] = x_rowsum[threadIdx.x];
-        }
 #pragma unroll
         for (int t = 0; t < MTILES; ++t) {
             const int m = 16 * t + fr;
@@ -101,7 +119,9 @@ __global__ __launch_bounds__(NWV* kWave) void k_skinny(
         }
     }
 
-    // ---- contraction
+    // ---- contraction.  A chunk past the row end has zero weights (its load
+    // was out of range), so its activation offset is clamped to 0 and it adds
+    // nothing.
     v4i acc[MTILES];
 #pragma unroll
     for (int t = 0; t < MTILES; ++t) acc[t] = v4i{0, 0, 0, 0};
@@ -109,25 +129,24 @@ __global__ __launch_bounds__(NWV* kWave) void k_skinny(
     for (int i = 0; i < QMAX; ++i) {
         const int s = wave + i * NWV;
         if (s < nq) {
-            const int koff = 64 * (4 * s + fg);
-            const bool kin = (4 * s + fg) < C;
+            const int c = 4 * s + fg;
+            const int koff = c < C ? 64 * c : 0;
             const uint32_t wd[4] = {w[i].x, w[i].y, w[i].z, w[i].w};
 #pragma unroll
             for (int d = 0; d < 4; ++d) {
                 const v4i b = v4i{codes4(wd[d], 0), codes4(wd[d], 1), codes4(wd[d], 2), codes4(wd[d], 3)};
 #pragma unroll
                 for (int t = 0; t < MTILES; ++t) {
-                    const v4i a = kin ? *reinterpret_cast<const v4i*>(arow[t] + koff + 16 * d) : v4i{0, 0, 0, 0};
+                    const v4i a = *reinterpret_cast<const v4i*>(arow[t] + koff + 16 * d);
                     acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, acc[t], 0, 0, 0);
                 }
             }
         }
     }
 
-    // ---- per-wave partial tiles -> LDS in wave order -> epilogue
-    int* red = reinterpret_cast<int*>(lds + (F32IN ? ((4 * K + 15) / 16) * 16 : 0));  // [NWV][16*MTILES][16]
-    constexpr int ROWS = 16 * MTILES;
-    __syncthreads();
+    // ---- per-wave partial tiles -> LDS (a region of its own) -> epilogue,
+    // summing the waves in index order
+    int* red = reinterpret_cast<int*>(lds + (F32IN ? 4 * K : 0));  // [NWV][ROWS][16]
 #pragma unroll
     for (int t = 0; t < MTILES; ++t)
 #pragma unroll
@@ -136,23 +155,33 @@ __global__ __launch_bounds__(NWV* kWave) void k_skinny(
             if (m < M) red[(wave * ROWS + m) * 16 + fr] = acc[t][r];
         }
     __syncthreads();
-    const float ws = *w_scale;
     for (int i = threadIdx.x; i < M * 16; i += NT) {
         const int m = i / 16, col = i % 16;
         const int n = n0 + col;
         if (n < N) {
+            const bool first = i == (int)threadIdx.x;
             int a = 0;
 #pragma unroll
             for (int q = 0; q < NWV; ++q) a += red[(q * ROWS + m) * 16 + col];
-            a -= rsx[m];
-            const float d = (gx[m] * ws) / 127.0f;
+            float xs;
+            if constexpr (F32IN) {
+                int rs = 0;
+#pragma unroll
+                for (int q = 0; q < NWV; ++q) rs += islot[m][q];
+                a -= rs;
+                xs = gx[m];
+            } else {
+                a -= first ? e_rs : x_rowsum[m];
+                xs = first ? e_xs : x_scale[m];
+            }
+            const float d = (xs * ws) / 127.0f;
             float y = (float)a * d;
             if (epi_flags & kEpiRelu2) {
                 const float tt = y > 0.0f ? y : 0.0f;
                 y = tt * tt;
             }
             const int64_t o = (int64_t)m * N + n;
-            if (epi_flags & kEpiResidual) y = y + residual[o];
+            if (epi_flags & kEpiResidual) y = y + (first ? e_res : residual[o]);
             if (Y != nullptr) Y[o] = y;
             if (acc_out != nullptr) acc_out[o] = a;
         }
@@ -163,7 +192,10 @@ struct Plan {
     int nw, qmax;
 };
 
-// Waves per workgroup and weight loads per lane from the chunk-quad count.
+// Waves per workgroup and weight loads per lane from the chunk-quad count:
+// (4, 2) up to K = 2048, (4, 4) up to 4096, (8, 4) up to 8192, (8, 8) up to
+// 16384.  In each case K <= 4 * 64 * nw * qmax, so an fp32 row fits in qmax
+// float4 per thread.
 bool plan(int64_t K, Plan& p) {
     const int64_t nq = (K / 64 + 3) / 4;
     p.nw = quant_threads(K) / kWave;  // 4 waves up to K = 4096, then 8 (same size as the quantiser)
@@ -182,9 +214,9 @@ hipError_t go(const float* X, const int8_t* Xq, const float* xs, const int32_t* 
               const float* residual, float* Y, int32_t* acc_out, hipStream_t s) {
     const unsigned blocks = (unsigned)((N + 15) / 16);
     const size_t red = (size_t)NWV * 16 * MT * 16 * sizeof(int);
-    const size_t lds = (F ? ((4 * (size_t)K + 15) / 16) * 16 : 0) + red;
+    const size_t lds = (F ? 4 * (size_t)K : 0) + red;
     hipLaunchKernelGGL((k_skinny<MT, NWV, Q, F>), dim3(blocks), dim3(NWV * kWave), lds, s, X, Xq, xs, rs, (int)M,
-                       (int)K, rms ? 1 : 0, gain, eps, reinterpret_cast<const uint4*>(packed), ws, (int)N, epi,
+                       (int)K, rms ? 1 : 0, gain, eps, packed, ws, (int)N, epi,
                        residual, Y, acc_out);
     return hipGetLastError();
 }
@@ -198,7 +230,6 @@ hipError_t go_mt(const Plan& p, const float* X, const int8_t* Xq, const float* x
         return go<MT, NWV, Q, F>(X, Xq, xs, rs, M, K, rms, gain, eps, packed, ws, N, epi, residual, Y, acc_out, s);
     BL_SK(4, 2)
     BL_SK(4, 4)
-    BL_SK(8, 2)
     BL_SK(8, 4)
     BL_SK(8, 8)
 #undef BL_SK
@@ -207,9 +238,10 @@ hipError_t go_mt(const Plan& p, const float* X, const int8_t* Xq, const float* x
 
 }  // namespace
 
-bool gemv_supported(int64_t M, int64_t K) {
+// Output offsets are taken in 32-bit bytes by the buffer loads: M * N * 4 < 2^31.
+bool gemv_supported(int64_t M, int64_t K, int64_t N) {
     Plan p;
-    return M >= 1 && M <= 64 && K <= 32768 && plan(K, p);
+    return M >= 1 && M <= 64 && K <= 32768 && M * N < (1LL << 29) && plan(K, p);
 }
 
 hipError_t launch_gemv(const int8_t* Xq, const float* xs, const int32_t* rs, int64_t M, int64_t K,
@@ -232,10 +264,9 @@ hipError_t launch_gemv(const int8_t* Xq, const float* xs, const int32_t* rs, int
 }
 
 bool decode_supported(int64_t M, int64_t K, int64_t N) {
-    (void)N;
     Plan p;
-    if (M < 1 || M > 4 || !plan(K, p) || quant_threads(K) != p.nw * kWave) return false;
-    return K <= (int64_t)4 * p.nw * kWave * kRowDepth;  // quant_row_*: kRowDepth float4 per thread
+    if (M < 1 || M > 4 || !gemv_supported(M, K, N) || !plan(K, p) || quant_threads(K) != p.nw * kWave) return false;
+    return K <= (int64_t)4 * p.nw * kWave * p.qmax;  // quant_row_*: qmax float4 per thread
 }
 
 hipError_t launch_decode_bitlinear(const float* X, int64_t M, int64_t K, bool rmsnorm, const float* gain, float eps,

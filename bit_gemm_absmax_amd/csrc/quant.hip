@@ -4,7 +4,7 @@
 // in normalisation layers; "BitNetConfig": rms_norm_eps).
 //
 // One workgroup per token row (quant_row_* in bl_device.h).
-// The row is loaded once into registers (up to 8 float4 per thread), so the
+// The row is loaded once into registers (8 float4 per thread), so the
 // row-wide reductions -- sum of squares (binary64), max |z| and the int8 row
 // sum -- never re-read HBM.
 #include "bl_device.h"
@@ -20,16 +20,23 @@ __global__ __launch_bounds__(NT) void k_quant(const float* __restrict__ X, int K
                                               int32_t* __restrict__ rowsum) {
     constexpr int NW = NT / kWave;
     __shared__ double dslot[NW];
-    __shared__ float fslot[NW];
+    __shared__ float fslot[NW], fslot2[NW];
     __shared__ int islot[NW];
     const int64_t m = blockIdx.x;
-    float4 v[8];
-    quant_row_load<NT, 8>(X + m * K, K, v);
-    const QuantRow q = quant_row_finish<NT, 8>(v, K, rmsnorm != 0, gain, eps, Xq + m * K, dslot, fslot, islot,
-                                               rowsum != nullptr);
+    float4 v[8], gv[8];
+    quant_row_load<NT, 8>(X + m * K, rmsnorm ? gain : nullptr, K, v, gv);
+    const float gamma = quant_row_finish<NT, 8>(v, gv, K, rmsnorm != 0, rmsnorm && gain != nullptr, eps,
+                                                Xq + m * K, dslot, fslot, fslot2,
+                                                rowsum != nullptr ? islot : nullptr);
+    if (rowsum != nullptr) __syncthreads();
     if (threadIdx.x == 0) {
-        scale[m] = q.gamma;
-        if (rowsum != nullptr) rowsum[m] = q.rowsum;
+        scale[m] = gamma;
+        if (rowsum != nullptr) {
+            int t = 0;
+#pragma unroll
+            for (int i = 0; i < NW; ++i) t += islot[i];
+            rowsum[m] = t;
+        }
     }
 }
 
