@@ -217,7 +217,7 @@ def main():
     traffic = traffic_from_profile("decode_up_m1", ["gemv.hip", "bl_device.h"])
     roofline = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": "k_decode_bitlinear (absmax quant + up BitLinear + ReLU^2, M=1, K=2560, N=6912)",
+                "kernel": "k_skinny<1,4,4,true> (absmax quant + up BitLinear + ReLU^2, M=1, K=2560, N=6912)",
                 "bytes_per_launch": PACKED_BYTES_MATRIX, "us_per_launch": round(gemv_s * 1e6, 3),
                 "down_us_per_launch": round(gemv_dn_s * 1e6, 3)}
     del layers, stacks, ups, dns
@@ -264,7 +264,7 @@ def main():
                    "roofline": {"bound": "mfma", "achieved": round(tops_up, 2), "peak": INT8_PEAK_TOPS,
                                 "unit": "TOPS", "frac": round(tops_up / INT8_PEAK_TOPS, 4),
                                 "traffic": traffic_from_profile("gemm_up_m4096", ["gemm.hip", "bl_device.h"]),
-                                "kernel": "k_gemm (M=4096, K=2560, N=6912, +ReLU^2)",
+                                "kernel": "k_gemm_pipe<256,256,4,2,3,1> (M=4096, K=2560, N=6912, +ReLU^2)",
                                 "ops_per_launch": int(ops), "us_per_launch": round(up_s * 1e6, 2),
                                 "down_us_per_launch": round(dn_s * 1e6, 2),
                                 "down_tops": round(tops_dn, 2)}}
