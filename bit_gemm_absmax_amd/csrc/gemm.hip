@@ -14,6 +14,8 @@
 // its L2.
 // The MFMA accumulates codes (q + 1); the epilogue subtracts the token's
 // activation row sum, dequantises and applies the fused ReLU^2 / residual.
+#include <atomic>
+
 #include "bl_device.h"
 #include "bl_internal.h"
 
@@ -124,19 +126,18 @@ __global__ __launch_bounds__(WM* WN* kWave, OCC) void k_gemm_pipe(
     const int fg = lane >> 4;
 
     // Epilogue operands, loaded now so their latency hides under the main
-    // loop: lane l holds rows (wave row 0 + 64 h + l)'s row sum and dequant
-    // factor; the epilogue fetches them per row with a cross-lane read.
-    constexpr int RPL = (TM + kWave - 1) / kWave;
-    int row_rs[RPL];
-    float row_d[RPL];
+    // loop: in fragment fm this lane's outputs belong to token
+    // m0 + wm*TM + 16*fm + fr (see the output layout below).
+    int row_rs[FM];
+    float row_d[FM];
     {
         const float wsc = *w_scale;
 #pragma unroll
-        for (int h = 0; h < RPL; ++h) {
-            int m = m0 + wm * TM + h * kWave + lane;
+        for (int fm = 0; fm < FM; ++fm) {
+            int m = m0 + wm * TM + fm * 16 + (lane & 15);
             m = m < M ? m : M - 1;
-            row_rs[h] = rowsum[m];
-            row_d[h] = (x_scale[m] * wsc) / 127.0f;
+            row_rs[fm] = rowsum[m];
+            row_d[fm] = (x_scale[m] * wsc) / 127.0f;
         }
     }
 
@@ -174,7 +175,7 @@ __global__ __launch_bounds__(WM* WN* kWave, OCC) void k_gemm_pipe(
             const v4i bv = v4i{codes4(wq[fn], 0), codes4(wq[fn], 1), codes4(wq[fn], 2), codes4(wq[fn], 3)};
 #pragma unroll
             for (int fm = 0; fm < FM; ++fm)
-                acc[fm][fn] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[fm], bv, acc[fm][fn], 0, 0, 0);
+                acc[fm][fn] = __builtin_amdgcn_mfma_i32_16x16x64_i8(bv, a[fm], acc[fm][fn], 0, 0, 0);
         }
     };
     // Stage st is ready in LDS for every wave: this wave's loads have landed
@@ -227,72 +228,62 @@ __global__ __launch_bounds__(WM* WN* kWave, OCC) void k_gemm_pipe(
         }
     }
 
-    // Epilogue.  acc holds 4 consecutive rows of one column per lane, so
-    // direct stores would write 64-byte pieces of 4 rows.  Instead each wave
-    // stages 16 rows x TN of finished values (dequant, ReLU^2) in LDS, with a
-    // row pitch of TN + 4 floats (the minimum, 2-way, conflict for the
-    // 64-lane writes), then writes whole rows with 16-byte stores, adding the
-    // residual there.  The main loop's buffers are free after the barrier.
-    __syncthreads();
-    constexpr int PITCH = TN + 4;
-    float* stage = reinterpret_cast<float*>(smem) + wave * 16 * PITCH;
-    static_assert(NW * 16 * PITCH * 4 <= NBUF * STAGE, "epilogue staging fits the LDS ring");
-    static_assert(TN % 4 == 0, "16-byte row stores");
+    // Epilogue.  The weights are the MFMA's A operand and the tokens its B
+    // operand, so a fragment is 16 outputs x 16 tokens and lane (fr, fg)
+    // holds outputs 4fg..4fg+3 of token fr: four consecutive floats of one
+    // row of Y, written with one 16-byte store (the two fragments of a
+    // 128-byte line go out back to back and merge in L2).  Partial tiles and
+    // N % 4 != 0 take the element-wise path.
+    const bool whole = m0 + BM <= M && n0 + BN <= N && (N % 4) == 0;
+    const bool relu2 = (epi.flags & kEpiRelu2) != 0;
+    const bool resid = (epi.flags & kEpiResidual) != 0;
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm) {
+        const int m = m0 + wm * TM + fm * 16 + fr;
+        const int64_t row = (int64_t)m * N;
+        float4 res[FN];
+        if (whole && resid) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int ri = fm * 16 + 4 * fg + r;     // row inside the wave tile
-            const int m = m0 + wm * TM + ri;
-            const int rsum = __shfl(row_rs[fm / 4], ri % kWave, kWave);
-            const float d = __shfl(row_d[fm / 4], ri % kWave, kWave);
-#pragma unroll
-            for (int fn = 0; fn < FN; ++fn) {
-                const int av = acc[fm][fn][r] - rsum;
-                float y = (float)av * d;
-                if (epi.flags & kEpiRelu2) {
-                    const float tt = y > 0.0f ? y : 0.0f;
-                    y = tt * tt;
-                }
-                stage[(4 * fg + r) * PITCH + fn * 16 + fr] = y;
-                const int n = n0 + wn * TN + fn * 16 + fr;
-                if (acc_out != nullptr && m < M && n < N) acc_out[(int64_t)m * N + n] = av;
-            }
+            for (int fn = 0; fn < FN; ++fn)
+                res[fn] = *reinterpret_cast<const float4*>(epi.residual + row + n0 + wn * TN + fn * 16 + 4 * fg);
         }
-        // the wave reads back only its own rows: no workgroup barrier needed,
-        // the LDS counter orders this wave's writes before its reads
-        constexpr int VPR = TN / 4;                  // 16-byte vectors per row
 #pragma unroll
-        for (int i = lane; i < 16 * VPR; i += kWave) {
-            const int rr = i / VPR, cv = i % VPR;
-            const int m = m0 + wm * TM + fm * 16 + rr;
-            const int n = n0 + wn * TN + cv * 4;
-            float4 v = *reinterpret_cast<const float4*>(&stage[rr * PITCH + cv * 4]);
-            if (m < M && Y != nullptr) {
-                const int64_t o = (int64_t)m * N + n;
-                if (n + 3 < N && (N % 4) == 0) {
-                    if (epi.flags & kEpiResidual) {
-                        const float4 res = *reinterpret_cast<const float4*>(epi.residual + o);
-                        v.x = v.x + res.x;
-                        v.y = v.y + res.y;
-                        v.z = v.z + res.z;
-                        v.w = v.w + res.w;
-                    }
-                    *reinterpret_cast<float4*>(Y + o) = v;
-                } else {
-                    const float e[4] = {v.x, v.y, v.z, v.w};
+        for (int fn = 0; fn < FN; ++fn) {
+            const int n = n0 + wn * TN + fn * 16 + 4 * fg;
+            int av[4];
+            float y[4];
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        if (n + q < N) {
-                            float yq = e[q];
-                            if (epi.flags & kEpiResidual) yq = yq + epi.residual[o + q];
-                            Y[o + q] = yq;
-                        }
+            for (int r = 0; r < 4; ++r) {
+                av[r] = acc[fm][fn][r] - row_rs[fm];
+                float t = (float)av[r] * row_d[fm];
+                if (relu2) {
+                    t = t > 0.0f ? t : 0.0f;
+                    t = t * t;
+                }
+                y[r] = t;
+            }
+            if (whole) {
+                if (resid) {
+                    y[0] = y[0] + res[fn].x;
+                    y[1] = y[1] + res[fn].y;
+                    y[2] = y[2] + res[fn].z;
+                    y[3] = y[3] + res[fn].w;
+                }
+                if (Y != nullptr) *reinterpret_cast<float4*>(Y + row + n) = make_float4(y[0], y[1], y[2], y[3]);
+                if (acc_out != nullptr)
+                    *reinterpret_cast<int4*>(acc_out + row + n) = make_int4(av[0], av[1], av[2], av[3]);
+            } else if (m < M) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    if (n + r < N) {
+                        float t = y[r];
+                        if (resid) t = t + epi.residual[row + n + r];
+                        if (Y != nullptr) Y[row + n + r] = t;
+                        if (acc_out != nullptr) acc_out[row + n + r] = av[r];
                     }
                 }
             }
         }
-        __builtin_amdgcn_s_waitcnt(0xC07F);          // lgkmcnt(0): reads done before the next fm reuses the rows
     }
 }
 
@@ -309,16 +300,37 @@ hipError_t launch_pipe(const int8_t* Xq, const float* xs, const int32_t* rs, int
 
 }  // namespace
 
-// Tile choice: 256-row tiles with 256 columns, or 160 columns when N is a
-// multiple of 160 and not of 256 (2560 -> 16 tiles of 160, one per CU row of
-// work); 128-row tiles for mid-size M.
+// Compute units of the current device, looked up once per device.
+int cu_count() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cache[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
+// Tile choice.  One workgroup fits a CU (the LDS ring takes 120 KB), so the
+// time goes as whole rounds of tiles over the CUs times the tile's work:
+// 256x256 tiles (2x4 waves of 128x64: each unpacked weight fragment feeds 8
+// MFMAs) unless 256x160 tiles (4x2 waves of 64x80, weighted 10% less
+// efficient) need fewer rounds' worth of work -- e.g. N = 2560 at M = 4096
+// is 160 tiles of 256 but 256 tiles of 160, one per CU.  128x128 tiles for
+// M <= 128.
 hipError_t launch_gemm(const int8_t* Xq, const float* xs, const int32_t* rs, int64_t M, int64_t K,
                        const uint8_t* packed, const float* ws, int64_t N, Epi epi, float* Y,
                        int32_t* acc_out, hipStream_t s) {
     if (M > 128) {
-        if (N % 256 != 0 && N % 160 == 0)
+        const int64_t cus = cu_count();
+        const int64_t mt = (M + 255) / 256;
+        const int64_t r256 = (mt * ((N + 255) / 256) + cus - 1) / cus;
+        const int64_t r160 = (mt * ((N + 159) / 160) + cus - 1) / cus;
+        if (r160 * 160 * 10 < r256 * 256 * 9)
             return launch_pipe<256, 160, 4, 2, 3, 1>(Xq, xs, rs, M, K, packed, ws, N, epi, Y, acc_out, s);
-        return launch_pipe<256, 256, 4, 2, 3, 1>(Xq, xs, rs, M, K, packed, ws, N, epi, Y, acc_out, s);
+        return launch_pipe<256, 256, 2, 4, 3, 1>(Xq, xs, rs, M, K, packed, ws, N, epi, Y, acc_out, s);
     }
     return launch_pipe<128, 128, 2, 2, 3, 1>(Xq, xs, rs, M, K, packed, ws, N, epi, Y, acc_out, s);
 }
