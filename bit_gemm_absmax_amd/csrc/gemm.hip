@@ -26,9 +26,9 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 
 constexpr int kXcds = 8;
 
-// Pipeline: k advances 128 per stage and NBUF stages ring through LDS,
-// filled by direct global->LDS loads (global_load_lds_dwordx4) issued NBUF-1
-// stages ahead, so several stages of L2/HBM latency overlap the MFMAs.
+// Pipeline: k advances 128 per stage and NBUF (4) stages ring through LDS,
+// filled by direct global->LDS loads (global_load_lds_dwordx4) issued up to
+// four stages ahead, so L2/HBM latency overlaps the MFMAs.
 // A DMA instruction writes 64 lanes x 16 bytes contiguously; the global
 // address each lane fetches is chosen so that:
 //   - activations: one instruction covers 8 rows x 128 bytes (whole cache
@@ -39,53 +39,41 @@ constexpr int kXcds = 8;
 //     contiguous 256-byte span.
 // Rows past M or N are clamped to the last row for loading (never stored).
 
-// s_waitcnt on the vector-memory counter (at most N loads in flight) and
-// the LDS counter (all LDS reads returned); gfx9 encoding: vmcnt bits [3:0]
-// and [15:14], expcnt [6:4] left at max, lgkmcnt [11:8] = 0.
+// s_waitcnt on the vector-memory counter only: at most N loads in flight,
+// LDS counter left at its maximum; gfx9 encoding: vmcnt bits [3:0] and
+// [15:14], expcnt [6:4], lgkmcnt [11:8].
 template <int N>
-__device__ __forceinline__ void wait_vm_lgkm0() {
+__device__ __forceinline__ void wait_vm() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4));
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
-
-template <int PER_STAGE, int MAXS>
-__device__ __forceinline__ void wait_stages(int n) {
-    // n stages (PER_STAGE loads each) may stay in flight; n <= MAXS
-    if constexpr (MAXS >= 3) if (n >= 3) { wait_vm_lgkm0<3 * PER_STAGE>(); return; }
-    if constexpr (MAXS >= 2) if (n == 2) { wait_vm_lgkm0<2 * PER_STAGE>(); return; }
-    if constexpr (MAXS >= 1) if (n == 1) { wait_vm_lgkm0<1 * PER_STAGE>(); return; }
-    wait_vm_lgkm0<0>();
-}
-
 constexpr int kBK = 128;             // k per stage
-constexpr int kAChunks = kBK / 16;   // 16-byte activation chunks per row per stage
 
-// Issue one stage of direct global->LDS loads for this wave.
+typedef __attribute__((address_space(3))) void* lds_ptr;
+
+// Issue one stage of direct buffer->LDS loads for this wave.  A lane's byte
+// offset is its part inside an 8-row (activations) or 32-row (weights)
+// block, va / vb, fixed for the whole loop; the block's row offset, the tile
+// origin and the stage's k are wave-uniform and go in the scalar offset.
+// Reads past the tensor return zero (the descriptor's size), so no row or
+// k clamp is needed: rows past M or N are never stored, and when
+// K % 128 == 64 the second half of the last stage is never read.
 //   activations: A_BLKS instructions, block j = rows 8j..8j+7 of the tile;
 //   weights: B_INS instructions, each 32 rows x both 64-k chunks.
 template <int A_BLKS, int B_INS>
-__device__ __forceinline__ void issue_stage(const int8_t* Xq, int M, int K, int m0, int lane, int wave,
-                                            const uint4* Wp, int N, int C, int n0, int8_t* base,
-                                            int a_stage, int st) {
-    const int r8 = lane >> 3;                  // row inside the 8-row block
-    const int chunk = (lane & 7) ^ r8;         // global chunk this lane fetches
+__device__ __forceinline__ void issue_stage(Rsrc ra, Rsrc rb, uint32_t va, uint32_t vb, uint32_t a_s, uint32_t b_s,
+                                            uint32_t a_blk, uint32_t b_blk, int8_t* base, int a_stage, int wave) {
 #pragma unroll
     for (int i = 0; i < A_BLKS; ++i) {
-        const int blk = wave * A_BLKS + i;
-        int m = m0 + blk * 8 + r8;
-        m = m < M ? m : M - 1;
-        int k = st * kBK + chunk * 16;
-        k = k < K ? k : k - 64;                // K % 128 == 64: the unused half re-reads valid bytes
-        __builtin_amdgcn_global_load_lds(Xq + (int64_t)m * K + k, base + blk * 1024, 16, 0, 0);
+        const int j = wave * A_BLKS + i;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr)(base + j * 1024), 16, va, a_s + (uint32_t)j * a_blk,
+                                                 0, 0);
     }
-    int kc = st * 2 + (lane >> 5);
-    kc = kc < C ? kc : C - 1;                  // K % 128 == 64: the last half stage repeats a chunk
 #pragma unroll
     for (int i = 0; i < B_INS; ++i) {
-        const int blk = wave * B_INS + i;
-        int n = n0 + blk * 32 + (lane & 31);
-        n = n < N ? n : N - 1;
-        __builtin_amdgcn_global_load_lds(Wp + (int64_t)n * C + kc, base + a_stage + blk * 1024, 16, 0, 0);
+        const int j = wave * B_INS + i;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr)(base + a_stage + j * 1024), 16, vb,
+                                                 b_s + (uint32_t)j * b_blk, 0, 0);
     }
 }
 
@@ -108,7 +96,7 @@ __global__ __launch_bounds__(WM* WN* kWave, OCC) void k_gemm_pipe(
     __shared__ __align__(1024) int8_t smem[NBUF * STAGE];
 
     const int lane = threadIdx.x % kWave;
-    const int wave = threadIdx.x / kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int wm = wave / WN;
     const int wn = wave % WN;
 
@@ -125,21 +113,25 @@ __global__ __launch_bounds__(WM* WN* kWave, OCC) void k_gemm_pipe(
     const int fr = lane & 15;
     const int fg = lane >> 4;
 
-    // Epilogue operands, loaded now so their latency hides under the main
-    // loop: in fragment fm this lane's outputs belong to token
-    // m0 + wm*TM + 16*fm + fr (see the output layout below).
-    int row_rs[FM];
-    float row_d[FM];
-    {
-        const float wsc = *w_scale;
-#pragma unroll
-        for (int fm = 0; fm < FM; ++fm) {
-            int m = m0 + wm * TM + fm * 16 + (lane & 15);
-            m = m < M ? m : M - 1;
-            row_rs[fm] = rowsum[m];
-            row_d[fm] = (x_scale[m] * wsc) / 127.0f;
-        }
-    }
+    // DMA descriptors and this lane's fixed offsets (bytes).  Activations:
+    // lane (r8 = lane/8, c = lane%8) of a block fetches row r8 of the block,
+    // 16-byte chunk c ^ r8, stored at slot c of that row in LDS (so the 16
+    // rows an MFMA fragment reads at one k sit in distinct banks).  Weights:
+    // lane l of a block fetches row l%32, chunk l/32 of the stage
+    // (chunk-major in LDS).
+    const Rsrc ra = make_rsrc(Xq, (uint32_t)M * (uint32_t)K);
+    const Rsrc rb = make_rsrc(Wp, (uint32_t)N * (uint32_t)C * 16u);
+    const uint32_t va = (uint32_t)(lane >> 3) * (uint32_t)K + (uint32_t)((lane & 7) ^ (lane >> 3)) * 16u;
+    const uint32_t vb = (uint32_t)(lane & 31) * (uint32_t)C * 16u + (uint32_t)(lane >> 5) * 16u;
+    const uint32_t a_blk = 8u * (uint32_t)K, b_blk = 32u * (uint32_t)C * 16u;
+    const uint32_t a_base = (uint32_t)m0 * (uint32_t)K, b_base = (uint32_t)n0 * (uint32_t)C * 16u;
+    // A stage index past the last one gets a scalar offset past every
+    // descriptor: its loads write zeros to LDS without touching memory, so
+    // the issue is branch-free (those buffers are never read).
+#define BL_ISSUE(st)                                                                                          \
+    issue_stage<A_BLKS, B_INS>(ra, rb, va, vb, (st) < nst ? a_base + (uint32_t)(st) * kBK : kOob,              \
+                               (st) < nst ? b_base + (uint32_t)(st) * 32u : kOob, a_blk, b_blk,                \
+                               smem + ((st) % NBUF) * STAGE, A_STAGE, wave)
 
     v4i acc[FM][FN];
 #pragma unroll
@@ -147,10 +139,9 @@ __global__ __launch_bounds__(WM* WN* kWave, OCC) void k_gemm_pipe(
 #pragma unroll
         for (int j = 0; j < FN; ++j) acc[i][j] = v4i{0, 0, 0, 0};
 
-    constexpr int P = NBUF - 1;
+    static_assert(NBUF == 4, "two stages are read while two more are in flight");
 #pragma unroll
-    for (int p = 0; p < P; ++p)
-        if (p < nst) issue_stage<A_BLKS, B_INS>(Xq, M, K, m0, lane, wave, Wp, N, C, n0, smem + p * STAGE, A_STAGE, p);
+    for (int p = 0; p < NBUF - 1; ++p) BL_ISSUE(p);
 
     // Fragments of one 64-k step: activation rows R (block R/8, slot
     // (4s + fg) ^ (R % 8)) and the packed weight word g of 16 rows.
@@ -178,54 +169,76 @@ __global__ __launch_bounds__(WM* WN* kWave, OCC) void k_gemm_pipe(
                 acc[fm][fn] = __builtin_amdgcn_mfma_i32_16x16x64_i8(bv, a[fm], acc[fm][fn], 0, 0, 0);
         }
     };
-    // Stage st is ready in LDS for every wave: this wave's loads have landed
-    // (vmcnt) and the execution barrier waits for the others.  The same wait
-    // drains this wave's LDS reads, so once all waves pass the barrier no
-    // read of the previous stage's buffer is pending and the DMA issued right
-    // after may overwrite it.
-    auto stage_ready = [&](int st) {
-        const int ahead = nst - 1 - st;
-        wait_stages<LOADS, P - 1>(ahead < P - 1 ? ahead : P - 1);
-        __builtin_amdgcn_s_barrier();
-    };
-
-    // Full stages: both 64-k steps, branch-free, so the second step's
-    // fragment reads are in flight while the first step's MFMAs run.  The
-    // last stage is peeled (it may hold a single 64-k step).
-    for (int st = 0; st + 1 < nst; ++st) {
-        stage_ready(st);
-        if (st + P < nst)
-            issue_stage<A_BLKS, B_INS>(Xq, M, K, m0, lane, wave, Wp, N, C, n0,
-                                       smem + ((st + P) % NBUF) * STAGE, A_STAGE, st + P);
-        v4i a0[FM], a1[FM];
-        uint32_t w0[FN], w1[FN];
-        load_frags(st, 0, a0, w0);
-        __builtin_amdgcn_sched_barrier(0);
-        // second step's reads ride inside the first step's MFMA stream:
-        // per weight fragment, its unpack, then MFMAs with reads between
-        load_frags(st, 1, a1, w1);
-        mma(a0, w0);
+    auto interleave = [&](bool dma) {
+        // per weight fragment: its unpack, then MFMAs with LDS reads between;
+        // in the first step of a stage the DMA instructions of stage s+3 are
+        // spread through the MFMA stream, one or two per fragment, instead
+        // of leaving every wave to issue them in a burst after the barrier
 #pragma unroll
         for (int g = 0; g < FN; ++g) {
             __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);   // VALU: unpack
             __builtin_amdgcn_sched_group_barrier(0x008, FM / 2, 0);  // MFMA
             __builtin_amdgcn_sched_group_barrier(0x100, (FM + FN + FN - 1) / FN, 0);  // DS read
+            if (dma) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM (DMA)
+            if (dma && g == 0 && LOADS > FN)
+                __builtin_amdgcn_sched_group_barrier(0x020, LOADS > FN ? LOADS - FN : 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x008, FM - FM / 2, 0);  // MFMA
         }
+    };
+
+    // Schedule.  Stages s and s+1 are readable while s+2 and s+3 are in
+    // flight.  Within stage s the second 64-k step's fragments are read
+    // during the first step's MFMAs, and the first fragments of stage s+1
+    // during the second step's, so after a barrier the MFMAs resume at once.
+    // The DMA of stage s+3 goes out during the first step, into the buffer
+    // of stage s-1, which the barrier ending stage s-1 freed.  At the end of
+    // stage s this wave waits for its own loads of stage s+2 (stage s+3 may
+    // stay in flight) and the barrier makes stage s+2 visible from every
+    // wave.
+    wait_vm<LOADS>();
+    __builtin_amdgcn_s_barrier();
+    v4i a0[FM], a1[FM];
+    uint32_t w0[FN], w1[FN];
+    load_frags(0, 0, a0, w0);
+    for (int st = 0; st + 1 < nst; ++st) {   // full 128-k stages
+        load_frags(st, 1, a1, w1);
+        BL_ISSUE(st + NBUF - 1);
+        mma(a0, w0);
+        interleave(true);
         __builtin_amdgcn_sched_barrier(0);
+        load_frags(st + 1, 0, a0, w0);
         mma(a1, w1);
+        interleave(false);
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vm<LOADS>();
+        __builtin_amdgcn_s_barrier();
     }
+#undef BL_ISSUE
+    // Last stage (one or two 64-k steps).  The epilogue operands are loaded
+    // between its two steps, into the registers the first step's fragments
+    // free, so their latency hides under the second step's MFMAs (held any
+    // longer they would push accumulators out to scratch).  In fragment fm
+    // this lane's outputs belong to token m0 + wm*TM + 16*fm + fr (see the
+    // output layout below).
+    int row_rs[FM];
+    float row_d[FM];
     {
         const int st = nst - 1;
-        stage_ready(st);
-        v4i a[FM];
-        uint32_t w[FN];
-        load_frags(st, 0, a, w);
-        mma(a, w);
-        if (st * kBK + 64 < K) {
-            load_frags(st, 1, a, w);
-            mma(a, w);
+        const bool two = st * kBK + 64 < K;
+        if (two) load_frags(st, 1, a1, w1);
+        mma(a0, w0);
+        __builtin_amdgcn_sched_barrier(0);
+        const float wsc = *w_scale;
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm) {
+            int m = m0 + wm * TM + fm * 16 + fr;
+            m = m < M ? m : M - 1;
+            row_rs[fm] = rowsum[m];
+            row_d[fm] = (x_scale[m] * wsc) / 127.0f;
         }
+        __builtin_amdgcn_sched_barrier(0);
+        if (two) mma(a1, w1);
+        wait_vm<0>();   // no DMA may still write LDS when the workgroup ends
     }
 
     // Epilogue.  The weights are the MFMA's A operand and the tokens its B
@@ -313,7 +326,7 @@ int cu_count() {
     return n;
 }
 
-// Tile choice.  One workgroup fits a CU (the LDS ring takes 120 KB), so the
+// Tile choice.  One workgroup fits a CU (the LDS ring takes 160 KB), so the
 // time goes as whole rounds of tiles over the CUs times the tile's work:
 // 256x256 tiles (2x4 waves of 128x64: each unpacked weight fragment feeds 8
 // MFMAs) unless 256x160 tiles (4x2 waves of 64x80, weighted 10% less
@@ -329,10 +342,10 @@ hipError_t launch_gemm(const int8_t* Xq, const float* xs, const int32_t* rs, int
         const int64_t r256 = (mt * ((N + 255) / 256) + cus - 1) / cus;
         const int64_t r160 = (mt * ((N + 159) / 160) + cus - 1) / cus;
         if (r160 * 160 * 10 < r256 * 256 * 9)
-            return launch_pipe<256, 160, 4, 2, 3, 1>(Xq, xs, rs, M, K, packed, ws, N, epi, Y, acc_out, s);
-        return launch_pipe<256, 256, 2, 4, 3, 1>(Xq, xs, rs, M, K, packed, ws, N, epi, Y, acc_out, s);
+            return launch_pipe<256, 160, 4, 2, 4, 1>(Xq, xs, rs, M, K, packed, ws, N, epi, Y, acc_out, s);
+        return launch_pipe<256, 256, 2, 4, 4, 1>(Xq, xs, rs, M, K, packed, ws, N, epi, Y, acc_out, s);
     }
-    return launch_pipe<128, 128, 2, 2, 3, 1>(Xq, xs, rs, M, K, packed, ws, N, epi, Y, acc_out, s);
+    return launch_pipe<128, 128, 2, 2, 4, 1>(Xq, xs, rs, M, K, packed, ws, N, epi, Y, acc_out, s);
 }
 
 hipError_t launch_contract(const int8_t* Xq, const float* x_scale, const int32_t* rowsum,
