@@ -62,6 +62,121 @@ def traffic_from_profile(kernel_key, sources):
     return rec.get("bytes_per_launch")
 
 
+# Kernels whose HBM traffic is taken from rocprofv3 counters: key -> (kernel
+# name prefix in the trace, workgroups, sources whose hash the figures belong to)
+TRAFFIC_KERNELS = {
+    "decode_up_m1": ("k_skinny<1, 4, 4, true>", 432, ("gemv.hip", "bl_device.h")),
+    "gemm_up_m4096": ("k_gemm_pipe<256, 256, 2, 4, 4, 1>", 432, ("gemm.hip", "bl_device.h")),
+    "gemm_down_m4096": ("k_gemm_pipe<256, 160, 4, 2, 4, 1>", 256, ("gemm.hip", "bl_device.h")),
+}
+CALIB_BYTES = 256 << 20   # the calibration kernel reads and writes 256 MiB
+PMC_CMDS = [
+    "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o p -- python3 bench.py --pmc-drive",
+    "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o p -- python3 bench.py --pmc-drive",
+    "python3 bench.py --traffic-from gpurun_out/pmc_fetch gpurun_out/pmc_write",
+]
+
+
+def pmc_drive():
+    """The launches the traffic counters are read from: the decode up kernel
+    over 16 weight copies (more than the per-XCD L2 holds), a plain
+    elementwise pass over 256 MiB (x -> -x: reads and writes 256 MiB, the
+    counters' calibration), and the two prefill GEMMs."""
+    import torch
+
+    from bit_gemm_absmax_amd import bitlinear as bl
+    from bit_gemm_absmax_amd import synth
+    bl.load()
+    dev = torch.device("cuda:0")
+    d = synth.decode_gemv()
+    pu, su = bl.pack_weights(torch.from_numpy(d["W_up"]).to(dev))
+    ups = [bl.QuantForward(pu.clone(), su, 1, relu2=True) for _ in range(16)]
+    x = torch.from_numpy(d["X_up"]).to(dev)
+    y = torch.empty((1, F), dtype=torch.float32, device=dev)
+    for _ in range(3):
+        for q in ups:
+            q(x, y_out=y)
+    src = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    del src, dst, ups
+    p = synth.prefill()
+    X = torch.from_numpy(p["X"]).to(dev)
+    pu4, su4 = bl.pack_weights(torch.from_numpy(p["W_up"]).to(dev))
+    pd4, sd4 = bl.pack_weights(torch.from_numpy(p["W_down"]).to(dev))
+    xq, xs, rs = bl.quant_act(X)
+    up = bl.forward(xq, xs, pu4, su4, x_rowsum=rs, relu2=True, subln=True)
+    yu = torch.empty((X.shape[0], F), dtype=torch.float32, device=dev)
+    yd = torch.empty((X.shape[0], H), dtype=torch.float32, device=dev)
+    for _ in range(3):
+        bl.forward(xq, xs, pu4, su4, x_rowsum=rs, relu2=True, y_out=yu)
+        bl.forward(up["q"], up["q_scale"], pd4, sd4, x_rowsum=up["q_rowsum"], y_out=yd)
+    torch.cuda.synchronize()
+    log("pmc-drive done")
+
+
+def traffic_from(fetch_dir, write_dir):
+    """profiles/traffic.json and a markdown table from two rocprofv3 --pmc
+    runs of --pmc-drive (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch).
+    Each counter is scaled by what it reads for the calibration pass, whose
+    true traffic is known (256 MiB each way)."""
+    import csv
+    import glob
+    import statistics
+
+    def per_kernel(d, counter):
+        f = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        if not f:
+            raise SystemExit(f"no counter_collection.csv under {d}")
+        out = {}
+        for r in csv.DictReader(open(f[0])):
+            if r["Counter_Name"] != counter:
+                continue
+            name = r["Kernel_Name"].replace("bl::(anonymous namespace)::", "")
+            if name.startswith("void "):
+                name = name[5:]
+            wgs = int(r["Grid_Size"]) // int(r["Workgroup_Size"])
+            out.setdefault((name, wgs), []).append(float(r["Counter_Value"]) * 1024.0)
+        return out
+
+    fetch = per_kernel(fetch_dir, "FETCH_SIZE")
+    write = per_kernel(write_dir, "WRITE_SIZE")
+
+    def find(table, prefix, wgs):
+        vals = [v for (n, w), v in table.items() if n.startswith(prefix) and (wgs is None or w == wgs)]
+        if not vals:
+            raise SystemExit(f"kernel {prefix} ({wgs} WGs) not in the counters")
+        return statistics.median([x for v in vals for x in v])
+
+    def calib(table):
+        vals = [x for (n, w), v in table.items() if "neg_kernel" in n for x in v]
+        if not vals:
+            raise SystemExit("calibration pass (neg kernel) not in the counters")
+        return CALIB_BYTES / statistics.median(vals)
+
+    ff, fw = calib(fetch), calib(write)
+    rec = {"calibration": {"pass": "torch.neg over 256 MiB fp32 (reads and writes 268,435,456 B)",
+                           "fetch_factor": round(ff, 4), "write_factor": round(fw, 4)},
+           "commands": PMC_CMDS}
+    rows = []
+    for key, (prefix, wgs, srcs) in TRAFFIC_KERNELS.items():
+        fb = find(fetch, prefix, wgs) * ff
+        wb = find(write, prefix, wgs) * fw
+        rec[key] = {"kernel": prefix, "workgroups": wgs, "fetch_bytes": round(fb), "write_bytes": round(wb),
+                    "bytes_per_launch": round(fb + wb), "source_hash": src_hash(*srcs)}
+        rows.append(f"| {key} | `{prefix}` | {wgs} | {fb / 1e6:.2f} | {wb / 1e6:.2f} | {(fb + wb) / 1e6:.2f} |")
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as f:
+        json.dump(rec, f, indent=1)
+    print("| key | kernel | WGs | fetch MB | write MB | total MB |")
+    print("|---|---|---|---|---|---|")
+    print("\n".join(rows))
+    print(f"\nCalibration: FETCH_SIZE x {ff:.4f}, WRITE_SIZE x {fw:.4f} "
+          "(torch.neg over 256 MiB fp32 reads and writes 268,435,456 B).")
+
+
 def time_graph(torch, fn, reps=1):
     """Capture fn() into a HIP graph, replay once to warm, then time `reps`
     replays with events on the launch stream.  Returns seconds per replay."""
@@ -123,11 +238,22 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--pmc-drive", action="store_true",
+                    help="only run the launches the HBM traffic counters are read from")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/traffic.json from two rocprofv3 --pmc runs of --pmc-drive")
     args = ap.parse_args()
+    if args.traffic_from:
+        traffic_from(*args.traffic_from)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the BitLinear path here has no multi-GPU "
               "(sharded) implementation; run with --gpus 1", file=sys.stderr)
         sys.exit(2)
+
+    if args.pmc_drive:
+        pmc_drive()
+        return
 
     import torch
 
@@ -264,7 +390,7 @@ def main():
                    "roofline": {"bound": "mfma", "achieved": round(tops_up, 2), "peak": INT8_PEAK_TOPS,
                                 "unit": "TOPS", "frac": round(tops_up / INT8_PEAK_TOPS, 4),
                                 "traffic": traffic_from_profile("gemm_up_m4096", ["gemm.hip", "bl_device.h"]),
-                                "kernel": "k_gemm_pipe<256,256,4,2,3,1> (M=4096, K=2560, N=6912, +ReLU^2)",
+                                "kernel": "k_gemm_pipe<256,256,2,4,4,1> (M=4096, K=2560, N=6912, +ReLU^2)",
                                 "ops_per_launch": int(ops), "us_per_launch": round(up_s * 1e6, 2),
                                 "down_us_per_launch": round(dn_s * 1e6, 2),
                                 "down_tops": round(tops_dn, 2)}}

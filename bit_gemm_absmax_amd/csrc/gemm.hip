@@ -169,6 +169,28 @@ __global__ __launch_bounds__(WM* WN* kWave, OCC) void k_gemm_pipe(
                 acc[fm][fn] = __builtin_amdgcn_mfma_i32_16x16x64_i8(bv, a[fm], acc[fm][fn], 0, 0, 0);
         }
     };
+    auto mma_frag = [&](const v4i (&a)[FM], const uint32_t (&wq)[FN], int fn) {
+        const v4i bv = v4i{codes4(wq[fn], 0), codes4(wq[fn], 1), codes4(wq[fn], 2), codes4(wq[fn], 3)};
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+            acc[fm][fn] = __builtin_amdgcn_mfma_i32_16x16x64_i8(bv, a[fm], acc[fm][fn], 0, 0, 0);
+    };
+    // DMA instruction i (activation blocks first, then weight blocks) of a
+    // stage, as in issue_stage.
+    auto issue_one = [&](int st, int i) {
+        const uint32_t as = st < nst ? a_base + (uint32_t)st * kBK : kOob;
+        const uint32_t bs = st < nst ? b_base + (uint32_t)st * 32u : kOob;
+        int8_t* base = smem + (st % NBUF) * STAGE;
+        if (i < A_BLKS) {
+            const int j = wave * A_BLKS + i;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr)(base + j * 1024), 16, va,
+                                                     as + (uint32_t)j * a_blk, 0, 0);
+        } else {
+            const int j = wave * B_INS + (i - A_BLKS);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr)(base + A_STAGE + j * 1024), 16, vb,
+                                                     bs + (uint32_t)j * b_blk, 0, 0);
+        }
+    };
     auto interleave = [&](bool dma) {
         // per weight fragment: its unpack, then MFMAs with LDS reads between;
         // in the first step of a stage the DMA instructions of stage s+3 are
@@ -202,9 +224,20 @@ __global__ __launch_bounds__(WM* WN* kWave, OCC) void k_gemm_pipe(
     load_frags(0, 0, a0, w0);
     for (int st = 0; st + 1 < nst; ++st) {   // full 128-k stages
         load_frags(st, 1, a1, w1);
-        BL_ISSUE(st + NBUF - 1);
-        mma(a0, w0);
-        interleave(true);
+        if constexpr (FN >= LOADS) {
+            // as many weight fragments as DMA instructions: one DMA after
+            // each fragment's MFMAs, pinned there
+#pragma unroll
+            for (int g = 0; g < FN; ++g) {
+                mma_frag(a0, w0, g);
+                if (g < LOADS) issue_one(st + NBUF - 1, g);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        } else {
+            BL_ISSUE(st + NBUF - 1);
+            mma(a0, w0);
+            interleave(true);
+        }
         __builtin_amdgcn_sched_barrier(0);
         load_frags(st + 1, 0, a0, w0);
         mma(a1, w1);
