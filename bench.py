@@ -238,6 +238,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-shapes", action="store_true", help="skip the per-shape M=1 decode sweep")
     ap.add_argument("--pmc-drive", action="store_true",
                     help="only run the launches the HBM traffic counters are read from")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -255,6 +256,7 @@ def main():
         pmc_drive()
         return
 
+    import numpy as np
     import torch
 
     from bit_gemm_absmax_amd import bitlinear as bl
@@ -349,6 +351,38 @@ def main():
     del layers, stacks, ups, dns
     torch.cuda.empty_cache()
 
+    # ---------------------------------------------------------------- decode, M=1, per BitLinear shape
+    # Fused quantise + BitLinear at M=1 for the block's shapes (attention:
+    # q/o 2560->2560, k/v 2560->640, a 2560->3840 layer; FFN: up, down),
+    # rotating over >= 512 MB of packed copies so every launch reads HBM.
+    shapes = []
+    if not args.no_shapes:
+        rng = np.random.default_rng(5)
+        for K, N, what in ((2560, 2560, "q/o"), (2560, 640, "k/v"), (2560, 3840, "q+k+v size"),
+                           (2560, 6912, "up"), (6912, 2560, "down")):
+            Wt = torch.from_numpy(synth.weights(rng, N, K)).to(dev)
+            pk, sk = bl.pack_weights(Wt)
+            nb = N * K // 4
+            ncp = max(16, -(-(2 * MALL_BYTES) // nb))
+            pool = torch.empty((ncp, nb), dtype=torch.uint8, device=dev)
+            pool.copy_(pk.reshape(1, nb).expand(ncp, nb))
+            qfs = [bl.QuantForward(pool[i].view(N, K // 4), sk, 1) for i in range(ncp)]
+            xs1 = torch.from_numpy(synth.activations(rng, 1, K, outliers=True)).to(dev)
+            ys1 = torch.empty((1, N), dtype=torch.float32, device=dev)
+
+            def shape_run():
+                for q in qfs:
+                    q(xs1, y_out=ys1)
+
+            t, gg = time_graph(torch, shape_run, reps=3)
+            del gg
+            t /= ncp
+            shapes.append({"K": K, "N": N, "layer": what, "us_per_launch": round(t * 1e6, 3),
+                           "GB_per_s": round(nb / t / 1e9, 1), "weight_copies": ncp})
+            log(f"decode M=1 {K}->{N} ({what}): {t * 1e6:.2f} us -> {nb / t / 1e9:.0f} GB/s")
+            del pool, qfs, Wt
+        torch.cuda.empty_cache()
+
     # ---------------------------------------------------------------- prefill, M=4096
     prefill = None
     if not args.no_prefill:
@@ -406,7 +440,7 @@ def main():
                                                    "256 MB Infinity Cache",
                       "launch": "HIP graph of the K steps", "eager_us_per_step": round(eager_s * 1e6, 2),
                       "pack_ms_up_plus_down": round(pack_t * 1e3, 4)},
-           "roofline": roofline, "cpu_baseline": cpu, "prefill": prefill}
+           "roofline": roofline, "cpu_baseline": cpu, "prefill": prefill, "decode_shapes": shapes}
     print(json.dumps(out), flush=True)
 
 

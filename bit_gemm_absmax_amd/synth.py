@@ -4,8 +4,9 @@ This module draws random numbers only; it holds none of the layer's
 arithmetic, so both the HIP path and the CPU oracle may consume its arrays.
 
 Shapes follow the transformers "BitNet" page, section "BitNetConfig"
-(hidden_size 2560, intermediate_size 6912, num_hidden_layers 30) and section
-"Model details" (context length 4096).  Latent weights are N(0, 0.02) (the
+(hidden_size 2560, intermediate_size 6912, num_hidden_layers 30,
+num_attention_heads 20, num_key_value_heads 5) and section "Model details"
+(context length 4096).  Latent weights are N(0, 0.02) (the
 config's initializer_range used as a plain normal std); activations are
 N(0, 1), optionally with 1% of each token's entries scaled by 20.
 
@@ -23,6 +24,10 @@ HIDDEN = 2560
 FFN = 6912
 LAYERS = 30
 CONTEXT = 4096
+HEADS = 20
+KV_HEADS = 5
+HEAD_DIM = HIDDEN // HEADS          # 128
+KV_DIM = KV_HEADS * HEAD_DIM        # 640
 W_STD = 0.02
 
 
@@ -103,3 +108,16 @@ def ffn_stack_weights(seed: int = 4, layers: int = LAYERS, H: int = HIDDEN, F: i
 def ffn_stack_hidden(rng: np.random.Generator, M: int = 32, H: int = HIDDEN) -> np.ndarray:
     """Initial fp32 hidden state h0 [M][H] ~ N(0, 1); the M=1 run uses row 0."""
     return rng.standard_normal((M, H)).astype(np.float32)
+
+
+def attention_projections(seed: int = 5, Ms=(1, 5, 130), H: int = HIDDEN):
+    """The attention block's BitLinear layers at model width: q and o
+    2560->2560, k and v 2560->640 (grouped-query attention with 5 key/value
+    heads of 128), and a 2560->3840 layer of the size a fused q/k/v would
+    have; then token rows X for each M (with outliers)."""
+    rng = np.random.default_rng(seed)
+    out = {"W_q": weights(rng, H, H), "W_k": weights(rng, KV_DIM, H), "W_v": weights(rng, KV_DIM, H),
+           "W_o": weights(rng, H, H), "W_qkv": weights(rng, H + 2 * KV_DIM, H)}
+    for m in Ms:
+        out[f"X{m}"] = activations(rng, m, H, outliers=True)
+    return out

@@ -418,6 +418,28 @@ def test_workload_prefill():
     assert np.all(np.abs(q_all).max(axis=1) == 127)
 
 
+def test_attention_projections():
+    """The attention block's BitLinear shapes (q, o 2560->2560; k, v
+    2560->640; 2560->3840) at M = 1, 5, 130, through bitlinear_forward and,
+    for M <= 4, the fused quantise + forward; every element against the
+    oracle (M = 130 runs the GEMM, M <= 64 the skinny kernel)."""
+    d = synth.attention_projections()
+    for name in ("q", "k", "v", "o", "qkv"):
+        W = d[f"W_{name}"]
+        p, s, q, g = check_pack(W, f"attention {name}")
+        for M in (1, 5, 130):
+            X = d[f"X{M}"]
+            log(f"[attention] {name} N={W.shape[0]} M={M}")
+            ref = oracle.bitlinear(X, q, g)
+            xq, xs, rs = bl.quant_act(dev(X))
+            out = bl.forward(xq, xs, p, s, x_rowsum=rs, want_acc=True)
+            assert_exact(host(out["acc"]), ref["acc"], f"{name} M={M} acc")
+            assert_y_close(host(out["y"]), ref["y"], f"{name} M={M} y")
+            if M <= 4:
+                y = bl.quant_forward(dev(X), p, s)
+                assert_exact(host(y), host(out["y"]), f"{name} M={M} fused vs staged")
+
+
 @pytest.mark.parametrize("M", [1, 32])
 def test_workload_ffn_stack(M):
     """30-layer FFN stack, seed 4, M=1 and M=32; layer by layer teacher-forced
