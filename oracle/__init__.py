@@ -69,6 +69,10 @@ def _load():
     lib.orc_add.restype = None
     lib.orc_ffn_layer.argtypes = [P, I64, I64, I64, P, F, P, F, P, F, P, F,
                                   ctypes.c_int, P, P, P]
+    lib.orc_mul.argtypes = [P, P, I64]
+    lib.orc_mul.restype = None
+    lib.orc_ffn_layer_gated.argtypes = [P, I64, I64, I64, P, F, P, F, P, F, P, F, P, F, ctypes.c_int, P, P, P]
+    lib.orc_ffn_layer_gated.restype = None
     lib.orc_ffn_layer.restype = None
     _lib = lib
     return lib
@@ -215,6 +219,43 @@ def ffn_layer(H, q_up, gamma_up, q_down, gamma_down, pre_gain=None,
                           float(np.float32(eps)), _p(q_down),
                           float(np.float32(gamma_down)), int(bool(residual)),
                           _p(y1), _p(xq2), _p(g2))
+    if intermediates:
+        return H, {"y1": y1, "xq2": xq2, "g2": g2}
+    return H
+
+
+def mul(A, B) -> np.ndarray:
+    """Elementwise product in binary32 (orc_mul)."""
+    A = np.array(A, dtype=np.float32, copy=True, order="C")
+    B = _c(B, np.float32)
+    assert A.shape == B.shape
+    _load().orc_mul(_p(A), _p(B), A.size)
+    return A
+
+
+def ffn_layer_gated(H, q_gate, gamma_gate, q_up, gamma_up, q_down, gamma_down, pre_gain=None,
+                    sub_gain=None, residual=True, eps=RMS_EPS, intermediates=False):
+    """One gated BitNet FFN block (see orc_ffn_layer_gated): h =
+    ReLU^2(gate) * up, then subln, requantisation and down.  H is not
+    modified; intermediates returns h as "y1"."""
+    H = np.array(H, dtype=np.float32, copy=True, order="C")
+    M, Hd = H.shape
+    q_gate = _c(q_gate, np.int8)
+    q_up = _c(q_up, np.int8)
+    q_down = _c(q_down, np.int8)
+    F = q_up.shape[0]
+    assert q_gate.shape == (F, Hd) and q_up.shape == (F, Hd) and q_down.shape == (Hd, F)
+    pg = None if pre_gain is None else _c(pre_gain, np.float32)
+    sg = _c(np.ones(F, np.float32) if sub_gain is None else sub_gain, np.float32)
+    y1 = np.empty((M, F), np.float32) if intermediates else None
+    xq2 = np.empty((M, F), np.int8) if intermediates else None
+    g2 = np.empty(M, np.float32) if intermediates else None
+    _load().orc_ffn_layer_gated(_p(H), M, Hd, F, _p(pg), float(np.float32(eps)),
+                                _p(q_gate), float(np.float32(gamma_gate)),
+                                _p(q_up), float(np.float32(gamma_up)), _p(sg),
+                                float(np.float32(eps)), _p(q_down),
+                                float(np.float32(gamma_down)), int(bool(residual)),
+                                _p(y1), _p(xq2), _p(g2))
     if intermediates:
         return H, {"y1": y1, "xq2": xq2, "g2": g2}
     return H

@@ -190,3 +190,56 @@ void orc_ffn_layer(float* H, int64_t M, int64_t Hd, int64_t F,
     free(u); free(xq1); free(g1); free(acc1); free(y1);
     free(z); free(xq2); free(g2); free(acc2); free(y2);
 }
+
+/* Gating product of the gated FFN: elementwise, binary32. */
+void orc_mul(float* a, const float* b, int64_t n) {
+    for (int64_t i = 0; i < n; ++i) a[i] = a[i] * b[i];
+}
+
+/* Gated FFN block ("Model details" / Architecture: squared ReLU in the
+ * feed-forward layers; "BitNetConfig": hidden_act relu2).  The gate and up
+ * projections read the same quantised input; ReLU^2 is applied to the gate
+ * output and the result multiplies the up output, element by element. */
+void orc_ffn_layer_gated(float* H, int64_t M, int64_t Hd, int64_t F,
+                         const float* pre_gain, float pre_eps,
+                         const int8_t* q_gate, float gamma_gate,
+                         const int8_t* q_up, float gamma_up,
+                         const float* sub_gain, float sub_eps,
+                         const int8_t* q_down, float gamma_down,
+                         int residual,
+                         float* y1_out, int8_t* xq2_out, float* g2_out) {
+    float* u = (float*)malloc(sizeof(float) * (size_t)(M * Hd));
+    int8_t* xq1 = (int8_t*)malloc((size_t)(M * Hd));
+    float* g1 = (float*)malloc(sizeof(float) * (size_t)M);
+    int32_t* acc = (int32_t*)malloc(sizeof(int32_t) * (size_t)(M * F));
+    float* yg = (float*)malloc(sizeof(float) * (size_t)(M * F));
+    float* yu = (float*)malloc(sizeof(float) * (size_t)(M * F));
+    float* z = (float*)malloc(sizeof(float) * (size_t)(M * F));
+    int8_t* xq2 = (int8_t*)malloc((size_t)(M * F));
+    float* g2 = (float*)malloc(sizeof(float) * (size_t)M);
+    int32_t* acc2 = (int32_t*)malloc(sizeof(int32_t) * (size_t)(M * Hd));
+    float* y2 = (float*)malloc(sizeof(float) * (size_t)(M * Hd));
+
+    if (pre_gain) orc_rmsnorm(H, M, Hd, pre_gain, pre_eps, u);
+    else memcpy(u, H, sizeof(float) * (size_t)(M * Hd));
+    orc_quant_act(u, M, Hd, xq1, g1, NULL);
+    orc_int_matmul(xq1, M, Hd, q_gate, F, acc);
+    orc_dequant(acc, M, F, g1, gamma_gate, yg);
+    orc_relu2(yg, M * F);
+    orc_int_matmul(xq1, M, Hd, q_up, F, acc);
+    orc_dequant(acc, M, F, g1, gamma_up, yu);
+    orc_mul(yg, yu, M * F);                     /* h = ReLU^2(gate) * up */
+    orc_rmsnorm(yg, M, F, sub_gain, sub_eps, z);
+    orc_quant_act(z, M, F, xq2, g2, NULL);
+    orc_int_matmul(xq2, M, F, q_down, Hd, acc2);
+    orc_dequant(acc2, M, Hd, g2, gamma_down, y2);
+    if (residual) orc_add(H, y2, M * Hd);
+    else memcpy(H, y2, sizeof(float) * (size_t)(M * Hd));
+
+    if (y1_out) memcpy(y1_out, yg, sizeof(float) * (size_t)(M * F));
+    if (xq2_out) memcpy(xq2_out, xq2, (size_t)(M * F));
+    if (g2_out) memcpy(g2_out, g2, sizeof(float) * (size_t)M);
+
+    free(u); free(xq1); free(g1); free(acc); free(yg); free(yu);
+    free(z); free(xq2); free(g2); free(acc2); free(y2);
+}

@@ -97,6 +97,25 @@ void orc_ffn_layer(float* H, int64_t M, int64_t Hd, int64_t F,
                    int residual,
                    float* y1_out, int8_t* xq2_out, float* g2_out);
 
+/* a[i] = a[i] * b[i] in binary32 (the gating product). */
+void orc_mul(float* a, const float* b, int64_t n);
+
+/* Gated BitNet FFN block: as orc_ffn_layer, but the up projection's output
+ * is multiplied elementwise by ReLU^2 of a gate projection of the same
+ * quantised input,
+ *   y_gate = dequant(xq1 . q_gate^T), y_up = dequant(xq1 . q_up^T)
+ *   h = ReLU^2(y_gate) * y_up            (binary32, one rounding each)
+ * then subln RMSNorm of h, quantisation and the down projection as in the
+ * ungated block.  q_gate is ternary [F][Hd].  y1_out, if not NULL, receives h. */
+void orc_ffn_layer_gated(float* H, int64_t M, int64_t Hd, int64_t F,
+                         const float* pre_gain, float pre_eps,
+                         const int8_t* q_gate, float gamma_gate,
+                         const int8_t* q_up, float gamma_up,
+                         const float* sub_gain, float sub_eps,
+                         const int8_t* q_down, float gamma_down,
+                         int residual,
+                         float* y1_out, int8_t* xq2_out, float* g2_out);
+
 #ifdef __cplusplus
 }
 #endif

@@ -419,3 +419,77 @@ def test_prenorm_gain_reaches_quantiser():
     _, c = oracle.ffn_layer(H, qu, gu, qd, gd, pre_gain=None, **kw)
     assert np.count_nonzero(a["xq2"] != b["xq2"]) <= 3
     assert np.count_nonzero(c["xq2"] != b["xq2"]) > 100
+
+
+# ------------------------------------------------------------------ gated FFN block
+
+def _gated_inputs(seed, M=3, Hd=128, F=256):
+    rng = np.random.default_rng(seed)
+    Wg = synth.weights(rng, F, Hd)
+    Wu = synth.weights(rng, F, Hd)
+    Wd = synth.weights(rng, Hd, F)
+    X = synth.activations(rng, M, Hd, outliers=True)
+    return X, Wg, Wu, Wd
+
+
+def test_gated_scaled_up_closed_form():
+    """W_up = 2 W_gate: q is the same and gamma doubles exactly, so the up
+    output is exactly twice the gate output y, and the gated product must
+    equal fl(fl(t*t) * fl(2y)) with t = max(y, 0) (ReLU^2 on the gate, then
+    the product).  Squaring the up output instead, or dropping the ReLU,
+    changes the result."""
+    X, Wg, _, Wd = _gated_inputs(41)
+    qg, gg = oracle.quantize_weights(Wg)
+    qu, gu = oracle.quantize_weights(np.float32(2.0) * Wg)
+    assert np.array_equal(qu, qg) and gu == np.float32(2.0) * gg
+    qd, gd = oracle.quantize_weights(Wd)
+    y = oracle.bitlinear(X, qg, gg)["y"].astype(np.float32)
+    t = np.maximum(y, np.float32(0.0))
+    expect = (t * t) * (np.float32(2.0) * y)
+    _, it = oracle.ffn_layer_gated(X, qg, gg, qu, gu, qd, gd, residual=False, intermediates=True)
+    assert np.array_equal(it["y1"], expect)
+    assert np.all(it["y1"] >= 0) and np.any(it["y1"] > 0)
+
+
+def test_gated_zero_gate_keeps_residual():
+    """A zero gate matrix makes h = 0: the subln input is a zero row, its
+    requantisation is all zeros (scale floored at 1e-5), the down output is 0
+    and the residual stream passes through unchanged."""
+    X, Wg, Wu, Wd = _gated_inputs(42)
+    qg, gg = oracle.quantize_weights(np.zeros_like(Wg))
+    qu, gu = oracle.quantize_weights(Wu)
+    qd, gd = oracle.quantize_weights(Wd)
+    out, it = oracle.ffn_layer_gated(X, qg, gg, qu, gu, qd, gd, residual=True, intermediates=True)
+    assert np.array_equal(it["y1"], np.zeros_like(it["y1"]))
+    assert np.array_equal(it["xq2"], np.zeros_like(it["xq2"]))
+    assert np.all(it["g2"] == np.float32(1e-5))
+    assert np.array_equal(out, X)
+
+
+def test_gated_up_sign_is_linear():
+    """W_up -> -W_up flips h, the subln requantisation and the block output
+    exactly (ternarisation, absmax quantisation and the integer contraction
+    are odd; RMSNorm is odd in its input): the up projection enters
+    linearly, not through the square."""
+    X, Wg, Wu, Wd = _gated_inputs(43)
+    qg, gg = oracle.quantize_weights(Wg)
+    qu, gu = oracle.quantize_weights(Wu)
+    qn, gn = oracle.quantize_weights(-Wu)
+    assert np.array_equal(qn, -qu) and gn == gu
+    qd, gd = oracle.quantize_weights(Wd)
+    a, ia = oracle.ffn_layer_gated(X, qg, gg, qu, gu, qd, gd, residual=False, intermediates=True)
+    b, ib = oracle.ffn_layer_gated(X, qg, gg, qn, gn, qd, gd, residual=False, intermediates=True)
+    assert np.array_equal(ib["y1"], -ia["y1"])
+    assert np.array_equal(ib["xq2"], -ia["xq2"])
+    assert np.array_equal(b, -a)
+
+
+def test_gated_token_independence():
+    """Every step is per token: a row of a batch equals that row alone."""
+    X, Wg, Wu, Wd = _gated_inputs(44, M=5)
+    qs = [oracle.quantize_weights(W) for W in (Wg, Wu, Wd)]
+    args = (qs[0][0], qs[0][1], qs[1][0], qs[1][1], qs[2][0], qs[2][1])
+    full = oracle.ffn_layer_gated(X, *args)
+    for r in (0, 3):
+        one = oracle.ffn_layer_gated(X[r:r + 1], *args)
+        assert np.array_equal(one[0], full[r])
