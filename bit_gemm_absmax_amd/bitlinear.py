@@ -28,6 +28,7 @@ BL_QUANT_RMSNORM = 0x1
 BL_EPI_RELU2 = 0x1
 BL_EPI_RESIDUAL = 0x2
 BL_EPI_SUBLN_QUANT = 0x4
+BL_EPI_MUL = 0x8
 BL_FFN_PRE_NORM = 0x1
 BL_FFN_RESIDUAL = 0x2
 
@@ -52,7 +53,7 @@ class Epilogue(ctypes.Structure):
     _fields_ = [("flags", ctypes.c_uint32), ("residual", ctypes.c_void_p),
                 ("norm_gain", ctypes.c_void_p), ("norm_eps", ctypes.c_float),
                 ("out_q", ctypes.c_void_p), ("out_q_scale", ctypes.c_void_p),
-                ("out_q_rowsum", ctypes.c_void_p)]
+                ("out_q_rowsum", ctypes.c_void_p), ("mul_by", ctypes.c_void_p)]
 
 
 class FFNLayer(ctypes.Structure):
@@ -177,9 +178,11 @@ def forward(xq: torch.Tensor, x_scale: torch.Tensor, packed: torch.Tensor, w_sca
             x_rowsum: Optional[torch.Tensor] = None, relu2: bool = False,
             residual: Optional[torch.Tensor] = None, subln: bool = False,
             norm_gain: Optional[torch.Tensor] = None, eps: float = RMS_EPS,
-            want_y: bool = True, want_acc: bool = False, y_out: Optional[torch.Tensor] = None):
+            want_y: bool = True, want_acc: bool = False, y_out: Optional[torch.Tensor] = None,
+            mul_by: Optional[torch.Tensor] = None):
     """BitLinear forward.  Returns a dict with the requested outputs:
-    'y' (f32 [M][N]), 'acc' (i32 [M][N]) and, with subln, 'q', 'q_scale', 'q_rowsum'."""
+    'y' (f32 [M][N]), 'acc' (i32 [M][N]) and, with subln, 'q', 'q_scale', 'q_rowsum'.
+    mul_by multiplies the (ReLU^2'd) output elementwise: the gating product."""
     lib = load()
     _need(xq, torch.int8, 2, "xq")
     _need(packed, torch.uint8, 2, "packed")
@@ -197,6 +200,10 @@ def forward(xq: torch.Tensor, x_scale: torch.Tensor, packed: torch.Tensor, w_sca
         _need(residual, torch.float32, 2, "residual")
         flags |= BL_EPI_RESIDUAL
         epi.residual = residual.data_ptr()
+    if mul_by is not None:
+        _need(mul_by, torch.float32, 2, "mul_by")
+        flags |= BL_EPI_MUL
+        epi.mul_by = mul_by.data_ptr()
     if subln:
         flags |= BL_EPI_SUBLN_QUANT
         res["q"] = torch.empty((M, N), dtype=torch.int8, device=dev)
@@ -238,14 +245,18 @@ class QuantForward:
                              packed.device)
 
     def __call__(self, X: torch.Tensor, residual: Optional[torch.Tensor] = None,
-                 y_out: Optional[torch.Tensor] = None) -> torch.Tensor:
+                 y_out: Optional[torch.Tensor] = None, mul_by: Optional[torch.Tensor] = None) -> torch.Tensor:
         _need(X, torch.float32, 2, "X")
         M = X.shape[0]
         y = y_out if y_out is not None else torch.empty((M, self.N), dtype=torch.float32, device=X.device)
         epi = Epilogue()
-        epi.flags = (BL_EPI_RELU2 if self.relu2 else 0) | (BL_EPI_RESIDUAL if residual is not None else 0)
+        epi.flags = ((BL_EPI_RELU2 if self.relu2 else 0) | (BL_EPI_RESIDUAL if residual is not None else 0)
+                     | (BL_EPI_MUL if mul_by is not None else 0))
         if residual is not None:
             epi.residual = residual.data_ptr()
+        if mul_by is not None:
+            _need(mul_by, torch.float32, 2, "mul_by")
+            epi.mul_by = mul_by.data_ptr()
         _check(self.lib.bitlinear_quant_forward(_p(X), M, self.K, self.qflags, _p(self.gain), self.eps,
                                                 _p(self.packed), _p(self.w_scale), self.N, ctypes.byref(epi),
                                                 _p(y), _p(self.ws), 0 if self.ws is None else self.ws.numel(),
@@ -255,14 +266,16 @@ class QuantForward:
 
 def quant_forward(X: torch.Tensor, packed: torch.Tensor, w_scale: torch.Tensor, rmsnorm: bool = False,
                   norm_gain: Optional[torch.Tensor] = None, eps: float = RMS_EPS, relu2: bool = False,
-                  residual: Optional[torch.Tensor] = None, y_out: Optional[torch.Tensor] = None):
+                  residual: Optional[torch.Tensor] = None, y_out: Optional[torch.Tensor] = None,
+                  mul_by: Optional[torch.Tensor] = None):
     """Quantise fp32 X [M][K] and apply the BitLinear in one call; returns Y [M][N]."""
-    return QuantForward(packed, w_scale, X.shape[0], rmsnorm, norm_gain, eps, relu2)(X, residual, y_out)
+    return QuantForward(packed, w_scale, X.shape[0], rmsnorm, norm_gain, eps, relu2)(X, residual, y_out, mul_by)
 
 
 def make_layers(layers: Sequence[dict]):
     """Host array of FFN layer descriptors from dicts of device tensors
-    (keys: up, up_scale, down, down_scale, optional pre_norm_gain, sub_norm_gain)."""
+    (keys: up, up_scale, down, down_scale, optional gate, gate_scale, pre_norm_gain,
+    sub_norm_gain)."""
     arr = (FFNLayer * len(layers))()
     for i, L in enumerate(layers):
         arr[i].pre_norm_gain = None if L.get("pre_norm_gain") is None else L["pre_norm_gain"].data_ptr()

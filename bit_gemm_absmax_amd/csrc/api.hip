@@ -82,6 +82,37 @@ size_t ffn_ws(int64_t M, int64_t H, int64_t F) {
     return c.off;
 }
 
+// The contraction kernels' epilogue from the public one: ReLU^2, then the
+// residual add or the gating product (their common operand is aux).
+bl::Epi kernel_epi(const bl_epilogue* epi) {
+    if (!epi) return bl::Epi{0u, nullptr};
+    uint32_t k = 0;
+    const float* aux = nullptr;
+    if (epi->flags & BL_EPI_RELU2) k |= bl::kEpiRelu2;
+    if (epi->flags & BL_EPI_RESIDUAL) {
+        k |= bl::kEpiResidual;
+        aux = epi->residual;
+    }
+    if (epi->flags & BL_EPI_MUL) {
+        k |= bl::kEpiMul;
+        aux = epi->mul_by;
+    }
+    return bl::Epi{k, aux};
+}
+
+// Checks shared by forward and quant_forward for the residual / product operands.
+int check_aux(const bl_epilogue* epi, uint32_t flags, const char* who) {
+    if ((flags & BL_EPI_RESIDUAL) && (flags & BL_EPI_MUL))
+        return fail(BL_ERR_UNSUPPORTED, "%s: BL_EPI_RESIDUAL and BL_EPI_MUL together", who);
+    if ((flags & BL_EPI_RESIDUAL) && !epi->residual)
+        return fail(BL_ERR_NULL, "%s: BL_EPI_RESIDUAL needs epi->residual", who);
+    if ((flags & BL_EPI_MUL) && !epi->mul_by) return fail(BL_ERR_NULL, "%s: BL_EPI_MUL needs epi->mul_by", who);
+    if (((flags & BL_EPI_RESIDUAL) && !aligned(epi->residual, 16)) ||
+        ((flags & BL_EPI_MUL) && !aligned(epi->mul_by, 16)))
+        return fail(BL_ERR_ALIGN, "%s: residual / mul_by need 16-byte alignment", who);
+    return BL_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -162,11 +193,10 @@ int bitlinear_forward(const int8_t* Xq, const float* x_scale, const int32_t* x_r
     const bool subln = (flags & BL_EPI_SUBLN_QUANT) != 0;
     if (!Xq || !x_scale || !packed || !w_scale)
         return fail(BL_ERR_NULL, "forward: Xq, x_scale, packed and w_scale are required");
-    if (flags & ~(BL_EPI_RELU2 | BL_EPI_RESIDUAL | BL_EPI_SUBLN_QUANT))
+    if (flags & ~(BL_EPI_RELU2 | BL_EPI_RESIDUAL | BL_EPI_SUBLN_QUANT | BL_EPI_MUL))
         return fail(BL_ERR_UNSUPPORTED, "forward: unknown epilogue flags 0x%x", flags);
     if (!Y && !subln) return fail(BL_ERR_NULL, "forward: Y is required without BL_EPI_SUBLN_QUANT");
-    if ((flags & BL_EPI_RESIDUAL) && !epi->residual)
-        return fail(BL_ERR_NULL, "forward: BL_EPI_RESIDUAL needs epi->residual");
+    if (int r = epi ? check_aux(epi, flags, "forward") : BL_OK) return r;
     if (subln && (!epi->out_q || !epi->out_q_scale))
         return fail(BL_ERR_NULL, "forward: BL_EPI_SUBLN_QUANT needs out_q and out_q_scale");
     if (M < 0) return fail(BL_ERR_SHAPE, "forward: M = %lld must be >= 0", (long long)M);
@@ -182,8 +212,6 @@ int bitlinear_forward(const int8_t* Xq, const float* x_scale, const int32_t* x_r
     if (!aligned(Xq, 16) || !aligned(packed, 16) || !aligned(Y, 16) || !aligned(acc_out, 16) ||
         !aligned(x_scale, 4) || !aligned(x_rowsum, 4) || !aligned(w_scale, 4))
         return fail(BL_ERR_ALIGN, "forward: Xq, packed, Y, acc_out need 16-byte alignment, scales 4-byte");
-    if (epi && ((flags & BL_EPI_RESIDUAL) && !aligned(epi->residual, 16)))
-        return fail(BL_ERR_ALIGN, "forward: residual needs 16-byte alignment");
     if (subln && (!aligned(epi->out_q, 16) || !aligned(epi->out_q_scale, 4) ||
                   !aligned(epi->out_q_rowsum, 4) || !aligned(epi->norm_gain, 16)))
         return fail(BL_ERR_ALIGN, "forward: subln outputs/gain misaligned");
@@ -201,8 +229,7 @@ int bitlinear_forward(const int8_t* Xq, const float* x_scale, const int32_t* x_r
         e = bl::launch_rowsum(Xq, M, K, rs, stream);
         if (e != hipSuccess) return hip_status(e, "forward: rowsum");
     }
-    bl::Epi ke{flags & (BL_EPI_RELU2 | BL_EPI_RESIDUAL), epi ? epi->residual : nullptr};
-    e = bl::launch_contract(Xq, x_scale, rs, M, K, packed, w_scale, N, ke, y, acc_out, stream);
+    e = bl::launch_contract(Xq, x_scale, rs, M, K, packed, w_scale, N, kernel_epi(epi), y, acc_out, stream);
     if (e != hipSuccess) return hip_status(e, "forward: contraction");
     if (subln) {
         e = bl::launch_quant(y, M, N, true, epi->norm_gain, epi->norm_eps, epi->out_q,
@@ -232,10 +259,9 @@ int bitlinear_quant_forward(const float* X, int64_t M, int64_t K, uint32_t quant
         return fail(BL_ERR_NULL, "quant_forward: X, packed, w_scale and Y are required");
     if (quant_flags & ~BL_QUANT_RMSNORM)
         return fail(BL_ERR_UNSUPPORTED, "quant_forward: unknown quant flags 0x%x", quant_flags);
-    if (flags & ~(BL_EPI_RELU2 | BL_EPI_RESIDUAL))
+    if (flags & ~(BL_EPI_RELU2 | BL_EPI_RESIDUAL | BL_EPI_MUL))
         return fail(BL_ERR_UNSUPPORTED, "quant_forward: epilogue flags 0x%x not supported", flags);
-    if ((flags & BL_EPI_RESIDUAL) && !epi->residual)
-        return fail(BL_ERR_NULL, "quant_forward: BL_EPI_RESIDUAL needs epi->residual");
+    if (int r = epi ? check_aux(epi, flags, "quant_forward") : BL_OK) return r;
     if (M < 0) return fail(BL_ERR_SHAPE, "quant_forward: M = %lld must be >= 0", (long long)M);
     if (N < 1) return fail(BL_ERR_SHAPE, "quant_forward: N = %lld must be >= 1", (long long)N);
     if (int r = check_k(K, "quant_forward: K")) return r;
@@ -243,19 +269,17 @@ int bitlinear_quant_forward(const float* X, int64_t M, int64_t K, uint32_t quant
         return fail(BL_ERR_UNSUPPORTED, "quant_forward: K = %lld above 32768", (long long)K);
     if (M * K >= kLimit || M * N >= kLimit || N * K >= kLimit * 4)
         return fail(BL_ERR_SHAPE, "quant_forward: sizes exceed 2^31 elements");
-    if (!aligned(X, 16) || !aligned(packed, 16) || !aligned(Y, 16) || !aligned(w_scale, 4) ||
-        !aligned(norm_gain, 16) || ((flags & BL_EPI_RESIDUAL) && !aligned(epi->residual, 16)))
-        return fail(BL_ERR_ALIGN, "quant_forward: X, packed, Y, gain, residual need 16-byte alignment");
+    if (!aligned(X, 16) || !aligned(packed, 16) || !aligned(Y, 16) || !aligned(w_scale, 4) || !aligned(norm_gain, 16))
+        return fail(BL_ERR_ALIGN, "quant_forward: X, packed, Y, gain need 16-byte alignment");
     const bool fused = bl::decode_supported(M, K, N);
     if (int r = check_workspace(ws, ws_bytes, M == 0 || fused ? 0 : bitlinear_quant_forward_workspace_bytes(M, K, N)))
         return r;
     if (M == 0) return ok();
     const bool rms = (quant_flags & BL_QUANT_RMSNORM) != 0;
-    const uint32_t kflags = flags & (BL_EPI_RELU2 | BL_EPI_RESIDUAL);
-    const float* residual = (flags & BL_EPI_RESIDUAL) ? epi->residual : nullptr;
+    const bl::Epi ke = kernel_epi(epi);
     if (fused)
         return hip_status(bl::launch_decode_bitlinear(X, M, K, rms, rms ? norm_gain : nullptr, norm_eps, packed,
-                                                      w_scale, N, kflags, residual, Y, stream),
+                                                      w_scale, N, ke.flags, ke.aux, Y, stream),
                           "quant_forward: fused decode kernel");
     Carver c(ws);
     int8_t* xq = c.take<int8_t>((size_t)(M * K));
@@ -263,7 +287,7 @@ int bitlinear_quant_forward(const float* X, int64_t M, int64_t K, uint32_t quant
     int32_t* rs = c.take<int32_t>((size_t)M);
     hipError_t e = bl::launch_quant(X, M, K, rms, rms ? norm_gain : nullptr, norm_eps, xq, xs, rs, stream);
     if (e != hipSuccess) return hip_status(e, "quant_forward: quant");
-    e = bl::launch_contract(xq, xs, rs, M, K, packed, w_scale, N, bl::Epi{kflags, residual}, Y, nullptr, stream);
+    e = bl::launch_contract(xq, xs, rs, M, K, packed, w_scale, N, ke, Y, nullptr, stream);
     return hip_status(e, "quant_forward: contraction");
 }
 
@@ -292,12 +316,13 @@ int bitnet_ffn_forward(const bitnet_ffn_layer* layers, int32_t n_layers, float* 
     if (!aligned(hidden, 16)) return fail(BL_ERR_ALIGN, "ffn: hidden needs 16-byte alignment");
     for (int32_t l = 0; l < n_layers; ++l) {
         const bitnet_ffn_layer& L = layers[l];
-        if (L.gate || L.gate_scale)
-            return fail(BL_ERR_UNSUPPORTED, "ffn: layer %d: gated blocks are not implemented", l);
         if (!L.up || !L.up_scale || !L.down || !L.down_scale)
             return fail(BL_ERR_NULL, "ffn: layer %d: up/down weights and scales are required", l);
+        if ((L.gate != nullptr) != (L.gate_scale != nullptr))
+            return fail(BL_ERR_NULL, "ffn: layer %d: gate and gate_scale go together", l);
         if (!aligned(L.up, 16) || !aligned(L.down, 16) || !aligned(L.up_scale, 4) ||
-            !aligned(L.down_scale, 4) || !aligned(L.pre_norm_gain, 16) || !aligned(L.sub_norm_gain, 16))
+            !aligned(L.down_scale, 4) || !aligned(L.pre_norm_gain, 16) || !aligned(L.sub_norm_gain, 16) ||
+            !aligned(L.gate, 16) || !aligned(L.gate_scale, 4))
             return fail(BL_ERR_ALIGN, "ffn: layer %d: misaligned pointer", l);
     }
     if (int r = check_workspace(ws, ws_bytes, M == 0 || n_layers == 0 ? 0 : ffn_ws(M, H, F))) return r;
@@ -314,13 +339,21 @@ int bitnet_ffn_forward(const bitnet_ffn_layer* layers, int32_t n_layers, float* 
     const bool pre = (flags & BL_FFN_PRE_NORM) != 0;
     const bool res = (flags & BL_FFN_RESIDUAL) != 0;
 
-    // Few tokens: two launches per layer, each quantising its own input rows.
+    // Few tokens: two launches per layer (three when gated), each quantising
+    // its own input rows.  Gated: y1 = up, then y1 = ReLU^2(gate) * y1 in place.
     if (bl::decode_supported(M, H, F) && bl::decode_supported(M, F, H)) {
         for (int32_t l = 0; l < n_layers; ++l) {
             const bitnet_ffn_layer& L = layers[l];
+            const bool gated = L.gate != nullptr;
             hipError_t e = bl::launch_decode_bitlinear(hidden, M, H, pre, L.pre_norm_gain, norm_eps, L.up,
-                                                       L.up_scale, F, bl::kEpiRelu2, nullptr, y1, stream);
+                                                       L.up_scale, F, gated ? 0u : bl::kEpiRelu2, nullptr, y1,
+                                                       stream);
             if (e != hipSuccess) return hip_status(e, "ffn: decode up");
+            if (gated) {
+                e = bl::launch_decode_bitlinear(hidden, M, H, pre, L.pre_norm_gain, norm_eps, L.gate, L.gate_scale,
+                                                F, bl::kEpiRelu2 | bl::kEpiMul, y1, y1, stream);
+                if (e != hipSuccess) return hip_status(e, "ffn: decode gate");
+            }
             e = bl::launch_decode_bitlinear(y1, M, F, true, L.sub_norm_gain, norm_eps, L.down, L.down_scale, H,
                                             res ? bl::kEpiResidual : 0u, res ? hidden : nullptr, hidden, stream);
             if (e != hipSuccess) return hip_status(e, "ffn: decode down");
@@ -333,9 +366,15 @@ int bitnet_ffn_forward(const bitnet_ffn_layer* layers, int32_t n_layers, float* 
         hipError_t e = bl::launch_quant(hidden, M, H, pre, pre ? L.pre_norm_gain : nullptr, norm_eps,
                                         xq1, s1, rs1, stream);
         if (e != hipSuccess) return hip_status(e, "ffn: input quant");
-        e = bl::launch_contract(xq1, s1, rs1, M, H, L.up, L.up_scale, F, bl::Epi{bl::kEpiRelu2, nullptr},
-                                y1, nullptr, stream);
+        const bool gated = L.gate != nullptr;
+        e = bl::launch_contract(xq1, s1, rs1, M, H, L.up, L.up_scale, F,
+                                bl::Epi{gated ? 0u : bl::kEpiRelu2, nullptr}, y1, nullptr, stream);
         if (e != hipSuccess) return hip_status(e, "ffn: up");
+        if (gated) {
+            e = bl::launch_contract(xq1, s1, rs1, M, H, L.gate, L.gate_scale, F,
+                                    bl::Epi{bl::kEpiRelu2 | bl::kEpiMul, y1}, y1, nullptr, stream);
+            if (e != hipSuccess) return hip_status(e, "ffn: gate");
+        }
         e = bl::launch_quant(y1, M, F, true, L.sub_norm_gain, norm_eps, xq2, s2, rs2, stream);
         if (e != hipSuccess) return hip_status(e, "ffn: subln requant");
         e = bl::launch_contract(xq2, s2, rs2, M, F, L.down, L.down_scale, H,

@@ -9,13 +9,16 @@
 namespace bl {
 
 // Fused epilogue description handed to the contraction kernels by value.
+// After the dequantisation: optional ReLU^2, then either y + aux (residual)
+// or y * aux (the gating product); aux is [M][N] and may alias Y.
 struct Epi {
-    uint32_t flags;          // BL_EPI_RELU2 | BL_EPI_RESIDUAL (SUBLN is host-side)
-    const float* residual;   // [M][N] or nullptr
+    uint32_t flags;     // kEpi* bits (the subln requantisation is host-side)
+    const float* aux;   // [M][N] residual or multiplier, or nullptr
 };
 
 constexpr uint32_t kEpiRelu2 = 0x1u;
 constexpr uint32_t kEpiResidual = 0x2u;
+constexpr uint32_t kEpiMul = 0x4u;
 
 // ---- launchers (return hipError_t of the launch) ----------------------------
 
@@ -58,10 +61,10 @@ hipError_t launch_contract(const int8_t* Xq, const float* x_scale,
 
 // Few-token BitLinear from fp32 rows: every workgroup quantises the rows
 // itself (optional RMSNorm with gain), then contracts its slice of output
-// rows; epilogue ReLU^2 / residual (Y may alias residual).
+// rows; epilogue ReLU^2, then residual add or gating product (Y may alias aux).
 bool decode_supported(int64_t M, int64_t K, int64_t N);
 hipError_t launch_decode_bitlinear(const float* X, int64_t M, int64_t K, bool rmsnorm, const float* gain,
                                    float eps, const uint8_t* packed, const float* w_scale, int64_t N,
-                                   uint32_t epi, const float* residual, float* Y, hipStream_t s);
+                                   uint32_t epi, const float* aux, float* Y, hipStream_t s);
 
 }  // namespace bl

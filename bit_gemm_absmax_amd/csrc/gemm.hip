@@ -13,7 +13,8 @@
 // so consecutive tile indices are remapped to land on the same XCD and share
 // its L2.
 // The MFMA accumulates codes (q + 1); the epilogue subtracts the token's
-// activation row sum, dequantises and applies the fused ReLU^2 / residual.
+// activation row sum, dequantises and applies the fused ReLU^2 and residual
+// add or gating product.
 #include <atomic>
 
 #include "bl_device.h"
@@ -282,16 +283,17 @@ __global__ __launch_bounds__(WM* WN* kWave, OCC) void k_gemm_pipe(
     // N % 4 != 0 take the element-wise path.
     const bool whole = m0 + BM <= M && n0 + BN <= N && (N % 4) == 0;
     const bool relu2 = (epi.flags & kEpiRelu2) != 0;
-    const bool resid = (epi.flags & kEpiResidual) != 0;
+    const bool mul = (epi.flags & kEpiMul) != 0;
+    const bool resid = !mul && (epi.flags & kEpiResidual) != 0;
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm) {
         const int m = m0 + wm * TM + fm * 16 + fr;
         const int64_t row = (int64_t)m * N;
         float4 res[FN];
-        if (whole && resid) {
+        if (whole && (resid || mul)) {
 #pragma unroll
             for (int fn = 0; fn < FN; ++fn)
-                res[fn] = *reinterpret_cast<const float4*>(epi.residual + row + n0 + wn * TN + fn * 16 + 4 * fg);
+                res[fn] = *reinterpret_cast<const float4*>(epi.aux + row + n0 + wn * TN + fn * 16 + 4 * fg);
         }
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn) {
@@ -314,6 +316,11 @@ __global__ __launch_bounds__(WM* WN* kWave, OCC) void k_gemm_pipe(
                     y[1] = y[1] + res[fn].y;
                     y[2] = y[2] + res[fn].z;
                     y[3] = y[3] + res[fn].w;
+                } else if (mul) {
+                    y[0] = y[0] * res[fn].x;
+                    y[1] = y[1] * res[fn].y;
+                    y[2] = y[2] * res[fn].z;
+                    y[3] = y[3] * res[fn].w;
                 }
                 if (Y != nullptr) *reinterpret_cast<float4*>(Y + row + n) = make_float4(y[0], y[1], y[2], y[3]);
                 if (acc_out != nullptr)
@@ -323,7 +330,8 @@ __global__ __launch_bounds__(WM* WN* kWave, OCC) void k_gemm_pipe(
                 for (int r = 0; r < 4; ++r) {
                     if (n + r < N) {
                         float t = y[r];
-                        if (resid) t = t + epi.residual[row + n + r];
+                        if (resid) t = t + epi.aux[row + n + r];
+                        else if (mul) t = t * epi.aux[row + n + r];
                         if (Y != nullptr) Y[row + n + r] = t;
                         if (acc_out != nullptr) acc_out[row + n + r] = av[r];
                     }

@@ -18,7 +18,7 @@
 //     operands follow the same permutation of k and the sum is unchanged;
 //   - per-wave partial tiles meet in LDS in a fixed wave order (exact integer
 //     sums), then the epilogue subtracts the row sum of the code offset,
-//     dequantises and applies ReLU^2 / residual.
+//     dequantises and applies ReLU^2 and the residual add or gating product.
 //
 // Two prologues: int8 rows read straight from global memory (L2-resident,
 // shared by all workgroups), or -- for M <= 4 -- fp32 rows that every
@@ -41,7 +41,7 @@ __global__ __launch_bounds__(NWV* kWave) void k_skinny(
     const float* __restrict__ X, const int8_t* __restrict__ Xq, const float* __restrict__ x_scale,
     const int32_t* __restrict__ x_rowsum, int M, int K, int rmsnorm, const float* __restrict__ gain,
     float eps, const uint8_t* __restrict__ Wp, const float* __restrict__ w_scale, int N, uint32_t epi_flags,
-    const float* residual, float* Y, int32_t* __restrict__ acc_out) {
+    const float* aux, float* Y, int32_t* __restrict__ acc_out) {
     constexpr int NT = NWV * kWave;
     constexpr int ROWS = 16 * MTILES;
     extern __shared__ __align__(16) int8_t lds[];  // [fp32 input: xq, M <= 4 rows of K] [partials]
@@ -82,7 +82,7 @@ __global__ __launch_bounds__(NWV* kWave) void k_skinny(
     const bool e_first = (int)threadIdx.x < M * 16;
     const int e_m = threadIdx.x / 16, e_n = n0 + (int)(threadIdx.x % 16);
     const bool e_ok = e_first && e_n < N;
-    const float e_res = buf_load4f(make_rsrc(residual, (epi_flags & kEpiResidual) ? 0x7FFFFFFFu : 0u),
+    const float e_res = buf_load4f(make_rsrc(aux, (epi_flags & (kEpiResidual | kEpiMul)) ? 0x7FFFFFFFu : 0u),
                                    e_ok ? (uint32_t)((int64_t)e_m * N + e_n) * 4u : kOob);
     float e_xs = 0.0f;
     int e_rs = 0;
@@ -181,7 +181,8 @@ __global__ __launch_bounds__(NWV* kWave) void k_skinny(
                 y = tt * tt;
             }
             const int64_t o = (int64_t)m * N + n;
-            if (epi_flags & kEpiResidual) y = y + (first ? e_res : residual[o]);
+            if (epi_flags & kEpiMul) y = y * (first ? e_res : aux[o]);
+            else if (epi_flags & kEpiResidual) y = y + (first ? e_res : aux[o]);
             if (Y != nullptr) Y[o] = y;
             if (acc_out != nullptr) acc_out[o] = a;
         }
@@ -211,23 +212,23 @@ bool plan(int64_t K, Plan& p) {
 template <int MT, int NWV, int Q, bool F>
 hipError_t go(const float* X, const int8_t* Xq, const float* xs, const int32_t* rs, int64_t M, int64_t K, bool rms,
               const float* gain, float eps, const uint8_t* packed, const float* ws, int64_t N, uint32_t epi,
-              const float* residual, float* Y, int32_t* acc_out, hipStream_t s) {
+              const float* aux, float* Y, int32_t* acc_out, hipStream_t s) {
     const unsigned blocks = (unsigned)((N + 15) / 16);
     const size_t red = (size_t)NWV * 16 * MT * 16 * sizeof(int);
     const size_t lds = (F ? 4 * (size_t)K : 0) + red;
     hipLaunchKernelGGL((k_skinny<MT, NWV, Q, F>), dim3(blocks), dim3(NWV * kWave), lds, s, X, Xq, xs, rs, (int)M,
                        (int)K, rms ? 1 : 0, gain, eps, packed, ws, (int)N, epi,
-                       residual, Y, acc_out);
+                       aux, Y, acc_out);
     return hipGetLastError();
 }
 
 template <int MT, bool F>
 hipError_t go_mt(const Plan& p, const float* X, const int8_t* Xq, const float* xs, const int32_t* rs, int64_t M,
                  int64_t K, bool rms, const float* gain, float eps, const uint8_t* packed, const float* ws,
-                 int64_t N, uint32_t epi, const float* residual, float* Y, int32_t* acc_out, hipStream_t s) {
+                 int64_t N, uint32_t epi, const float* aux, float* Y, int32_t* acc_out, hipStream_t s) {
 #define BL_SK(NWV, Q)                                                                                     \
     if (p.nw == NWV && p.qmax == Q)                                                                       \
-        return go<MT, NWV, Q, F>(X, Xq, xs, rs, M, K, rms, gain, eps, packed, ws, N, epi, residual, Y, acc_out, s);
+        return go<MT, NWV, Q, F>(X, Xq, xs, rs, M, K, rms, gain, eps, packed, ws, N, epi, aux, Y, acc_out, s);
     BL_SK(4, 2)
     BL_SK(4, 4)
     BL_SK(8, 4)
@@ -252,13 +253,13 @@ hipError_t launch_gemv(const int8_t* Xq, const float* xs, const int32_t* rs, int
     const int mt = (int)((M + 15) / 16);
     switch (mt) {
         case 1: return go_mt<1, false>(p, nullptr, Xq, xs, rs, M, K, false, nullptr, 0.f, packed, ws, N, epi.flags,
-                                       epi.residual, Y, acc_out, s);
+                                       epi.aux, Y, acc_out, s);
         case 2: return go_mt<2, false>(p, nullptr, Xq, xs, rs, M, K, false, nullptr, 0.f, packed, ws, N, epi.flags,
-                                       epi.residual, Y, acc_out, s);
+                                       epi.aux, Y, acc_out, s);
         case 3: return go_mt<3, false>(p, nullptr, Xq, xs, rs, M, K, false, nullptr, 0.f, packed, ws, N, epi.flags,
-                                       epi.residual, Y, acc_out, s);
+                                       epi.aux, Y, acc_out, s);
         case 4: return go_mt<4, false>(p, nullptr, Xq, xs, rs, M, K, false, nullptr, 0.f, packed, ws, N, epi.flags,
-                                       epi.residual, Y, acc_out, s);
+                                       epi.aux, Y, acc_out, s);
         default: return hipErrorInvalidValue;
     }
 }
@@ -271,11 +272,11 @@ bool decode_supported(int64_t M, int64_t K, int64_t N) {
 
 hipError_t launch_decode_bitlinear(const float* X, int64_t M, int64_t K, bool rmsnorm, const float* gain, float eps,
                                    const uint8_t* packed, const float* w_scale, int64_t N, uint32_t epi,
-                                   const float* residual, float* Y, hipStream_t s) {
+                                   const float* aux, float* Y, hipStream_t s) {
     Plan p;
     if (!plan(K, p)) return hipErrorInvalidValue;
     return go_mt<1, true>(p, X, nullptr, nullptr, nullptr, M, K, rmsnorm, gain, eps, packed, w_scale, N, epi,
-                          residual, Y, nullptr, s);
+                          aux, Y, nullptr, s);
 }
 
 }  // namespace bl

@@ -81,7 +81,7 @@ const char* bitlinear_last_error(void);
 
 /* ABI version of this header, (major << 16) | minor. */
 int bitlinear_abi_version(void);
-#define BITLINEAR_ABI_VERSION ((1 << 16) | 0)
+#define BITLINEAR_ABI_VERSION ((1 << 16) | 1)
 
 /* ------------------------------------------------------------------------
  * Weight packing ("Model details" / Quantization: absmean ternary weights).
@@ -137,6 +137,9 @@ int bitlinear_quant_act(const float* X, int64_t M, int64_t K, uint32_t flags,
  *   y[m][n]   = (float)acc[m][n] * ((x_scale[m] * w_scale) / 127)
  *   BL_EPI_RELU2:       y = max(y, 0)^2
  *   BL_EPI_RESIDUAL:    y = y + residual[m][n]
+ *   BL_EPI_MUL:         y = y * mul_by[m][n]   (after ReLU^2; the gating
+ *                       product ReLU^2(gate) * up of a gated feed-forward
+ *                       block; not together with BL_EPI_RESIDUAL)
  *   BL_EPI_SUBLN_QUANT: out_q, out_q_scale, out_q_rowsum = the
  *                       bitlinear_quant_act of y with BL_QUANT_RMSNORM,
  *                       gain norm_gain (NULL = ones), eps norm_eps.
@@ -148,14 +151,16 @@ int bitlinear_quant_act(const float* X, int64_t M, int64_t K, uint32_t flags,
  * w_scale    in  fp32 [1]
  * epi        in  host pointer to a bl_epilogue, or NULL for plain dequant
  * Y          out fp32 [M][N]; may be NULL only with BL_EPI_SUBLN_QUANT.
- *                With BL_EPI_RESIDUAL, Y may equal residual (in place); any
- *                other overlap between outputs and inputs is not allowed.
+ *                With BL_EPI_RESIDUAL (BL_EPI_MUL), Y may equal residual
+ *                (mul_by), in place; any other overlap between outputs and
+ *                inputs is not allowed.
  * acc_out    out int32 [M][N], the exact accumulators, or NULL
  * ws         scratch of bitlinear_forward_workspace_bytes(M, K, N, flags)
  * ---------------------------------------------------------------------- */
 #define BL_EPI_RELU2       0x1u
 #define BL_EPI_RESIDUAL    0x2u
 #define BL_EPI_SUBLN_QUANT 0x4u
+#define BL_EPI_MUL         0x8u
 
 typedef struct bl_epilogue {
     uint32_t flags;          /* BL_EPI_* bits */
@@ -165,6 +170,7 @@ typedef struct bl_epilogue {
     int8_t* out_q;           /* [M][N] requantised output */
     float* out_q_scale;      /* [M] its absmax scales */
     int32_t* out_q_rowsum;   /* [M] its row sums, or NULL */
+    const float* mul_by;     /* [M][N] for BL_EPI_MUL */
 } bl_epilogue;
 
 size_t bitlinear_forward_workspace_bytes(int64_t M, int64_t K, int64_t N,
@@ -186,9 +192,10 @@ int bitlinear_forward(const int8_t* Xq, const float* x_scale,
  * quant_flags     BL_QUANT_RMSNORM or 0; norm_gain / norm_eps as in
  *                 bitlinear_quant_act
  * packed, w_scale, N  as in bitlinear_forward
- * epi         in  host pointer or NULL; only BL_EPI_RELU2 and BL_EPI_RESIDUAL
- *                 are accepted here (BL_ERR_UNSUPPORTED otherwise)
- * Y           out fp32 [M][N]; may equal epi->residual (in place)
+ * epi         in  host pointer or NULL; BL_EPI_RELU2, BL_EPI_RESIDUAL and
+ *                 BL_EPI_MUL are accepted here (BL_ERR_UNSUPPORTED otherwise)
+ * Y           out fp32 [M][N]; may equal epi->residual or epi->mul_by
+ *                 (in place)
  * ws          scratch of bitlinear_quant_forward_workspace_bytes(M, K, N)
  * ---------------------------------------------------------------------- */
 size_t bitlinear_quant_forward_workspace_bytes(int64_t M, int64_t K, int64_t N);
@@ -206,6 +213,8 @@ int bitlinear_quant_forward(const float* X, int64_t M, int64_t K, uint32_t quant
  *   u  = BL_FFN_PRE_NORM ? RMSNorm(hidden; pre_norm_gain) : hidden
  *   xq = absmax-quant(u)
  *   y1 = ReLU^2(BitLinear(xq; up))                          [M][F]
+ *        or, for a gated layer (gate != NULL),
+ *   y1 = ReLU^2(BitLinear(xq; gate)) * BitLinear(xq; up)    [M][F]
  *   x2 = absmax-quant(RMSNorm(y1; sub_norm_gain))           subln
  *   y2 = BitLinear(x2; down)                                [M][H]
  *   hidden = BL_FFN_RESIDUAL ? hidden + y2 : y2
@@ -215,7 +224,7 @@ int bitlinear_quant_forward(const float* X, int64_t M, int64_t K, uint32_t quant
  * norm_eps   eps of both RMSNorms (1e-5)
  * ws         scratch of bitnet_ffn_workspace_bytes(M, H, F); calls that
  *            share one workspace must not overlap in time.
- * Gated blocks (gate != NULL) return BL_ERR_UNSUPPORTED.
+ * A gate matrix needs its scale (gate_scale) and has the up matrix's shape.
  * ---------------------------------------------------------------------- */
 #define BL_FFN_PRE_NORM 0x1u
 #define BL_FFN_RESIDUAL 0x2u
@@ -224,8 +233,8 @@ typedef struct bitnet_ffn_layer {
     const float* pre_norm_gain;  /* [H] or NULL (ones) */
     const uint8_t* up;           /* [F][H/4] packed */
     const float* up_scale;       /* [1] */
-    const uint8_t* gate;         /* must be NULL */
-    const float* gate_scale;     /* must be NULL */
+    const uint8_t* gate;         /* [F][H/4] packed, or NULL (ungated) */
+    const float* gate_scale;     /* [1], with gate */
     const float* sub_norm_gain;  /* [F] or NULL (ones) */
     const uint8_t* down;         /* [H][F/4] packed */
     const float* down_scale;     /* [1] */

@@ -46,7 +46,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.bitlinear_abi_version() == (1 << 16)
+    assert lib.bitlinear_abi_version() == (1 << 16) | 1
     for s in range(-6, 1):
         assert lib.bitlinear_status_string(s)
     assert lib.bitlinear_status_string(-99) == b"unknown status"
@@ -118,6 +118,13 @@ def test_forward_validation(lib):
     assert f(A, B, D, 1, 64, C, D, 72, ctypes.byref(e), A, None, None, 0, None) == bl.BL_ERR_SHAPE
     e = E(flags=0x40)
     assert f(A, B, D, 1, 64, C, D, 8, ctypes.byref(e), A, None, None, 0, None) == bl.BL_ERR_UNSUPPORTED
+    # gating product: needs mul_by, 16-byte aligned, and not with the residual add
+    e = E(flags=bl.BL_EPI_MUL)
+    assert f(A, B, D, 1, 64, C, D, 8, ctypes.byref(e), A, None, None, 0, None) == bl.BL_ERR_NULL
+    e = E(flags=bl.BL_EPI_MUL, mul_by=MIS.value)
+    assert f(A, B, D, 1, 64, C, D, 8, ctypes.byref(e), A, None, None, 0, None) == bl.BL_ERR_ALIGN
+    e = E(flags=bl.BL_EPI_MUL | bl.BL_EPI_RESIDUAL, mul_by=A.value, residual=B.value)
+    assert f(A, B, D, 1, 64, C, D, 8, ctypes.byref(e), A, None, None, 0, None) == bl.BL_ERR_UNSUPPORTED
     # empty batch with everything else valid
     assert f(A, B, D, 0, 64, C, D, 8, nul, A, None, None, 0, None) == bl.BL_OK
 
@@ -134,8 +141,12 @@ def test_ffn_validation(lib):
     assert f(L, 1, A, 1, 64, 64, 3, 1e-5, None, 0, None) == bl.BL_ERR_WORKSPACE
     G = (bl.FFNLayer * 1)()
     ctypes.memmove(G, L, ctypes.sizeof(L))
-    G[0].gate = A.value
-    assert f(G, 1, A, 1, 64, 64, 3, 1e-5, None, 0, None) == bl.BL_ERR_UNSUPPORTED
+    G[0].gate = A.value          # a gate needs its scale
+    assert f(G, 1, A, 1, 64, 64, 3, 1e-5, None, 0, None) == bl.BL_ERR_NULL
+    G[0].gate_scale = MIS.value + 2  # and both need their alignment (4 bytes for a scale)
+    assert f(G, 1, A, 1, 64, 64, 3, 1e-5, None, 0, None) == bl.BL_ERR_ALIGN
+    G[0].gate_scale = B.value    # a valid gated layer then needs the workspace
+    assert f(G, 1, A, 1, 64, 64, 3, 1e-5, None, 0, None) == bl.BL_ERR_WORKSPACE
     Z = (bl.FFNLayer * 1)()
     assert f(Z, 1, A, 1, 64, 64, 3, 1e-5, None, 0, None) == bl.BL_ERR_NULL
     assert f(L, 0, A, 1, 64, 64, 3, 1e-5, None, 0, None) == bl.BL_OK
@@ -159,6 +170,10 @@ def test_quant_forward_validation(lib):
     assert f(A, 1, 64, 0, None, 1e-5, B, C, 8, ctypes.byref(e), D, None, 0, None) == bl.BL_ERR_UNSUPPORTED
     e = E(flags=bl.BL_EPI_RESIDUAL)
     assert f(A, 1, 64, 0, None, 1e-5, B, C, 8, ctypes.byref(e), D, None, 0, None) == bl.BL_ERR_NULL
+    e = E(flags=bl.BL_EPI_MUL)
+    assert f(A, 1, 64, 0, None, 1e-5, B, C, 8, ctypes.byref(e), D, None, 0, None) == bl.BL_ERR_NULL
+    e = E(flags=bl.BL_EPI_MUL | bl.BL_EPI_RESIDUAL, mul_by=A.value, residual=B.value)
+    assert f(A, 1, 64, 0, None, 1e-5, B, C, 8, ctypes.byref(e), D, None, 0, None) == bl.BL_ERR_UNSUPPORTED
     assert f(A, 1, 96, 0, None, 1e-5, B, C, 8, nul, D, None, 0, None) == bl.BL_ERR_SHAPE
     assert f(A, 1, 64, 0, None, 1e-5, B, C, 0, nul, D, None, 0, None) == bl.BL_ERR_SHAPE
     assert f(A, 1, 64, 0, None, 1e-5, B, C, 8, nul, MIS, None, 0, None) == bl.BL_ERR_ALIGN

@@ -333,6 +333,115 @@ def test_ffn_no_prenorm_no_residual():
     assert_exact(host(hs), h, "ffn flags=0")
 
 
+# ------------------------------------------------------------------ gating product, gated FFN
+
+@pytest.mark.parametrize("M", [1, 3, 12, 70, 130])
+@pytest.mark.parametrize("K,N", [(256, 512), (320, 130)])
+def test_forward_mul_epilogue(M, K, N):
+    """y = ReLU^2(dequant(acc)) * aux, written in place over aux, through the
+    skinny (M <= 64) and GEMM paths; the fused quantise + forward (M <= 4
+    one launch) gives the same values."""
+    log(f"[mul epilogue] M={M} K={K} N={N}")
+    rng = np.random.default_rng(M * 13 + K + N)
+    X = synth.activations(rng, M, K, outliers=True)
+    W = synth.weights(rng, N, K)
+    aux = rng.standard_normal((M, N)).astype(np.float32)
+    p, s, q, g = check_pack(W, "mul")
+    xq, xs, rs = bl.quant_act(dev(X))
+    a = dev(aux)
+    out = bl.forward(xq, xs, p, s, x_rowsum=rs, relu2=True, mul_by=a, y_out=a, want_acc=True)
+    rq = oracle.quant_act(X)
+    acc = oracle.int_matmul(rq[0], q)
+    assert_exact(host(out["acc"]), acc, "acc")
+    assert_y_close(host(a), oracle.mul(oracle.relu2(oracle.dequant(acc, rq[1], g)), aux), "relu2 * aux")
+    if M <= 12:
+        a2 = dev(aux)
+        bl.quant_forward(dev(X), p, s, relu2=True, mul_by=a2, y_out=a2)
+        assert_exact(host(a2), host(a), "quant_forward vs forward")
+
+
+def gated_layers_np(rng, n, H, F, gains=False):
+    out = []
+    for _ in range(n):
+        Wg = synth.weights(rng, F, H)
+        Wu = synth.weights(rng, F, H)
+        Wd = synth.weights(rng, H, F)
+        pre = synth.gains(rng, H) if gains else None
+        sub = synth.gains(rng, F) if gains else None
+        out.append((Wg, Wu, Wd, pre, sub))
+    return out
+
+
+def to_gpu_gated(layers_np):
+    gl, ol = [], []
+    for Wg, Wu, Wd, pre, sub in layers_np:
+        pg, sg, qg, gg = check_pack(Wg, "ffn gate")
+        pu, su, qu, gu = check_pack(Wu, "ffn up")
+        pd, sd, qd, gd = check_pack(Wd, "ffn down")
+        gl.append({"gate": pg, "gate_scale": sg, "up": pu, "up_scale": su, "down": pd, "down_scale": sd,
+                   "pre_norm_gain": None if pre is None else dev(pre),
+                   "sub_norm_gain": None if sub is None else dev(sub)})
+        ol.append({"q_gate": qg, "gamma_gate": gg, "q_up": qu, "gamma_up": gu, "q_down": qd, "gamma_down": gd,
+                   "pre_gain": pre if pre is not None else np.ones(Wu.shape[1], np.float32), "sub_gain": sub})
+    return gl, ol
+
+
+def gated_layer_teacher_forced(h_in, G, O, pre=True, residual=True):
+    """One gated layer through the C ABI stage by stage (up, then gate with
+    ReLU^2 * up and the subln requantisation, then down), each stage against
+    the oracle fed with the GPU's inputs to it.  Returns (output, flips)."""
+    flips = 0
+    xq, xs, rs = bl.quant_act(dev(h_in), rmsnorm=pre, norm_gain=G["pre_norm_gain"])
+    z = oracle.rmsnorm(h_in, O["pre_gain"]) if pre else h_in
+    flips += check_requant(z, host(xq), host(xs), host(rs), "gated input quant")
+    up = bl.forward(xq, xs, G["up"], G["up_scale"], x_rowsum=rs, want_acc=True)
+    acc_u = oracle.int_matmul(host(xq), O["q_up"])
+    assert_exact(host(up["acc"]), acc_u, "gated up acc")
+    yu = host(up["y"])
+    assert_y_close(yu, oracle.dequant(acc_u, host(xs), O["gamma_up"]), "gated up y")
+    gt = bl.forward(xq, xs, G["gate"], G["gate_scale"], x_rowsum=rs, relu2=True, mul_by=up["y"], subln=True,
+                    norm_gain=G["sub_norm_gain"], want_acc=True)
+    acc_g = oracle.int_matmul(host(xq), O["q_gate"])
+    assert_exact(host(gt["acc"]), acc_g, "gate acc")
+    hh = host(gt["y"])
+    assert_y_close(hh, oracle.mul(oracle.relu2(oracle.dequant(acc_g, host(xs), O["gamma_gate"])), yu), "gated h")
+    flips += check_requant(oracle.rmsnorm(hh, O["sub_gain"]), host(gt["q"]), host(gt["q_scale"]),
+                           host(gt["q_rowsum"]), "gated subln")
+    h = dev(h_in)
+    dn = bl.forward(gt["q"], gt["q_scale"], G["down"], G["down_scale"], x_rowsum=gt["q_rowsum"],
+                    residual=h if residual else None, y_out=h, want_acc=True)
+    acc2 = oracle.int_matmul(host(gt["q"]), O["q_down"])
+    assert_exact(host(dn["acc"]), acc2, "gated down acc")
+    y2 = oracle.dequant(acc2, host(gt["q_scale"]), O["gamma_down"])
+    assert_y_close(host(h), oracle.add(h_in, y2) if residual else y2, "gated down y")
+    return host(h), flips
+
+
+@pytest.mark.parametrize("M", [1, 3, 20])
+def test_ffn_gated_block(M):
+    """Gated FFN layers (ReLU^2(gate) * up): teacher-forced stage by stage,
+    then the stack call (fused decode kernels for M <= 4, staged kernels
+    otherwise) exactly equal to the staged calls, twice in a row."""
+    log(f"[ffn gated] M={M}")
+    rng = np.random.default_rng(1900 + M)
+    H, F, L = 256, 640, 2
+    gl, ol = to_gpu_gated(gated_layers_np(rng, L, H, F, gains=True))
+    h0 = synth.activations(rng, M, H)
+    h = h0
+    for l in range(L):
+        h, _ = gated_layer_teacher_forced(h, gl[l], ol[l])
+    stack = bl.FFNStack(gl, H, F, M, DEV)
+    for rep in range(2):
+        hs = dev(h0)
+        stack(hs)
+        assert_exact(host(hs), h, f"gated stack vs staged calls (call {rep})")
+    ref = h0
+    for O in ol:
+        ref = oracle.ffn_layer_gated(ref, O["q_gate"], O["gamma_gate"], O["q_up"], O["gamma_up"], O["q_down"],
+                                     O["gamma_down"], pre_gain=O["pre_gain"], sub_gain=O["sub_gain"])
+    assert np.abs(host(hs) - ref).max() <= 1e-3 * np.abs(ref).max()
+
+
 # ------------------------------------------------------------------ the five workloads
 
 def test_workload_single_bitlinear():
