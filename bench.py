@@ -316,6 +316,25 @@ def main():
     eager_s = (time.perf_counter() - t) / 200
     del g
 
+    # gated variant of the same step (context): ReLU^2(gate) * up, one
+    # launch streaming gate and up, then the down launch; 3 matrices per step
+    gate_w = torch.from_numpy(synth.weights(np.random.default_rng(6), F, H)).to(dev)
+    pg, sg = bl.pack_weights(gate_w)
+    del gate_w
+    gstacks = [bl.FFNStack([dict(L, gate=pg.clone(), gate_scale=sg)], H, F, 1, dev, pre_norm=False,
+                           residual=False) for L in layers[:max(8, R * 2 // 3)]]
+    RG = len(gstacks)
+
+    def gsteps(n):
+        for i in range(n):
+            gstacks[i % RG](h)
+
+    gsteps(50)
+    gated_s, gg = time_graph(torch, lambda: gsteps(4 * RG), reps=2)
+    del gg
+    gated_s /= 4 * RG
+    log(f"gated decode step (graph): {gated_s * 1e6:.2f} us -> {1.5 * PACKED_BYTES_STEP / gated_s / 1e9:.1f} GB/s")
+
     # dominant kernel: the step's up kernel (fused absmax quant + up BitLinear
     # + ReLU^2 at M=1), back to back over the weight copies; then the down one
     L_launch = 4 * R
@@ -348,7 +367,7 @@ def main():
                 "kernel": "k_skinny<1,4,4,true> (absmax quant + up BitLinear + ReLU^2, M=1, K=2560, N=6912)",
                 "bytes_per_launch": PACKED_BYTES_MATRIX, "us_per_launch": round(gemv_s * 1e6, 3),
                 "down_us_per_launch": round(gemv_dn_s * 1e6, 3)}
-    del layers, stacks, ups, dns
+    del layers, stacks, ups, dns, gstacks
     torch.cuda.empty_cache()
 
     # ---------------------------------------------------------------- decode, M=1, per BitLinear shape
@@ -439,7 +458,9 @@ def main():
                       "weight_copies": R, "cache": "cold: rotating packed-weight copies exceed 2x the "
                                                    "256 MB Infinity Cache",
                       "launch": "HIP graph of the K steps", "eager_us_per_step": round(eager_s * 1e6, 2),
-                      "pack_ms_up_plus_down": round(pack_t * 1e3, 4)},
+                      "pack_ms_up_plus_down": round(pack_t * 1e3, 4),
+                      "gated_step_us": round(gated_s * 1e6, 3),
+                      "gated_step_GB_per_s": round(1.5 * PACKED_BYTES_STEP / gated_s / 1e9, 1)},
            "roofline": roofline, "cpu_baseline": cpu, "prefill": prefill, "decode_shapes": shapes}
     print(json.dumps(out), flush=True)
 

@@ -339,21 +339,16 @@ int bitnet_ffn_forward(const bitnet_ffn_layer* layers, int32_t n_layers, float* 
     const bool pre = (flags & BL_FFN_PRE_NORM) != 0;
     const bool res = (flags & BL_FFN_RESIDUAL) != 0;
 
-    // Few tokens: two launches per layer (three when gated), each quantising
-    // its own input rows.  Gated: y1 = up, then y1 = ReLU^2(gate) * y1 in place.
+    // Few tokens: two launches per layer, each quantising its own input rows
+    // (a gated layer streams gate and up in the first one).
     if (bl::decode_supported(M, H, F) && bl::decode_supported(M, F, H)) {
         for (int32_t l = 0; l < n_layers; ++l) {
             const bitnet_ffn_layer& L = layers[l];
-            const bool gated = L.gate != nullptr;
-            hipError_t e = bl::launch_decode_bitlinear(hidden, M, H, pre, L.pre_norm_gain, norm_eps, L.up,
-                                                       L.up_scale, F, gated ? 0u : bl::kEpiRelu2, nullptr, y1,
-                                                       stream);
-            if (e != hipSuccess) return hip_status(e, "ffn: decode up");
-            if (gated) {
-                e = bl::launch_decode_bitlinear(hidden, M, H, pre, L.pre_norm_gain, norm_eps, L.gate, L.gate_scale,
-                                                F, bl::kEpiRelu2 | bl::kEpiMul, y1, y1, stream);
-                if (e != hipSuccess) return hip_status(e, "ffn: decode gate");
-            }
+            hipError_t e = L.gate ? bl::launch_decode_gated(hidden, M, H, pre, L.pre_norm_gain, norm_eps, L.up,
+                                                            L.up_scale, L.gate, L.gate_scale, F, y1, stream)
+                                  : bl::launch_decode_bitlinear(hidden, M, H, pre, L.pre_norm_gain, norm_eps, L.up,
+                                                                L.up_scale, F, bl::kEpiRelu2, nullptr, y1, stream);
+            if (e != hipSuccess) return hip_status(e, "ffn: decode up/gate");
             e = bl::launch_decode_bitlinear(y1, M, F, true, L.sub_norm_gain, norm_eps, L.down, L.down_scale, H,
                                             res ? bl::kEpiResidual : 0u, res ? hidden : nullptr, hidden, stream);
             if (e != hipSuccess) return hip_status(e, "ffn: decode down");

@@ -66,5 +66,10 @@ bool decode_supported(int64_t M, int64_t K, int64_t N);
 hipError_t launch_decode_bitlinear(const float* X, int64_t M, int64_t K, bool rmsnorm, const float* gain,
                                    float eps, const uint8_t* packed, const float* w_scale, int64_t N,
                                    uint32_t epi, const float* aux, float* Y, hipStream_t s);
+// The same for a gated pair: Y = ReLU^2(BitLinear(x; gate)) * BitLinear(x; up),
+// both from one in-workgroup quantisation of the rows.
+hipError_t launch_decode_gated(const float* X, int64_t M, int64_t K, bool rmsnorm, const float* gain, float eps,
+                               const uint8_t* up, const float* up_scale, const uint8_t* gate,
+                               const float* gate_scale, int64_t N, float* Y, hipStream_t s);
 
 }  // namespace bl

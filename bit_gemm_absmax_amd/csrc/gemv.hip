@@ -35,13 +35,16 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 
 // QMAX 16-byte weight chunks per lane; with fp32 input the activation row
 // takes QMAX float4 per thread as well (quant_row_*: K <= 4 * NT * QMAX,
-// which the plan below guarantees).
-template <int MTILES, int NWV, int QMAX, bool F32IN>
+// which the plan below guarantees).  GATED: a second matrix Wg (the gate)
+// of the same shape is streamed by the same lanes against the same
+// quantised rows, and the output is ReLU^2(gate) * up (Wp is up).
+template <int MTILES, int NWV, int QMAX, bool F32IN, bool GATED = false>
 __global__ __launch_bounds__(NWV* kWave) void k_skinny(
     const float* __restrict__ X, const int8_t* __restrict__ Xq, const float* __restrict__ x_scale,
     const int32_t* __restrict__ x_rowsum, int M, int K, int rmsnorm, const float* __restrict__ gain,
     float eps, const uint8_t* __restrict__ Wp, const float* __restrict__ w_scale, int N, uint32_t epi_flags,
-    const float* aux, float* Y, int32_t* __restrict__ acc_out) {
+    const float* aux, float* Y, int32_t* __restrict__ acc_out, const uint8_t* __restrict__ Wg,
+    const float* __restrict__ g_scale) {
     constexpr int NT = NWV * kWave;
     constexpr int ROWS = 16 * MTILES;
     extern __shared__ __align__(16) int8_t lds[];  // [fp32 input: xq, M <= 4 rows of K] [partials]
@@ -58,6 +61,7 @@ __global__ __launch_bounds__(NWV* kWave) void k_skinny(
     const int C = K / 64;          // 64-weight chunks per row
     const int nq = (C + 3) / 4;    // chunk quads
     const float ws = *w_scale;
+    const float gws = GATED ? *g_scale : 0.0f;
 
     // ---- every load up front, in the order they are needed: the first fp32
     // activation row (and the norm gain), the weights, then the epilogue's
@@ -77,6 +81,17 @@ __global__ __launch_bounds__(NWV* kWave) void k_skinny(
             const int s = wave + i * NWV;
             const int c = 4 * s + fg;
             w[i] = buf_load16(rw, (s < nq && c < C) ? (uint32_t)(fr * C + c) * 16u : kOob);
+        }
+    }
+    uint4 wg[GATED ? QMAX : 1];
+    if constexpr (GATED) {
+        const int rows = N - n0 < 16 ? N - n0 : 16;
+        const Rsrc rg = make_rsrc(Wg + (int64_t)n0 * (K / 4), (uint32_t)rows * (uint32_t)(K / 4));
+#pragma unroll
+        for (int i = 0; i < QMAX; ++i) {
+            const int s = wave + i * NWV;
+            const int c = 4 * s + fg;
+            wg[i] = buf_load16(rg, (s < nq && c < C) ? (uint32_t)(fr * C + c) * 16u : kOob);
         }
     }
     const bool e_first = (int)threadIdx.x < M * 16;
@@ -122,9 +137,13 @@ __global__ __launch_bounds__(NWV* kWave) void k_skinny(
     // ---- contraction.  A chunk past the row end has zero weights (its load
     // was out of range), so its activation offset is clamped to 0 and it adds
     // nothing.
-    v4i acc[MTILES];
+    v4i acc[MTILES], accg[GATED ? MTILES : 1];
 #pragma unroll
     for (int t = 0; t < MTILES; ++t) acc[t] = v4i{0, 0, 0, 0};
+    if constexpr (GATED) {
+#pragma unroll
+        for (int t = 0; t < MTILES; ++t) accg[t] = v4i{0, 0, 0, 0};
+    }
 #pragma unroll
     for (int i = 0; i < QMAX; ++i) {
         const int s = wave + i * NWV;
@@ -139,6 +158,11 @@ __global__ __launch_bounds__(NWV* kWave) void k_skinny(
                 for (int t = 0; t < MTILES; ++t) {
                     const v4i a = *reinterpret_cast<const v4i*>(arow[t] + koff + 16 * d);
                     acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, acc[t], 0, 0, 0);
+                    if constexpr (GATED) {
+                        const uint32_t g4 = d == 0 ? wg[i].x : d == 1 ? wg[i].y : d == 2 ? wg[i].z : wg[i].w;
+                        const v4i bg = v4i{codes4(g4, 0), codes4(g4, 1), codes4(g4, 2), codes4(g4, 3)};
+                        accg[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, bg, accg[t], 0, 0, 0);
+                    }
                 }
             }
         }
@@ -146,13 +170,17 @@ __global__ __launch_bounds__(NWV* kWave) void k_skinny(
 
     // ---- per-wave partial tiles -> LDS (a region of its own) -> epilogue,
     // summing the waves in index order
-    int* red = reinterpret_cast<int*>(lds + (F32IN ? 4 * K : 0));  // [NWV][ROWS][16]
+    int* red = reinterpret_cast<int*>(lds + (F32IN ? 4 * K : 0));  // [NWV][ROWS][16], gate after it
+    int* redg = red + NWV * ROWS * 16;
 #pragma unroll
     for (int t = 0; t < MTILES; ++t)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int m = 16 * t + 4 * fg + r;
-            if (m < M) red[(wave * ROWS + m) * 16 + fr] = acc[t][r];
+            if (m < M) {
+                red[(wave * ROWS + m) * 16 + fr] = acc[t][r];
+                if constexpr (GATED) redg[(wave * ROWS + m) * 16 + fr] = accg[t][r];
+            }
         }
     __syncthreads();
     for (int i = threadIdx.x; i < M * 16; i += NT) {
@@ -160,29 +188,42 @@ __global__ __launch_bounds__(NWV* kWave) void k_skinny(
         const int n = n0 + col;
         if (n < N) {
             const bool first = i == (int)threadIdx.x;
-            int a = 0;
+            int a = 0, ag = 0;
 #pragma unroll
             for (int q = 0; q < NWV; ++q) a += red[(q * ROWS + m) * 16 + col];
+            if constexpr (GATED) {
+#pragma unroll
+                for (int q = 0; q < NWV; ++q) ag += redg[(q * ROWS + m) * 16 + col];
+            }
             float xs;
+            int rs;
             if constexpr (F32IN) {
-                int rs = 0;
+                rs = 0;
 #pragma unroll
                 for (int q = 0; q < NWV; ++q) rs += islot[m][q];
-                a -= rs;
                 xs = gx[m];
             } else {
-                a -= first ? e_rs : x_rowsum[m];
+                rs = first ? e_rs : x_rowsum[m];
                 xs = first ? e_xs : x_scale[m];
             }
+            a -= rs;
             const float d = (xs * ws) / 127.0f;
             float y = (float)a * d;
-            if (epi_flags & kEpiRelu2) {
-                const float tt = y > 0.0f ? y : 0.0f;
-                y = tt * tt;
-            }
             const int64_t o = (int64_t)m * N + n;
-            if (epi_flags & kEpiMul) y = y * (first ? e_res : aux[o]);
-            else if (epi_flags & kEpiResidual) y = y + (first ? e_res : aux[o]);
+            if constexpr (GATED) {
+                // ReLU^2(gate) * up, in that order
+                ag -= rs;
+                float t = (float)ag * ((xs * gws) / 127.0f);
+                t = t > 0.0f ? t : 0.0f;
+                y = (t * t) * y;
+            } else {
+                if (epi_flags & kEpiRelu2) {
+                    const float tt = y > 0.0f ? y : 0.0f;
+                    y = tt * tt;
+                }
+                if (epi_flags & kEpiMul) y = y * (first ? e_res : aux[o]);
+                else if (epi_flags & kEpiResidual) y = y + (first ? e_res : aux[o]);
+            }
             if (Y != nullptr) Y[o] = y;
             if (acc_out != nullptr) acc_out[o] = a;
         }
@@ -209,26 +250,28 @@ bool plan(int64_t K, Plan& p) {
     return true;
 }
 
-template <int MT, int NWV, int Q, bool F>
+template <int MT, int NWV, int Q, bool F, bool G>
 hipError_t go(const float* X, const int8_t* Xq, const float* xs, const int32_t* rs, int64_t M, int64_t K, bool rms,
               const float* gain, float eps, const uint8_t* packed, const float* ws, int64_t N, uint32_t epi,
-              const float* aux, float* Y, int32_t* acc_out, hipStream_t s) {
+              const float* aux, float* Y, int32_t* acc_out, const uint8_t* gate, const float* gate_scale,
+              hipStream_t s) {
     const unsigned blocks = (unsigned)((N + 15) / 16);
-    const size_t red = (size_t)NWV * 16 * MT * 16 * sizeof(int);
+    const size_t red = (size_t)NWV * 16 * MT * 16 * sizeof(int) * (G ? 2 : 1);
     const size_t lds = (F ? 4 * (size_t)K : 0) + red;
-    hipLaunchKernelGGL((k_skinny<MT, NWV, Q, F>), dim3(blocks), dim3(NWV * kWave), lds, s, X, Xq, xs, rs, (int)M,
-                       (int)K, rms ? 1 : 0, gain, eps, packed, ws, (int)N, epi,
-                       aux, Y, acc_out);
+    hipLaunchKernelGGL((k_skinny<MT, NWV, Q, F, G>), dim3(blocks), dim3(NWV * kWave), lds, s, X, Xq, xs, rs, (int)M,
+                       (int)K, rms ? 1 : 0, gain, eps, packed, ws, (int)N, epi, aux, Y, acc_out, gate, gate_scale);
     return hipGetLastError();
 }
 
-template <int MT, bool F>
+template <int MT, bool F, bool G = false>
 hipError_t go_mt(const Plan& p, const float* X, const int8_t* Xq, const float* xs, const int32_t* rs, int64_t M,
                  int64_t K, bool rms, const float* gain, float eps, const uint8_t* packed, const float* ws,
-                 int64_t N, uint32_t epi, const float* aux, float* Y, int32_t* acc_out, hipStream_t s) {
+                 int64_t N, uint32_t epi, const float* aux, float* Y, int32_t* acc_out, hipStream_t s,
+                 const uint8_t* gate = nullptr, const float* gate_scale = nullptr) {
 #define BL_SK(NWV, Q)                                                                                     \
     if (p.nw == NWV && p.qmax == Q)                                                                       \
-        return go<MT, NWV, Q, F>(X, Xq, xs, rs, M, K, rms, gain, eps, packed, ws, N, epi, aux, Y, acc_out, s);
+        return go<MT, NWV, Q, F, G>(X, Xq, xs, rs, M, K, rms, gain, eps, packed, ws, N, epi, aux, Y, acc_out,  \
+                                    gate, gate_scale, s);
     BL_SK(4, 2)
     BL_SK(4, 4)
     BL_SK(8, 4)
@@ -277,6 +320,15 @@ hipError_t launch_decode_bitlinear(const float* X, int64_t M, int64_t K, bool rm
     if (!plan(K, p)) return hipErrorInvalidValue;
     return go_mt<1, true>(p, X, nullptr, nullptr, nullptr, M, K, rmsnorm, gain, eps, packed, w_scale, N, epi,
                           aux, Y, nullptr, s);
+}
+
+hipError_t launch_decode_gated(const float* X, int64_t M, int64_t K, bool rmsnorm, const float* gain, float eps,
+                               const uint8_t* up, const float* up_scale, const uint8_t* gate,
+                               const float* gate_scale, int64_t N, float* Y, hipStream_t s) {
+    Plan p;
+    if (!plan(K, p)) return hipErrorInvalidValue;
+    return go_mt<1, true, true>(p, X, nullptr, nullptr, nullptr, M, K, rmsnorm, gain, eps, up, up_scale, N, 0u,
+                                nullptr, Y, nullptr, s, gate, gate_scale);
 }
 
 }  // namespace bl
