@@ -37,6 +37,8 @@ bool quant_supported(int64_t K);
 // to 16384, else 1024); every kernel that quantises rows uses this size, so
 // all of them reduce in the same order.
 int quant_threads(int64_t K);
+// float4 per thread that cover a row of length K at quant_threads(K).
+int quant_depth(int64_t K);
 
 // rowsum[m] = sum_k Xq[m][k]
 hipError_t launch_rowsum(const int8_t* Xq, int64_t M, int64_t K, int32_t* rowsum,

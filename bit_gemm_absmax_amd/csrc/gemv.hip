@@ -34,11 +34,12 @@ namespace {
 typedef int v4i __attribute__((ext_vector_type(4)));
 
 // QMAX 16-byte weight chunks per lane; with fp32 input the activation row
-// takes QMAX float4 per thread as well (quant_row_*: K <= 4 * NT * QMAX,
-// which the plan below guarantees).  GATED: a second matrix Wg (the gate)
+// takes NV float4 per thread (quant_row_*: K <= 4 * NT * NV; NV is the
+// quantiser's depth for K, at most QMAX by the plan below).  GATED: a second
+// matrix Wg (the gate)
 // of the same shape is streamed by the same lanes against the same
 // quantised rows, and the output is ReLU^2(gate) * up (Wp is up).
-template <int MTILES, int NWV, int QMAX, bool F32IN, bool GATED = false>
+template <int MTILES, int NWV, int QMAX, bool F32IN, bool GATED = false, int NV = 1>
 __global__ __launch_bounds__(NWV* kWave) void k_skinny(
     const float* __restrict__ X, const int8_t* __restrict__ Xq, const float* __restrict__ x_scale,
     const int32_t* __restrict__ x_rowsum, int M, int K, int rmsnorm, const float* __restrict__ gain,
@@ -66,10 +67,10 @@ __global__ __launch_bounds__(NWV* kWave) void k_skinny(
     // ---- every load up front, in the order they are needed: the first fp32
     // activation row (and the norm gain), the weights, then the epilogue's
     // operands for this thread's first output.
-    float4 v[F32IN ? QMAX : 1], gv[F32IN ? QMAX : 1];
+    float4 v[F32IN ? NV : 1], gv[F32IN ? NV : 1];
     const bool has_gain = rmsnorm != 0 && gain != nullptr;
     if constexpr (F32IN) {
-        quant_row_load<NT, QMAX>(X, has_gain ? gain : nullptr, K, v, gv);
+        quant_row_load<NT, NV>(X, has_gain ? gain : nullptr, K, v, gv);
         __builtin_amdgcn_sched_barrier(0);  // keep these loads ahead of the weights'
     }
     uint4 w[QMAX];
@@ -117,9 +118,9 @@ __global__ __launch_bounds__(NWV* kWave) void k_skinny(
             if (m == 0 || m < M) {
                 if (m > 0) {
                     __syncthreads();  // the reduction slots are reused
-                    quant_row_load_x<NT, QMAX>(X + (int64_t)m * K, K, v);
+                    quant_row_load_x<NT, NV>(X + (int64_t)m * K, K, v);
                 }
-                const float g = quant_row_finish<NT, QMAX>(v, gv, K, rmsnorm != 0, has_gain, eps, xq + m * K,
+                const float g = quant_row_finish<NT, NV>(v, gv, K, rmsnorm != 0, has_gain, eps, xq + m * K,
                                                            dslot, fslot, fslot2, islot[m]);
                 if (threadIdx.x == 0) gx[m] = g;
             }
@@ -250,7 +251,7 @@ bool plan(int64_t K, Plan& p) {
     return true;
 }
 
-template <int MT, int NWV, int Q, bool F, bool G>
+template <int MT, int NWV, int Q, bool F, bool G, int NV = 1>
 hipError_t go(const float* X, const int8_t* Xq, const float* xs, const int32_t* rs, int64_t M, int64_t K, bool rms,
               const float* gain, float eps, const uint8_t* packed, const float* ws, int64_t N, uint32_t epi,
               const float* aux, float* Y, int32_t* acc_out, const uint8_t* gate, const float* gate_scale,
@@ -258,7 +259,7 @@ hipError_t go(const float* X, const int8_t* Xq, const float* xs, const int32_t* 
     const unsigned blocks = (unsigned)((N + 15) / 16);
     const size_t red = (size_t)NWV * 16 * MT * 16 * sizeof(int) * (G ? 2 : 1);
     const size_t lds = (F ? 4 * (size_t)K : 0) + red;
-    hipLaunchKernelGGL((k_skinny<MT, NWV, Q, F, G>), dim3(blocks), dim3(NWV * kWave), lds, s, X, Xq, xs, rs, (int)M,
+    hipLaunchKernelGGL((k_skinny<MT, NWV, Q, F, G, NV>), dim3(blocks), dim3(NWV * kWave), lds, s, X, Xq, xs, rs, (int)M,
                        (int)K, rms ? 1 : 0, gain, eps, packed, ws, (int)N, epi, aux, Y, acc_out, gate, gate_scale);
     return hipGetLastError();
 }
@@ -268,15 +269,35 @@ hipError_t go_mt(const Plan& p, const float* X, const int8_t* Xq, const float* x
                  int64_t K, bool rms, const float* gain, float eps, const uint8_t* packed, const float* ws,
                  int64_t N, uint32_t epi, const float* aux, float* Y, int32_t* acc_out, hipStream_t s,
                  const uint8_t* gate = nullptr, const float* gate_scale = nullptr) {
-#define BL_SK(NWV, Q)                                                                                     \
-    if (p.nw == NWV && p.qmax == Q)                                                                       \
-        return go<MT, NWV, Q, F, G>(X, Xq, xs, rs, M, K, rms, gain, eps, packed, ws, N, epi, aux, Y, acc_out,  \
+    if constexpr (!F) {
+#define BL_SK(NWV, Q)                                                                                       \
+    if (p.nw == NWV && p.qmax == Q)                                                                         \
+        return go<MT, NWV, Q, F, G>(X, Xq, xs, rs, M, K, rms, gain, eps, packed, ws, N, epi, aux, Y, acc_out,    \
                                     gate, gate_scale, s);
-    BL_SK(4, 2)
-    BL_SK(4, 4)
-    BL_SK(8, 4)
-    BL_SK(8, 8)
+        BL_SK(4, 2)
+        BL_SK(4, 4)
+        BL_SK(8, 4)
+        BL_SK(8, 8)
 #undef BL_SK
+    } else {
+        // fp32 rows: the quantiser's depth for K (which the plan bounds by qmax)
+        const int nv = quant_depth(K);
+#define BL_SKF(NWV, Q, NV)                                                                                  \
+    if (p.nw == NWV && p.qmax == Q && nv == NV)                                                             \
+        return go<MT, NWV, Q, F, G, NV>(X, Xq, xs, rs, M, K, rms, gain, eps, packed, ws, N, epi, aux, Y, acc_out, \
+                                        gate, gate_scale, s);
+        BL_SKF(4, 2, 1)
+        BL_SKF(4, 2, 2)
+        BL_SKF(4, 4, 3)
+        BL_SKF(4, 4, 4)
+        BL_SKF(8, 4, 3)
+        BL_SKF(8, 4, 4)
+        BL_SKF(8, 8, 5)
+        BL_SKF(8, 8, 6)
+        BL_SKF(8, 8, 7)
+        BL_SKF(8, 8, 8)
+#undef BL_SKF
+    }
     return hipErrorInvalidValue;
 }
 
@@ -310,7 +331,7 @@ hipError_t launch_gemv(const int8_t* Xq, const float* xs, const int32_t* rs, int
 bool decode_supported(int64_t M, int64_t K, int64_t N) {
     Plan p;
     if (M < 1 || M > 4 || !gemv_supported(M, K, N) || !plan(K, p) || quant_threads(K) != p.nw * kWave) return false;
-    return K <= (int64_t)4 * p.nw * kWave * p.qmax;  // quant_row_*: qmax float4 per thread
+    return quant_depth(K) <= p.qmax;  // the fp32 row fits the kernel's depth (it always does under plan())
 }
 
 hipError_t launch_decode_bitlinear(const float* X, int64_t M, int64_t K, bool rmsnorm, const float* gain, float eps,
