@@ -228,6 +228,127 @@ def cpu_baseline(budget_s=10.0):
                       f"6912->2560, seed 1) by the single-threaded scalar C oracle, {el:.1f} s"}
 
 
+def bench_batched(torch, bl, synth, dev, log):
+    """Batched decode, M = 8, 32, 64 (seed 2): one layer's BitLinear set --
+    quantise x, o 2560->2560, gate 2560->6912, up 2560->6912 (+ReLU^2, subln
+    RMSNorm and int8 requant), down 6912->2560 -- over rotating packed copies
+    (cold: more than twice the Infinity Cache).  Per kernel and per set."""
+    d = synth.batched_decode()
+    names = ("o", "gate", "up", "down")
+    packed = {}
+    for n in names:
+        W = torch.from_numpy(d[f"W_{n}"]).to(dev)
+        packed[n] = bl.pack_weights(W)
+        del W
+    set_bytes = sum(packed[n][0].numel() for n in names)
+    C = -(-(2 * MALL_BYTES) // set_bytes) + 1
+    copies = [{n: packed[n][0].clone() for n in names} for _ in range(C)]
+    scale = {n: packed[n][1] for n in names}
+    out = []
+    for M in (8, 32, 64):
+        X = torch.from_numpy(d[f"X{M}"]).to(dev)
+        xq, xs, rs = bl.quant_act(X)
+        u0 = bl.forward(xq, xs, copies[0]["up"], scale["up"], x_rowsum=rs, relu2=True, subln=True)
+        yo = torch.empty((M, H), dtype=torch.float32, device=dev)
+        yg = torch.empty((M, F), dtype=torch.float32, device=dev)
+        yu = torch.empty((M, F), dtype=torch.float32, device=dev)
+        yd = torch.empty((M, H), dtype=torch.float32, device=dev)
+
+        def one(n, c):
+            if n == "o":
+                bl.forward(xq, xs, c["o"], scale["o"], x_rowsum=rs, y_out=yo)
+            elif n == "gate":
+                bl.forward(xq, xs, c["gate"], scale["gate"], x_rowsum=rs, y_out=yg)
+            elif n == "up":
+                bl.forward(xq, xs, c["up"], scale["up"], x_rowsum=rs, relu2=True, subln=True, y_out=yu)
+            else:
+                bl.forward(u0["q"], u0["q_scale"], c["down"], scale["down"], x_rowsum=u0["q_rowsum"], y_out=yd)
+
+        per = {}
+        for n in names:
+            t, gg = time_graph(torch, lambda n=n: [one(n, c) for c in copies], reps=3)
+            del gg
+            t /= C
+            nb = copies[0][n].numel()
+            per[n] = {"us": round(t * 1e6, 3), "GB_per_s": round(nb / t / 1e9, 1)}
+
+        def layer_set():
+            for c in copies:
+                a, b, r = bl.quant_act(X)
+                bl.forward(a, b, c["o"], scale["o"], x_rowsum=r, y_out=yo)
+                bl.forward(a, b, c["gate"], scale["gate"], x_rowsum=r, y_out=yg)
+                u = bl.forward(a, b, c["up"], scale["up"], x_rowsum=r, relu2=True, subln=True, y_out=yu)
+                bl.forward(u["q"], u["q_scale"], c["down"], scale["down"], x_rowsum=u["q_rowsum"], y_out=yd)
+
+        t, gg = time_graph(torch, layer_set, reps=3)
+        del gg
+        t /= C
+        ops = 2.0 * M * set_bytes * 4
+        floor = max(set_bytes / (HBM_PEAK_GBS * 1e9), ops / (INT8_PEAK_TOPS * 1e12))
+        rec = {"M": M, "set_us": round(t * 1e6, 3), "set_GB_per_s": round(set_bytes / t / 1e9, 1),
+               "set_TOPS": round(ops / t / 1e12, 2), "roofline_frac": round(floor / t, 4), "kernels": per}
+        out.append(rec)
+        log(f"batched decode M={M}: set {t * 1e6:.2f} us -> {set_bytes / t / 1e9:.0f} GB/s; "
+            + ", ".join(f"{n} {per[n]['us']:.2f} us" for n in names))
+    return {"workload": "batched decode, one layer's BitLinear set (quant, o 2560->2560, gate and up "
+                        "2560->6912, ReLU^2 + subln requant, down 6912->2560), seed 2",
+            "packed_bytes_per_set": int(set_bytes), "weight_copies": C,
+            "roofline": "max(packed bytes / 8 TB/s, int8 ops / 5 POPS) over the measured time", "runs": out}
+
+
+def bench_stack(torch, bl, synth, dev, log, passes=8):
+    """The 30-layer FFN stack (seed 4) with pre-norm and residual, at M=1 and
+    M=32, all layers' packed weights resident; the timed passes rotate over
+    three copies of the stack so each pass reads its weights from HBM."""
+    import numpy as np
+    layers = []
+    rng = None
+    t0 = time.perf_counter()
+    for rng, l, Wu, Wd in synth.ffn_stack_weights():
+        pu, su = bl.pack_weights(torch.from_numpy(Wu).to(dev))
+        pd, sd = bl.pack_weights(torch.from_numpy(Wd).to(dev))
+        layers.append({"up": pu, "up_scale": su, "down": pd, "down_scale": sd})
+    h0 = synth.ffn_stack_hidden(rng)
+    log(f"stack weights generated and packed in {time.perf_counter() - t0:.1f} s")
+    nbytes = sum(L["up"].numel() + L["down"].numel() for L in layers)
+    R = max(2, -(-(2 * MALL_BYTES) // nbytes) + 1)
+    sets = [layers] + [[{k: (v.clone() if k in ("up", "down") else v) for k, v in L.items()} for L in layers]
+                       for _ in range(R - 1)]
+    out = []
+    for M in (1, 32):
+        stacks = [bl.FFNStack(ls, H, F, M, dev) for ls in sets]
+        h = torch.from_numpy(np.ascontiguousarray(h0[:M])).to(dev)
+
+        def run():
+            for i in range(passes):
+                stacks[i % R](h)
+
+        t, gg = time_graph(torch, run, reps=2)
+        del gg
+        t /= passes
+        ops = 2.0 * M * nbytes * 4
+        rec = {"M": M, "us_per_pass": round(t * 1e6, 2), "us_per_layer": round(t * 1e6 / len(layers), 3),
+               "GB_per_s": round(nbytes / t / 1e9, 1), "TOPS": round(ops / t / 1e12, 3),
+               "frac_hbm": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4)}
+        out.append(rec)
+        log(f"stack M={M}: {t * 1e6:.1f} us per 30-layer pass -> {nbytes / t / 1e9:.0f} GB/s")
+        del stacks
+    return {"workload": "30-layer FFN stack (RMSNorm, quant, up 2560->6912, ReLU^2, subln requant, down "
+                        "6912->2560, residual add), seed 4",
+            "layers": len(layers), "packed_bytes_per_pass": int(nbytes), "weight_copies": R,
+            "launch": "HIP graph of the timed passes", "runs": out}
+
+
+def stream_read(torch, dev, log):
+    """Context only: a plain streaming read (torch sum over 1 GiB of fp32)."""
+    buf = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    t, gg = time_graph(torch, lambda: buf.sum(), reps=20)
+    del gg, buf
+    gbs = (1 << 30) / t / 1e9
+    log(f"streaming read (torch.sum, 1 GiB): {gbs:.0f} GB/s")
+    return round(gbs, 1)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -239,6 +360,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-shapes", action="store_true", help="skip the per-shape M=1 decode sweep")
+    ap.add_argument("--no-batched", action="store_true", help="skip the batched decode (M = 8, 32, 64)")
+    ap.add_argument("--no-stack", action="store_true", help="skip the 30-layer stack (M = 1, 32)")
     ap.add_argument("--pmc-drive", action="store_true",
                     help="only run the launches the HBM traffic counters are read from")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -448,6 +571,12 @@ def main():
                                 "down_us_per_launch": round(dn_s * 1e6, 2),
                                 "down_tops": round(tops_dn, 2)}}
 
+    batched = None if args.no_batched else bench_batched(torch, bl, synth, dev, log)
+    torch.cuda.empty_cache()
+    stack = None if args.no_stack else bench_stack(torch, bl, synth, dev, log)
+    torch.cuda.empty_cache()
+    read_gbs = stream_read(torch, dev, log)
+
     cpu = None if args.no_cpu else cpu_baseline(args.cpu_seconds)
     out = {"metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": round(step_s * 1e3, 6), "higher_is_better": True,
@@ -461,7 +590,8 @@ def main():
                       "pack_ms_up_plus_down": round(pack_t * 1e3, 4),
                       "gated_step_us": round(gated_s * 1e6, 3),
                       "gated_step_GB_per_s": round(1.5 * PACKED_BYTES_STEP / gated_s / 1e9, 1)},
-           "roofline": roofline, "cpu_baseline": cpu, "prefill": prefill, "decode_shapes": shapes}
+           "roofline": roofline, "cpu_baseline": cpu, "prefill": prefill, "decode_shapes": shapes,
+           "batched_decode": batched, "stack": stack, "stream_read_GB_per_s": read_gbs}
     print(json.dumps(out), flush=True)
 
 

@@ -36,6 +36,20 @@ __device__ __forceinline__ int buf_load4i(Rsrc r, uint32_t off) {
     return (int)__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
 }
 
+// s_waitcnt on the vector-memory counter only: at most N loads in flight,
+// LDS counter left at its maximum; gfx9 encoding: vmcnt bits [3:0] and
+// [15:14], expcnt [6:4], lgkmcnt [11:8].  Loads complete in issue order, so
+// this also waits for every load issued before the last N.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// LDS destination of a direct buffer->LDS load (the base goes in M0; lane i
+// of the wave writes its 16 bytes at base + 16 i).
+typedef __attribute__((address_space(3))) void* lds_ptr;
+
 // Wave reductions.  Within each row of 16 lanes, four DPP steps pair lane i
 // with i^1, i^2 (quad permutes), 7-i (half mirror) and 15-i (mirror); after
 // the first two steps the four lanes of a quad agree, so each step combines

@@ -40,17 +40,7 @@ constexpr int kXcds = 8;
 //     contiguous 256-byte span.
 // Rows past M or N are clamped to the last row for loading (never stored).
 
-// s_waitcnt on the vector-memory counter only: at most N loads in flight,
-// LDS counter left at its maximum; gfx9 encoding: vmcnt bits [3:0] and
-// [15:14], expcnt [6:4], lgkmcnt [11:8].
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
 constexpr int kBK = 128;             // k per stage
-
-typedef __attribute__((address_space(3))) void* lds_ptr;
 
 // Issue one stage of direct buffer->LDS loads for this wave.  A lane's byte
 // offset is its part inside an 8-row (activations) or 32-row (weights)

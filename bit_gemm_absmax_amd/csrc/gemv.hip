@@ -231,6 +231,223 @@ __global__ __launch_bounds__(NWV* kWave) void k_skinny(
     }
 }
 
+// int8 rows from the standalone quantiser, M <= 64 tokens (batched decode).
+// A workgroup owns 16 * CT output rows (CT column tiles) and all M tokens
+// (MT token tiles of 16).  Its four waves split K in chunk quads (256 k),
+// quad s going to wave s % 4, so a wave has Q or Q - 1 of them; every wave
+// runs the same straight-line body of Q steps, and a missing last quad reads
+// nothing (out-of-range offsets) and adds zeros.  Weights go to registers
+// (every load issued first, as in k_skinny).  Activations are the part that needs
+// care: every workgroup reads all M x K of them from L2, and the MFMA
+// operand layout (lane = token row) makes a direct load touch one cache line
+// per lane, which the address unit serves at about a quarter of its rate.
+// So they travel by direct buffer->LDS loads in whole-line order: one DMA
+// instruction moves 8 rows x 128 bytes, adjacent lanes on adjacent 16-byte
+// chunks, into a ring of NS stages private to the wave (no barrier in the
+// loop); the operand reads then pick the MFMA layout out of LDS.  Inside a
+// DMA block the chunk cc of row r lands at slot cc ^ (r / 2) (r = row of the
+// 16-row tile, 3 bits), which keeps the 16 rows of an operand read on 16
+// distinct bank groups.  Each operand fragment feeds all CT column tiles.
+// A row past M or a chunk past the row end loads zeros or stale bytes: its
+// outputs are dropped, or its weights are zero.
+constexpr int kBatchWaves = 4;
+constexpr int kTileBytes = 16 * 256;  // one token tile x one chunk quad
+
+__device__ __forceinline__ void wait_vm_le(int n) {
+    // n is a constant once the caller's loop is unrolled: one s_waitcnt remains
+#define BL_W(N)          \
+    if (n <= N) {        \
+        wait_vm<N>();    \
+        return;          \
+    }
+    BL_W(0) BL_W(4) BL_W(8) BL_W(12) BL_W(16) BL_W(20) BL_W(24) BL_W(28) BL_W(32) BL_W(36) BL_W(40) BL_W(44) BL_W(48)
+#undef BL_W
+    wait_vm<0>();
+}
+
+template <int MT, int CT, int NS, int Q>
+__device__ __forceinline__ void batch_body(Rsrc ra, const uint32_t (&voff)[MT][2], const Rsrc (&rw)[CT], int wave,
+                                           int fr, int fg, int C, int nq, int8_t* ring, const uint32_t (&rd)[4],
+                                           v4i (&acc)[CT][MT]) {
+    constexpr int SB = MT * kTileBytes;  // bytes per stage
+    uint4 w[CT][Q];
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+        for (int i = 0; i < Q; ++i) {
+            const int c = 4 * (wave + i * kBatchWaves) + fg;
+            w[ct][i] = buf_load16(rw[ct], c < C ? (uint32_t)(fr * C + c) * 16u : kOob);
+        }
+    // quad i (the wave's i-th) -> stage i % NS: per token tile, 4 DMAs of 8 rows x 128 bytes
+#define BL_DMA(ii)                                                                                        \
+    do {                                                                                                  \
+        const int s_ = wave + (ii) * kBatchWaves;                                                         \
+        /* past every row for a missing quad (and no wrap when added to a kOob lane offset) */           \
+        const uint32_t k0 = s_ < nq ? 256u * (uint32_t)s_ : 0x40000000u;                                  \
+        int8_t* st_ = ring + ((ii) % NS) * SB;                                                            \
+        _Pragma("unroll") for (int t = 0; t < MT; ++t)                                                    \
+        _Pragma("unroll") for (int j = 0; j < 4; ++j)                                                     \
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr)(st_ + t * kTileBytes + j * 1024), 16,  \
+                                                     voff[t][j & 1], k0 + 128u * (uint32_t)(j >> 1), 0, 0);     \
+    } while (0)
+#pragma unroll
+    for (int i = 0; i < NS - 1; ++i)
+        if (i < Q) BL_DMA(i);
+#pragma unroll
+    for (int i = 0; i < Q; ++i) {
+        // quad i has landed once no more than the later quads' DMAs are in flight
+        wait_vm_le((Q - 1 - i < NS - 2 ? Q - 1 - i : NS - 2) * MT * 4);
+        __builtin_amdgcn_sched_barrier(0);
+        // all of quad i's operand fragments, then the DMA that refills the
+        // stage read one step earlier (with every read in flight issued
+        // before it, the compiler's own wait for LDS written by DMA is the
+        // one above), then the MFMAs
+        const int8_t* st = ring + (i % NS) * SB;
+        v4i a[4][MT];
+#pragma unroll
+        for (int d = 0; d < 4; ++d)
+#pragma unroll
+            for (int t = 0; t < MT; ++t) a[d][t] = *reinterpret_cast<const v4i*>(st + t * kTileBytes + rd[d]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (i + NS - 1 < Q) BL_DMA(i + NS - 1);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int d = 0; d < 4; ++d)
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) {
+                const uint32_t wd = d == 0 ? w[ct][i].x : d == 1 ? w[ct][i].y : d == 2 ? w[ct][i].z : w[ct][i].w;
+                const v4i b = v4i{codes4(wd, 0), codes4(wd, 1), codes4(wd, 2), codes4(wd, 3)};
+#pragma unroll
+                for (int t = 0; t < MT; ++t) acc[ct][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[d][t], b, acc[ct][t], 0, 0, 0);
+            }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+#undef BL_DMA
+}
+
+template <int MT, int CT, int NS, int QMAX>
+__global__ __launch_bounds__(kBatchWaves* kWave) void k_batch(const int8_t* __restrict__ Xq,
+                                                               const float* __restrict__ x_scale,
+                                                               const int32_t* __restrict__ x_rowsum, int M, int K,
+                                                               const uint8_t* __restrict__ Wp,
+                                                               const float* __restrict__ w_scale, int N,
+                                                               uint32_t epi_flags, const float* aux, float* Y,
+                                                               int32_t* __restrict__ acc_out) {
+    constexpr int NWV = kBatchWaves;
+    constexpr int NT = NWV * kWave;
+    constexpr int COLS = 16 * CT;
+    constexpr int EPT = (16 * MT * COLS + NT - 1) / NT;  // outputs per thread in the epilogue (upper bound)
+    constexpr int RING = NS * MT * kTileBytes;           // bytes per wave
+    static_assert(NWV * 16 * MT * COLS * 4 <= NWV * RING, "partial tiles fit in the rings");
+    __shared__ __align__(1024) int8_t lds[NWV * RING];   // activation rings, then partial tiles [NWV][M][COLS]
+    __shared__ float sxs[16 * MT];
+    __shared__ int srs[16 * MT];
+
+    const int lane = threadIdx.x % kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int fr = lane & 15;  // activation row of the A operand / output column of the tile
+    const int fg = lane >> 4;  // k group
+    const int n0 = blockIdx.x * COLS;
+    const int C = K / 64;
+    const int nq = (C + 3) / 4;
+    const float ws = *w_scale;
+
+    // ---- the epilogue's operands, loaded first: the rows' scales and sums
+    // (thread t < M takes row t) and the residual or multiplier of every
+    // output this thread finishes (output i = threadIdx.x + e * NT).
+    const float p_xs = buf_load4f(make_rsrc(x_scale, (uint32_t)M * 4u), (uint32_t)threadIdx.x * 4u);
+    const int p_rs = buf_load4i(make_rsrc(x_rowsum, (uint32_t)M * 4u), (uint32_t)threadIdx.x * 4u);
+    float e_aux[EPT];
+    {
+        const Rsrc rx = make_rsrc(aux, (epi_flags & (kEpiResidual | kEpiMul)) ? 0x7FFFFFFFu : 0u);
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) {
+            const int i = threadIdx.x + e * NT;
+            const int m = i / COLS, n = n0 + i % COLS;
+            e_aux[e] = buf_load4f(rx, (m < M && n < N) ? (uint32_t)((int64_t)m * N + n) * 4u : kOob);
+        }
+    }
+
+    Rsrc rw[CT];
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+        const int r0 = n0 + 16 * ct;
+        // readfirstlane: a clamp the compiler leaves in a VGPR would make the
+        // descriptor look divergent (and every load a waterfall loop)
+        const int rows = __builtin_amdgcn_readfirstlane(N - r0 < 0 ? 0 : (N - r0 < 16 ? N - r0 : 16));
+        rw[ct] = make_rsrc(Wp + (int64_t)(rows > 0 ? r0 : 0) * (K / 4), (uint32_t)rows * (uint32_t)(K / 4));
+    }
+    // DMA lane offsets: lane L moves row 8h + (L >> 3) of token tile t, 16-byte
+    // chunk (L & 7) ^ (row / 2) of the 128-byte span (h = half of the tile)
+    const Rsrc ra = make_rsrc(Xq, (uint32_t)M * (uint32_t)K);
+    uint32_t voff[MT][2];
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int r = 8 * h + (lane >> 3);
+            const int m = 16 * t + r;
+            voff[t][h] = m < M ? (uint32_t)m * (uint32_t)K + 16u * (uint32_t)((lane & 7) ^ (r >> 1)) : kOob;
+        }
+    // operand reads: row fr, k bytes 64 fg + 16 d of the quad -> DMA block
+    // 2 (fg / 2) + fr / 8, lane 8 (fr % 8) + ((4 (fg % 2) + d) ^ (fr / 2))
+    uint32_t rd[4];
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+        rd[d] = 1024u * (uint32_t)(2 * (fg >> 1) + (fr >> 3)) +
+                16u * (uint32_t)(8 * (fr & 7) + ((4 * (fg & 1) + d) ^ (fr >> 1)));
+    int8_t* ring = lds + wave * RING;
+
+    v4i acc[CT][MT];
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+        for (int t = 0; t < MT; ++t) acc[ct][t] = v4i{0, 0, 0, 0};
+    batch_body<MT, CT, NS, QMAX>(ra, voff, rw, wave, fr, fg, C, nq, ring, rd, acc);
+
+    // ---- per-wave partial tiles -> LDS (over the rings, once every wave is
+    // done with its own) -> sum over the waves in index order
+    if ((int)threadIdx.x < 16 * MT) {
+        sxs[threadIdx.x] = p_xs;
+        srs[threadIdx.x] = p_rs;
+    }
+    __syncthreads();
+    int* red = reinterpret_cast<int*>(lds);
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+        for (int t = 0; t < MT; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int m = 16 * t + 4 * fg + r;
+                if (m < M) red[(wave * M + m) * COLS + 16 * ct + fr] = acc[ct][t][r];
+            }
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+        const int i = threadIdx.x + e * NT;
+        const int m = i / COLS, col = i % COLS;
+        const int n = n0 + col;
+        if (m < M && n < N) {
+            int a = 0;
+#pragma unroll
+            for (int q = 0; q < NWV; ++q) a += red[(q * M + m) * COLS + col];
+            a -= srs[m];
+            const float d = (sxs[m] * ws) / 127.0f;
+            float y = (float)a * d;
+            const int64_t o = (int64_t)m * N + n;
+            if (epi_flags & kEpiRelu2) {
+                const float tt = y > 0.0f ? y : 0.0f;
+                y = tt * tt;
+            }
+            if (epi_flags & kEpiMul) y = y * e_aux[e];
+            else if (epi_flags & kEpiResidual) y = y + e_aux[e];
+            if (Y != nullptr) Y[o] = y;
+            if (acc_out != nullptr) acc_out[o] = a;
+        }
+    }
+}
+
 struct Plan {
     int nw, qmax;
 };
@@ -303,34 +520,68 @@ hipError_t go_mt(const Plan& p, const float* X, const int8_t* Xq, const float* x
 
 }  // namespace
 
+// Batched kernel shape: four waves, up to 8 chunk quads each (K <= 8192;
+// longer rows go to the GEMM); token tiles 1, 2 or 4 (M = 33..48 runs a
+// zero tile) with 4, 3 or 2 ring stages (64, 96 or 128 KB of LDS); two
+// column tiles per workgroup once several token tiles share each operand
+// fragment, while that still leaves >= 128 workgroups.
+static bool batch_shape(int64_t M, int64_t K, int64_t N, int& q, int& mt, int& ct) {
+    const int64_t nq = (K / 64 + 3) / 4;
+    q = (int)((nq + kBatchWaves - 1) / kBatchWaves);
+    mt = M <= 16 ? 1 : M <= 32 ? 2 : 4;
+    ct = (mt >= 2 && (N + 31) / 32 >= 128) ? 2 : 1;
+    return M >= 1 && M <= 64 && K >= 64 && K <= 8192 && q >= 1 && q <= 8;
+}
+
 // Output offsets are taken in 32-bit bytes by the buffer loads: M * N * 4 < 2^31.
 bool gemv_supported(int64_t M, int64_t K, int64_t N) {
-    Plan p;
-    return M >= 1 && M <= 64 && K <= 32768 && M * N < (1LL << 29) && plan(K, p);
+    int q, mt, ct;
+    return M * N < (1LL << 29) && batch_shape(M, K, N, q, mt, ct);
+}
+
+template <int MT, int CT, int Q>
+static hipError_t go_batch(const int8_t* Xq, const float* xs, const int32_t* rs, int64_t M, int64_t K,
+                           const uint8_t* packed, const float* ws, int64_t N, Epi epi, float* Y, int32_t* acc_out,
+                           hipStream_t s) {
+    constexpr int NS = MT == 1 ? 4 : MT == 2 ? 3 : 2;
+    const unsigned blocks = (unsigned)((N + 16 * CT - 1) / (16 * CT));
+    hipLaunchKernelGGL((k_batch<MT, CT, NS, Q>), dim3(blocks), dim3(kBatchWaves * kWave), 0, s, Xq, xs, rs, (int)M,
+                       (int)K, packed, ws, (int)N, epi.flags, epi.aux, Y, acc_out);
+    return hipGetLastError();
+}
+
+template <int MT, int CT>
+static hipError_t go_batch_q(int q, const int8_t* Xq, const float* xs, const int32_t* rs, int64_t M, int64_t K,
+                             const uint8_t* packed, const float* ws, int64_t N, Epi epi, float* Y, int32_t* acc_out,
+                             hipStream_t s) {
+    switch (q) {
+#define BL_BQ(Q) \
+    case Q: return go_batch<MT, CT, Q>(Xq, xs, rs, M, K, packed, ws, N, epi, Y, acc_out, s);
+        BL_BQ(1) BL_BQ(2) BL_BQ(3) BL_BQ(4) BL_BQ(5) BL_BQ(6) BL_BQ(7) BL_BQ(8)
+#undef BL_BQ
+        default: return hipErrorInvalidValue;
+    }
 }
 
 hipError_t launch_gemv(const int8_t* Xq, const float* xs, const int32_t* rs, int64_t M, int64_t K,
                        const uint8_t* packed, const float* ws, int64_t N, Epi epi, float* Y, int32_t* acc_out,
                        hipStream_t s) {
-    Plan p;
-    if (!plan(K, p)) return hipErrorInvalidValue;
-    const int mt = (int)((M + 15) / 16);
-    switch (mt) {
-        case 1: return go_mt<1, false>(p, nullptr, Xq, xs, rs, M, K, false, nullptr, 0.f, packed, ws, N, epi.flags,
-                                       epi.aux, Y, acc_out, s);
-        case 2: return go_mt<2, false>(p, nullptr, Xq, xs, rs, M, K, false, nullptr, 0.f, packed, ws, N, epi.flags,
-                                       epi.aux, Y, acc_out, s);
-        case 3: return go_mt<3, false>(p, nullptr, Xq, xs, rs, M, K, false, nullptr, 0.f, packed, ws, N, epi.flags,
-                                       epi.aux, Y, acc_out, s);
-        case 4: return go_mt<4, false>(p, nullptr, Xq, xs, rs, M, K, false, nullptr, 0.f, packed, ws, N, epi.flags,
-                                       epi.aux, Y, acc_out, s);
+    int q, mt, ct;
+    if (!batch_shape(M, K, N, q, mt, ct)) return hipErrorInvalidValue;
+    switch (mt * 2 + ct - 1) {
+        case 2: return go_batch_q<1, 1>(q, Xq, xs, rs, M, K, packed, ws, N, epi, Y, acc_out, s);
+        case 4: return go_batch_q<2, 1>(q, Xq, xs, rs, M, K, packed, ws, N, epi, Y, acc_out, s);
+        case 5: return go_batch_q<2, 2>(q, Xq, xs, rs, M, K, packed, ws, N, epi, Y, acc_out, s);
+        case 8: return go_batch_q<4, 1>(q, Xq, xs, rs, M, K, packed, ws, N, epi, Y, acc_out, s);
+        case 9: return go_batch_q<4, 2>(q, Xq, xs, rs, M, K, packed, ws, N, epi, Y, acc_out, s);
         default: return hipErrorInvalidValue;
     }
 }
 
 bool decode_supported(int64_t M, int64_t K, int64_t N) {
     Plan p;
-    if (M < 1 || M > 4 || !gemv_supported(M, K, N) || !plan(K, p) || quant_threads(K) != p.nw * kWave) return false;
+    if (M < 1 || M > 4 || K < 64 || M * N >= (1LL << 29) || !plan(K, p) || quant_threads(K) != p.nw * kWave)
+        return false;
     return quant_depth(K) <= p.qmax;  // the fp32 row fits the kernel's depth (it always does under plan())
 }
 
