@@ -253,16 +253,34 @@ __global__ __launch_bounds__(NWV* kWave) void k_skinny(
 constexpr int kBatchWaves = 4;
 constexpr int kTileBytes = 16 * 256;  // one token tile x one chunk quad
 
-__device__ __forceinline__ void wait_vm_le(int n) {
-    // n is a constant once the caller's loop is unrolled: one s_waitcnt remains
-#define BL_W(N)          \
-    if (n <= N) {        \
-        wait_vm<N>();    \
-        return;          \
+// s_waitcnt vmcnt(n) for a count that is a constant once the caller's loop
+// is unrolled (the chain of ifs folds to one instruction); n <= 63.
+template <int N = 63>
+__device__ __forceinline__ void wait_vm_n(int n) {
+    if constexpr (N > 0) {
+        if (n >= N) {
+            wait_vm<N>();
+            return;
+        }
+        wait_vm_n<N - 1>(n);
+    } else {
+        wait_vm<0>();
     }
-    BL_W(0) BL_W(4) BL_W(8) BL_W(12) BL_W(16) BL_W(20) BL_W(24) BL_W(28) BL_W(32) BL_W(36) BL_W(40) BL_W(44) BL_W(48)
-#undef BL_W
-    wait_vm<0>();
+}
+
+// Loads a wave issues after quad i's DMAs and before its wait for quad i,
+// in the issue order of batch_body: (DMAs of quad j, weights of quad j) for
+// j < NS - 1, then the remaining weights; iteration j of the loop then adds
+// the DMAs of quad j + NS - 1.
+constexpr int batch_loads_after(int i, int Q, int NS, int MT, int CT) {
+    const int dma = 4 * MT;
+    if (i <= NS - 2) {
+        const int last_pro = NS - 2 < Q - 1 ? NS - 2 : Q - 1;
+        const int rest = Q - (NS - 1) > 0 ? Q - (NS - 1) : 0;
+        return CT + (last_pro - i) * (dma + CT) + CT * rest + (i < rest ? i : rest) * dma;
+    }
+    const int hi = Q - 1 < i + NS - 2 ? Q - 1 : i + NS - 2;
+    return (hi - i) * dma;
 }
 
 template <int MT, int CT, int NS, int Q>
@@ -271,13 +289,12 @@ __device__ __forceinline__ void batch_body(Rsrc ra, const uint32_t (&voff)[MT][2
                                            v4i (&acc)[CT][MT]) {
     constexpr int SB = MT * kTileBytes;  // bytes per stage
     uint4 w[CT][Q];
-#pragma unroll
-    for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-        for (int i = 0; i < Q; ++i) {
-            const int c = 4 * (wave + i * kBatchWaves) + fg;
-            w[ct][i] = buf_load16(rw[ct], c < C ? (uint32_t)(fr * C + c) * 16u : kOob);
-        }
+#define BL_WT(ii)                                                                                  \
+    do {                                                                                           \
+        const int c_ = 4 * (wave + (ii) * kBatchWaves) + fg;                                       \
+        _Pragma("unroll") for (int ct = 0; ct < CT; ++ct)                                          \
+            w[ct][ii] = buf_load16(rw[ct], c_ < C ? (uint32_t)(fr * C + c_) * 16u : kOob);         \
+    } while (0)
     // quad i (the wave's i-th) -> stage i % NS: per token tile, 4 DMAs of 8 rows x 128 bytes
 #define BL_DMA(ii)                                                                                        \
     do {                                                                                                  \
@@ -290,13 +307,26 @@ __device__ __forceinline__ void batch_body(Rsrc ra, const uint32_t (&voff)[MT][2
             __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr)(st_ + t * kTileBytes + j * 1024), 16,  \
                                                      voff[t][j & 1], k0 + 128u * (uint32_t)(j >> 1), 0, 0);     \
     } while (0)
+    // issue order (pinned: the waits below count loads): each of the first
+    // NS - 1 quads' DMAs then its weights, then the other weights.  Loads
+    // complete in issue order, so the wait for quad i's activations leaves
+    // its weights and every later load in flight (the MFMAs wait for the
+    // weights they use).
 #pragma unroll
     for (int i = 0; i < NS - 1; ++i)
-        if (i < Q) BL_DMA(i);
+        if (i < Q) {
+            BL_DMA(i);
+            __builtin_amdgcn_sched_barrier(0);
+            BL_WT(i);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+    for (int i = NS - 1; i < Q; ++i) BL_WT(i);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < Q; ++i) {
-        // quad i has landed once no more than the later quads' DMAs are in flight
-        wait_vm_le((Q - 1 - i < NS - 2 ? Q - 1 - i : NS - 2) * MT * 4);
+        // quad i's activations have landed once only later loads are in flight
+        wait_vm_n(batch_loads_after(i, Q, NS, MT, CT));
         __builtin_amdgcn_sched_barrier(0);
         // all of quad i's operand fragments, then the DMA that refills the
         // stage read one step earlier (with every read in flight issued
@@ -323,6 +353,7 @@ __device__ __forceinline__ void batch_body(Rsrc ra, const uint32_t (&voff)[MT][2
         __builtin_amdgcn_sched_barrier(0);
     }
 #undef BL_DMA
+#undef BL_WT
 }
 
 template <int MT, int CT, int NS, int QMAX>
@@ -336,11 +367,12 @@ __global__ __launch_bounds__(kBatchWaves* kWave) void k_batch(const int8_t* __re
     constexpr int NWV = kBatchWaves;
     constexpr int NT = NWV * kWave;
     constexpr int COLS = 16 * CT;
-    constexpr int EPT = (16 * MT * COLS + NT - 1) / NT;  // outputs per thread in the epilogue (upper bound)
+    constexpr int GROUPS = 16 * MT * COLS / 4;          // epilogue: 4 adjacent outputs of one row per group
+    constexpr int EPG = (GROUPS + NT - 1) / NT;          // groups per thread
     constexpr int RING = NS * MT * kTileBytes;           // bytes per wave
     static_assert(NWV * 16 * MT * COLS * 4 <= NWV * RING, "partial tiles fit in the rings");
     __shared__ __align__(1024) int8_t lds[NWV * RING];   // activation rings, then partial tiles [NWV][M][COLS]
-    __shared__ float sxs[16 * MT];
+    __shared__ float sdq[16 * MT];  // per-row dequantisation factor (x_scale * w_scale) / 127
     __shared__ int srs[16 * MT];
 
     const int lane = threadIdx.x % kWave;
@@ -354,17 +386,20 @@ __global__ __launch_bounds__(kBatchWaves* kWave) void k_batch(const int8_t* __re
 
     // ---- the epilogue's operands, loaded first: the rows' scales and sums
     // (thread t < M takes row t) and the residual or multiplier of every
-    // output this thread finishes (output i = threadIdx.x + e * NT).
+    // output this thread finishes (group g = threadIdx.x + e * NT covers row
+    // g / (COLS / 4), columns 4 (g % (COLS / 4)) .. + 3 of the tile).
     const float p_xs = buf_load4f(make_rsrc(x_scale, (uint32_t)M * 4u), (uint32_t)threadIdx.x * 4u);
     const int p_rs = buf_load4i(make_rsrc(x_rowsum, (uint32_t)M * 4u), (uint32_t)threadIdx.x * 4u);
-    float e_aux[EPT];
+    float e_aux[EPG][4];
     {
         const Rsrc rx = make_rsrc(aux, (epi_flags & (kEpiResidual | kEpiMul)) ? 0x7FFFFFFFu : 0u);
 #pragma unroll
-        for (int e = 0; e < EPT; ++e) {
-            const int i = threadIdx.x + e * NT;
-            const int m = i / COLS, n = n0 + i % COLS;
-            e_aux[e] = buf_load4f(rx, (m < M && n < N) ? (uint32_t)((int64_t)m * N + n) * 4u : kOob);
+        for (int e = 0; e < EPG; ++e) {
+            const int g = threadIdx.x + e * NT;
+            const int m = g / (COLS / 4), n = n0 + 4 * (g % (COLS / 4));
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                e_aux[e][j] = buf_load4f(rx, (m < M && n + j < N) ? (uint32_t)((int64_t)m * N + n + j) * 4u : kOob);
         }
     }
 
@@ -408,7 +443,7 @@ __global__ __launch_bounds__(kBatchWaves* kWave) void k_batch(const int8_t* __re
     // ---- per-wave partial tiles -> LDS (over the rings, once every wave is
     // done with its own) -> sum over the waves in index order
     if ((int)threadIdx.x < 16 * MT) {
-        sxs[threadIdx.x] = p_xs;
+        sdq[threadIdx.x] = (p_xs * ws) / 127.0f;
         srs[threadIdx.x] = p_rs;
     }
     __syncthreads();
@@ -423,27 +458,59 @@ __global__ __launch_bounds__(kBatchWaves* kWave) void k_batch(const int8_t* __re
                 if (m < M) red[(wave * M + m) * COLS + 16 * ct + fr] = acc[ct][t][r];
             }
     __syncthreads();
+    // all partial-tile reads first (16 bytes: 4 adjacent columns), then the
+    // arithmetic; a group past M reads row M - 1 and stores nothing
+    int4 part[EPG][NWV];
 #pragma unroll
-    for (int e = 0; e < EPT; ++e) {
-        const int i = threadIdx.x + e * NT;
-        const int m = i / COLS, col = i % COLS;
-        const int n = n0 + col;
+    for (int e = 0; e < EPG; ++e) {
+        const int g = threadIdx.x + e * NT;
+        const int m = g / (COLS / 4) < M ? g / (COLS / 4) : M - 1;
+        const int c = 4 * (g % (COLS / 4));
+#pragma unroll
+        for (int q = 0; q < NWV; ++q) part[e][q] = *reinterpret_cast<const int4*>(red + (q * M + m) * COLS + c);
+    }
+    const bool vec = (N & 3) == 0;  // rows start 16-byte aligned
+#pragma unroll
+    for (int e = 0; e < EPG; ++e) {
+        const int g = threadIdx.x + e * NT;
+        const int m = g / (COLS / 4);
+        const int n = n0 + 4 * (g % (COLS / 4));
         if (m < M && n < N) {
-            int a = 0;
+            int a[4] = {0, 0, 0, 0};
 #pragma unroll
-            for (int q = 0; q < NWV; ++q) a += red[(q * M + m) * COLS + col];
-            a -= srs[m];
-            const float d = (sxs[m] * ws) / 127.0f;
-            float y = (float)a * d;
-            const int64_t o = (int64_t)m * N + n;
-            if (epi_flags & kEpiRelu2) {
-                const float tt = y > 0.0f ? y : 0.0f;
-                y = tt * tt;
+            for (int q = 0; q < NWV; ++q) {
+                a[0] += part[e][q].x;
+                a[1] += part[e][q].y;
+                a[2] += part[e][q].z;
+                a[3] += part[e][q].w;
             }
-            if (epi_flags & kEpiMul) y = y * e_aux[e];
-            else if (epi_flags & kEpiResidual) y = y + e_aux[e];
-            if (Y != nullptr) Y[o] = y;
-            if (acc_out != nullptr) acc_out[o] = a;
+            const int rsum = srs[m];
+            const float dq = sdq[m];
+            float y[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                a[j] -= rsum;
+                float v = (float)a[j] * dq;
+                if (epi_flags & kEpiRelu2) {
+                    const float tt = v > 0.0f ? v : 0.0f;
+                    v = tt * tt;
+                }
+                if (epi_flags & kEpiMul) v = v * e_aux[e][j];
+                else if (epi_flags & kEpiResidual) v = v + e_aux[e][j];
+                y[j] = v;
+            }
+            const int64_t o = (int64_t)m * N + n;
+            if (vec) {  // n + 3 < N as well
+                if (Y != nullptr) *reinterpret_cast<float4*>(Y + o) = make_float4(y[0], y[1], y[2], y[3]);
+                if (acc_out != nullptr) *reinterpret_cast<int4*>(acc_out + o) = make_int4(a[0], a[1], a[2], a[3]);
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    if (n + j < N) {
+                        if (Y != nullptr) Y[o + j] = y[j];
+                        if (acc_out != nullptr) acc_out[o + j] = a[j];
+                    }
+            }
         }
     }
 }
