@@ -1,17 +1,16 @@
-// Skinny contraction for decode and batched decode (M <= 64 tokens)
+// Skinny contractions for decode and batched decode (M <= 64 tokens)
 // (transformers "BitNet" page, "Model details" / Quantization: W1.58A8,
 // int8 activations times ternary weights).  The work is a stream of packed
 // weights against a few KB of activations, so it is laid out for memory
 // parallelism and a short tail after the data lands:
 //
-//   - a workgroup owns 16 output rows (one MFMA column tile); its NW waves
-//     split K, and every lane issues all of its 16-byte weight loads before
-//     doing anything else;
+//   - a workgroup owns 16 output rows (one MFMA column tile) or more; its
+//     waves split K, and every lane issues its 16-byte weight loads before
+//     anything that waits;
 //   - the contraction runs on v_mfma_i32_16x16x64_i8 with the token rows as
 //     the 16-row A operand: rows past M are don't-care (their outputs are
-//     dropped), so one instruction serves 1..16 tokens and up to four M
-//     tiles reuse the same weight registers; the MFMA does the k-reduction,
-//     and expanding 16 weights costs one shift + mask per 4;
+//     dropped), so one instruction serves 1..16 tokens; the MFMA does the
+//     k-reduction, and expanding 16 weights costs one shift + mask per 4;
 //   - lane (n, g) holds the whole 64-weight chunk 4s + g of row n (one 16-byte
 //     load) and feeds its four 32-bit words to four MFMAs; the activation
 //     operand of lane (m, g) is the matching 16 bytes of row m, so both
@@ -20,11 +19,10 @@
 //     sums), then the epilogue subtracts the row sum of the code offset,
 //     dequantises and applies ReLU^2 and the residual add or gating product.
 //
-// Two prologues: int8 rows read straight from global memory (L2-resident,
-// shared by all workgroups), or -- for M <= 4 -- fp32 rows that every
-// workgroup quantises itself into LDS (the same quant_row_* as the
-// standalone quantiser, so the same int8 values), which removes the
-// quantiser launch from the decode chain.
+// k_decode (M <= 4) takes fp32 rows that every workgroup quantises itself
+// into LDS (the same quant_row_* as the standalone quantiser, so the same
+// int8 values), which removes the quantiser launch from the decode chain.
+// k_batch (M <= 64) takes the standalone quantiser's int8 rows.
 #include "bl_device.h"
 #include "bl_internal.h"
 
@@ -33,22 +31,21 @@ namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 
-// QMAX 16-byte weight chunks per lane; with fp32 input the activation row
-// takes NV float4 per thread (quant_row_*: K <= 4 * NT * NV; NV is the
-// quantiser's depth for K, at most QMAX by the plan below).  GATED: a second
-// matrix Wg (the gate)
-// of the same shape is streamed by the same lanes against the same
-// quantised rows, and the output is ReLU^2(gate) * up (Wp is up).
-template <int MTILES, int NWV, int QMAX, bool F32IN, bool GATED = false, int NV = 1>
-__global__ __launch_bounds__(NWV* kWave) void k_skinny(
-    const float* __restrict__ X, const int8_t* __restrict__ Xq, const float* __restrict__ x_scale,
-    const int32_t* __restrict__ x_rowsum, int M, int K, int rmsnorm, const float* __restrict__ gain,
-    float eps, const uint8_t* __restrict__ Wp, const float* __restrict__ w_scale, int N, uint32_t epi_flags,
-    const float* aux, float* Y, int32_t* __restrict__ acc_out, const uint8_t* __restrict__ Wg,
-    const float* __restrict__ g_scale) {
+// QMAX 16-byte weight chunks per lane; the fp32 activation row takes NV
+// float4 per thread (quant_row_*: K <= 4 * NT * NV; NV is the quantiser's
+// depth for K, at most QMAX by the plan below).  GATED: a second matrix Wg
+// (the gate) of the same shape is streamed by the same lanes against the
+// same quantised rows, and the output is ReLU^2(gate) * up (Wp is up).
+template <int NWV, int QMAX, bool GATED, int NV>
+__global__ __launch_bounds__(NWV* kWave) void k_decode(const float* __restrict__ X, int M, int K, int rmsnorm,
+                                                        const float* __restrict__ gain, float eps,
+                                                        const uint8_t* __restrict__ Wp,
+                                                        const float* __restrict__ w_scale, int N,
+                                                        uint32_t epi_flags, const float* aux, float* Y,
+                                                        const uint8_t* __restrict__ Wg,
+                                                        const float* __restrict__ g_scale) {
     constexpr int NT = NWV * kWave;
-    constexpr int ROWS = 16 * MTILES;
-    extern __shared__ __align__(16) int8_t lds[];  // [fp32 input: xq, M <= 4 rows of K] [partials]
+    extern __shared__ __align__(16) int8_t lds[];  // [xq: M <= 4 rows of K] [partials]
     __shared__ double dslot[NWV];
     __shared__ float fslot[NWV], fslot2[NWV];
     __shared__ int islot[4][NWV];
@@ -66,13 +63,11 @@ __global__ __launch_bounds__(NWV* kWave) void k_skinny(
 
     // ---- every load up front, in the order they are needed: the first fp32
     // activation row (and the norm gain), the weights, then the epilogue's
-    // operands for this thread's first output.
-    float4 v[F32IN ? NV : 1], gv[F32IN ? NV : 1];
+    // operand for this thread's output.
+    float4 v[NV], gv[NV];
     const bool has_gain = rmsnorm != 0 && gain != nullptr;
-    if constexpr (F32IN) {
-        quant_row_load<NT, NV>(X, has_gain ? gain : nullptr, K, v, gv);
-        __builtin_amdgcn_sched_barrier(0);  // keep these loads ahead of the weights'
-    }
+    quant_row_load<NT, NV>(X, has_gain ? gain : nullptr, K, v, gv);
+    __builtin_amdgcn_sched_barrier(0);  // keep these loads ahead of the weights'
     uint4 w[QMAX];
     {
         const int rows = N - n0 < 16 ? N - n0 : 16;
@@ -95,56 +90,34 @@ __global__ __launch_bounds__(NWV* kWave) void k_skinny(
             wg[i] = buf_load16(rg, (s < nq && c < C) ? (uint32_t)(fr * C + c) * 16u : kOob);
         }
     }
-    const bool e_first = (int)threadIdx.x < M * 16;
     const int e_m = threadIdx.x / 16, e_n = n0 + (int)(threadIdx.x % 16);
-    const bool e_ok = e_first && e_n < N;
+    const bool e_ok = (int)threadIdx.x < M * 16 && e_n < N;
     const float e_res = buf_load4f(make_rsrc(aux, (epi_flags & (kEpiResidual | kEpiMul)) ? 0x7FFFFFFFu : 0u),
                                    e_ok ? (uint32_t)((int64_t)e_m * N + e_n) * 4u : kOob);
-    float e_xs = 0.0f;
-    int e_rs = 0;
-    if constexpr (!F32IN) {
-        e_xs = buf_load4f(make_rsrc(x_scale, (uint32_t)M * 4u), e_first ? (uint32_t)e_m * 4u : kOob);
-        e_rs = buf_load4i(make_rsrc(x_rowsum, (uint32_t)M * 4u), e_first ? (uint32_t)e_m * 4u : kOob);
-    }
 
-    // ---- activation rows: quantised here (fp32 input) or read as int8
-    const int8_t* arow[MTILES];
-    if constexpr (F32IN) {
-        int8_t* xq = lds;
-        // Row 0 unconditionally (the host launches with M >= 1): a guard
-        // would let the compiler sink its loads behind the weights'.
+    // ---- activation rows, quantised here.  Row 0 unconditionally (the host
+    // launches with M >= 1): a guard would let the compiler sink its loads
+    // behind the weights'.
+    int8_t* xq = lds;
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            if (m == 0 || m < M) {
-                if (m > 0) {
-                    __syncthreads();  // the reduction slots are reused
-                    quant_row_load_x<NT, NV>(X + (int64_t)m * K, K, v);
-                }
-                const float g = quant_row_finish<NT, NV>(v, gv, K, rmsnorm != 0, has_gain, eps, xq + m * K,
-                                                           dslot, fslot, fslot2, islot[m]);
-                if (threadIdx.x == 0) gx[m] = g;
+    for (int m = 0; m < 4; ++m) {
+        if (m == 0 || m < M) {
+            if (m > 0) {
+                __syncthreads();  // the reduction slots are reused
+                quant_row_load_x<NT, NV>(X + (int64_t)m * K, K, v);
             }
-        }
-        __syncthreads();
-        arow[0] = xq + (fr < M ? fr : M - 1) * K;
-    } else {
-#pragma unroll
-        for (int t = 0; t < MTILES; ++t) {
-            const int m = 16 * t + fr;
-            arow[t] = Xq + (int64_t)(m < M ? m : M - 1) * K;
+            const float g = quant_row_finish<NT, NV>(v, gv, K, rmsnorm != 0, has_gain, eps, xq + m * K, dslot,
+                                                       fslot, fslot2, islot[m]);
+            if (threadIdx.x == 0) gx[m] = g;
         }
     }
+    __syncthreads();
+    const int8_t* arow = xq + (fr < M ? fr : M - 1) * K;
 
     // ---- contraction.  A chunk past the row end has zero weights (its load
     // was out of range), so its activation offset is clamped to 0 and it adds
     // nothing.
-    v4i acc[MTILES], accg[GATED ? MTILES : 1];
-#pragma unroll
-    for (int t = 0; t < MTILES; ++t) acc[t] = v4i{0, 0, 0, 0};
-    if constexpr (GATED) {
-#pragma unroll
-        for (int t = 0; t < MTILES; ++t) accg[t] = v4i{0, 0, 0, 0};
-    }
+    v4i acc = v4i{0, 0, 0, 0}, accg = v4i{0, 0, 0, 0};
 #pragma unroll
     for (int i = 0; i < QMAX; ++i) {
         const int s = wave + i * NWV;
@@ -155,15 +128,12 @@ __global__ __launch_bounds__(NWV* kWave) void k_skinny(
 #pragma unroll
             for (int d = 0; d < 4; ++d) {
                 const v4i b = v4i{codes4(wd[d], 0), codes4(wd[d], 1), codes4(wd[d], 2), codes4(wd[d], 3)};
-#pragma unroll
-                for (int t = 0; t < MTILES; ++t) {
-                    const v4i a = *reinterpret_cast<const v4i*>(arow[t] + koff + 16 * d);
-                    acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, acc[t], 0, 0, 0);
-                    if constexpr (GATED) {
-                        const uint32_t g4 = d == 0 ? wg[i].x : d == 1 ? wg[i].y : d == 2 ? wg[i].z : wg[i].w;
-                        const v4i bg = v4i{codes4(g4, 0), codes4(g4, 1), codes4(g4, 2), codes4(g4, 3)};
-                        accg[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, bg, accg[t], 0, 0, 0);
-                    }
+                const v4i a = *reinterpret_cast<const v4i*>(arow + koff + 16 * d);
+                acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, acc, 0, 0, 0);
+                if constexpr (GATED) {
+                    const uint32_t g4 = d == 0 ? wg[i].x : d == 1 ? wg[i].y : d == 2 ? wg[i].z : wg[i].w;
+                    const v4i bg = v4i{codes4(g4, 0), codes4(g4, 1), codes4(g4, 2), codes4(g4, 3)};
+                    accg = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, bg, accg, 0, 0, 0);
                 }
             }
         }
@@ -171,63 +141,49 @@ __global__ __launch_bounds__(NWV* kWave) void k_skinny(
 
     // ---- per-wave partial tiles -> LDS (a region of its own) -> epilogue,
     // summing the waves in index order
-    int* red = reinterpret_cast<int*>(lds + (F32IN ? 4 * K : 0));  // [NWV][ROWS][16], gate after it
-    int* redg = red + NWV * ROWS * 16;
+    int* red = reinterpret_cast<int*>(lds + 4 * K);  // [NWV][16 tokens][16], gate after it
+    int* redg = red + NWV * 16 * 16;
 #pragma unroll
-    for (int t = 0; t < MTILES; ++t)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int m = 16 * t + 4 * fg + r;
-            if (m < M) {
-                red[(wave * ROWS + m) * 16 + fr] = acc[t][r];
-                if constexpr (GATED) redg[(wave * ROWS + m) * 16 + fr] = accg[t][r];
-            }
+    for (int r = 0; r < 4; ++r) {
+        const int m = 4 * fg + r;
+        if (m < M) {
+            red[(wave * 16 + m) * 16 + fr] = acc[r];
+            if constexpr (GATED) redg[(wave * 16 + m) * 16 + fr] = accg[r];
         }
+    }
     __syncthreads();
-    for (int i = threadIdx.x; i < M * 16; i += NT) {
-        const int m = i / 16, col = i % 16;
-        const int n = n0 + col;
-        if (n < N) {
-            const bool first = i == (int)threadIdx.x;
-            int a = 0, ag = 0;
+    if (e_ok) {
+        const int m = e_m, col = (int)threadIdx.x % 16;
+        int a = 0, ag = 0;
 #pragma unroll
-            for (int q = 0; q < NWV; ++q) a += red[(q * ROWS + m) * 16 + col];
-            if constexpr (GATED) {
+        for (int q = 0; q < NWV; ++q) a += red[(q * 16 + m) * 16 + col];
+        if constexpr (GATED) {
 #pragma unroll
-                for (int q = 0; q < NWV; ++q) ag += redg[(q * ROWS + m) * 16 + col];
-            }
-            float xs;
-            int rs;
-            if constexpr (F32IN) {
-                rs = 0;
-#pragma unroll
-                for (int q = 0; q < NWV; ++q) rs += islot[m][q];
-                xs = gx[m];
-            } else {
-                rs = first ? e_rs : x_rowsum[m];
-                xs = first ? e_xs : x_scale[m];
-            }
-            a -= rs;
-            const float d = (xs * ws) / 127.0f;
-            float y = (float)a * d;
-            const int64_t o = (int64_t)m * N + n;
-            if constexpr (GATED) {
-                // ReLU^2(gate) * up, in that order
-                ag -= rs;
-                float t = (float)ag * ((xs * gws) / 127.0f);
-                t = t > 0.0f ? t : 0.0f;
-                y = (t * t) * y;
-            } else {
-                if (epi_flags & kEpiRelu2) {
-                    const float tt = y > 0.0f ? y : 0.0f;
-                    y = tt * tt;
-                }
-                if (epi_flags & kEpiMul) y = y * (first ? e_res : aux[o]);
-                else if (epi_flags & kEpiResidual) y = y + (first ? e_res : aux[o]);
-            }
-            if (Y != nullptr) Y[o] = y;
-            if (acc_out != nullptr) acc_out[o] = a;
+            for (int q = 0; q < NWV; ++q) ag += redg[(q * 16 + m) * 16 + col];
         }
+        int rs = 0;
+#pragma unroll
+        for (int q = 0; q < NWV; ++q) rs += islot[m][q];
+        const float xs = gx[m];
+        a -= rs;
+        const float d = (xs * ws) / 127.0f;
+        float y = (float)a * d;
+        const int64_t o = (int64_t)m * N + e_n;
+        if constexpr (GATED) {
+            // ReLU^2(gate) * up, in that order
+            ag -= rs;
+            float t = (float)ag * ((xs * gws) / 127.0f);
+            t = t > 0.0f ? t : 0.0f;
+            y = (t * t) * y;
+        } else {
+            if (epi_flags & kEpiRelu2) {
+                const float tt = y > 0.0f ? y : 0.0f;
+                y = tt * tt;
+            }
+            if (epi_flags & kEpiMul) y = y * e_res;
+            else if (epi_flags & kEpiResidual) y = y + e_res;
+        }
+        Y[o] = y;
     }
 }
 
@@ -237,7 +193,7 @@ __global__ __launch_bounds__(NWV* kWave) void k_skinny(
 // quad s going to wave s % 4, so a wave has Q or Q - 1 of them; every wave
 // runs the same straight-line body of Q steps, and a missing last quad reads
 // nothing (out-of-range offsets) and adds zeros.  Weights go to registers
-// (every load issued first, as in k_skinny).  Activations are the part that needs
+// (every load issued first, as in k_decode).  Activations are the part that needs
 // care: every workgroup reads all M x K of them from L2, and the MFMA
 // operand layout (lane = token row) makes a direct load touch one cache line
 // per lane, which the address unit serves at about a quarter of its rate.
@@ -535,53 +491,39 @@ bool plan(int64_t K, Plan& p) {
     return true;
 }
 
-template <int MT, int NWV, int Q, bool F, bool G, int NV = 1>
-hipError_t go(const float* X, const int8_t* Xq, const float* xs, const int32_t* rs, int64_t M, int64_t K, bool rms,
-              const float* gain, float eps, const uint8_t* packed, const float* ws, int64_t N, uint32_t epi,
-              const float* aux, float* Y, int32_t* acc_out, const uint8_t* gate, const float* gate_scale,
-              hipStream_t s) {
+template <int NWV, int Q, bool G, int NV>
+hipError_t go_decode(const float* X, int64_t M, int64_t K, bool rms, const float* gain, float eps,
+                     const uint8_t* packed, const float* ws, int64_t N, uint32_t epi, const float* aux, float* Y,
+                     const uint8_t* gate, const float* gate_scale, hipStream_t s) {
     const unsigned blocks = (unsigned)((N + 15) / 16);
-    const size_t red = (size_t)NWV * 16 * MT * 16 * sizeof(int) * (G ? 2 : 1);
-    const size_t lds = (F ? 4 * (size_t)K : 0) + red;
-    hipLaunchKernelGGL((k_skinny<MT, NWV, Q, F, G, NV>), dim3(blocks), dim3(NWV * kWave), lds, s, X, Xq, xs, rs, (int)M,
-                       (int)K, rms ? 1 : 0, gain, eps, packed, ws, (int)N, epi, aux, Y, acc_out, gate, gate_scale);
+    const size_t red = (size_t)NWV * 16 * 16 * sizeof(int) * (G ? 2 : 1);
+    const size_t lds = 4 * (size_t)K + red;
+    hipLaunchKernelGGL((k_decode<NWV, Q, G, NV>), dim3(blocks), dim3(NWV * kWave), lds, s, X, (int)M, (int)K,
+                       rms ? 1 : 0, gain, eps, packed, ws, (int)N, epi, aux, Y, gate, gate_scale);
     return hipGetLastError();
 }
 
-template <int MT, bool F, bool G = false>
-hipError_t go_mt(const Plan& p, const float* X, const int8_t* Xq, const float* xs, const int32_t* rs, int64_t M,
-                 int64_t K, bool rms, const float* gain, float eps, const uint8_t* packed, const float* ws,
-                 int64_t N, uint32_t epi, const float* aux, float* Y, int32_t* acc_out, hipStream_t s,
-                 const uint8_t* gate = nullptr, const float* gate_scale = nullptr) {
-    if constexpr (!F) {
-#define BL_SK(NWV, Q)                                                                                       \
-    if (p.nw == NWV && p.qmax == Q)                                                                         \
-        return go<MT, NWV, Q, F, G>(X, Xq, xs, rs, M, K, rms, gain, eps, packed, ws, N, epi, aux, Y, acc_out,    \
-                                    gate, gate_scale, s);
-        BL_SK(4, 2)
-        BL_SK(4, 4)
-        BL_SK(8, 4)
-        BL_SK(8, 8)
-#undef BL_SK
-    } else {
-        // fp32 rows: the quantiser's depth for K (which the plan bounds by qmax)
-        const int nv = quant_depth(K);
-#define BL_SKF(NWV, Q, NV)                                                                                  \
-    if (p.nw == NWV && p.qmax == Q && nv == NV)                                                             \
-        return go<MT, NWV, Q, F, G, NV>(X, Xq, xs, rs, M, K, rms, gain, eps, packed, ws, N, epi, aux, Y, acc_out, \
-                                        gate, gate_scale, s);
-        BL_SKF(4, 2, 1)
-        BL_SKF(4, 2, 2)
-        BL_SKF(4, 4, 3)
-        BL_SKF(4, 4, 4)
-        BL_SKF(8, 4, 3)
-        BL_SKF(8, 4, 4)
-        BL_SKF(8, 8, 5)
-        BL_SKF(8, 8, 6)
-        BL_SKF(8, 8, 7)
-        BL_SKF(8, 8, 8)
-#undef BL_SKF
-    }
+// The quantiser's depth for K (which the plan bounds by qmax) picks NV.
+template <bool G>
+hipError_t go_decode_plan(const Plan& p, const float* X, int64_t M, int64_t K, bool rms, const float* gain,
+                          float eps, const uint8_t* packed, const float* ws, int64_t N, uint32_t epi,
+                          const float* aux, float* Y, hipStream_t s, const uint8_t* gate = nullptr,
+                          const float* gate_scale = nullptr) {
+    const int nv = quant_depth(K);
+#define BL_DEC(NWV, Q, NV)                                                                                 \
+    if (p.nw == NWV && p.qmax == Q && nv == NV)                                                            \
+        return go_decode<NWV, Q, G, NV>(X, M, K, rms, gain, eps, packed, ws, N, epi, aux, Y, gate, gate_scale, s);
+    BL_DEC(4, 2, 1)
+    BL_DEC(4, 2, 2)
+    BL_DEC(4, 4, 3)
+    BL_DEC(4, 4, 4)
+    BL_DEC(8, 4, 3)
+    BL_DEC(8, 4, 4)
+    BL_DEC(8, 8, 5)
+    BL_DEC(8, 8, 6)
+    BL_DEC(8, 8, 7)
+    BL_DEC(8, 8, 8)
+#undef BL_DEC
     return hipErrorInvalidValue;
 }
 
@@ -657,8 +599,7 @@ hipError_t launch_decode_bitlinear(const float* X, int64_t M, int64_t K, bool rm
                                    const float* aux, float* Y, hipStream_t s) {
     Plan p;
     if (!plan(K, p)) return hipErrorInvalidValue;
-    return go_mt<1, true>(p, X, nullptr, nullptr, nullptr, M, K, rmsnorm, gain, eps, packed, w_scale, N, epi,
-                          aux, Y, nullptr, s);
+    return go_decode_plan<false>(p, X, M, K, rmsnorm, gain, eps, packed, w_scale, N, epi, aux, Y, s);
 }
 
 hipError_t launch_decode_gated(const float* X, int64_t M, int64_t K, bool rmsnorm, const float* gain, float eps,
@@ -666,8 +607,8 @@ hipError_t launch_decode_gated(const float* X, int64_t M, int64_t K, bool rmsnor
                                const float* gate_scale, int64_t N, float* Y, hipStream_t s) {
     Plan p;
     if (!plan(K, p)) return hipErrorInvalidValue;
-    return go_mt<1, true, true>(p, X, nullptr, nullptr, nullptr, M, K, rmsnorm, gain, eps, up, up_scale, N, 0u,
-                                nullptr, Y, nullptr, s, gate, gate_scale);
+    return go_decode_plan<true>(p, X, M, K, rmsnorm, gain, eps, up, up_scale, N, 0u, nullptr, Y, s, gate,
+                                gate_scale);
 }
 
 }  // namespace bl
