@@ -68,6 +68,8 @@ TRAFFIC_KERNELS = {
     "decode_up_m1": ("k_decode<4, 4, false, 3>", 432, ("gemv.hip", "bl_device.h")),
     "gemm_up_m4096": ("k_gemm_pipe<256, 256, 2, 4, 4, 1>", 432, ("gemm.hip", "bl_device.h")),
     "gemm_down_m4096": ("k_gemm_pipe<256, 160, 4, 2, 4, 1>", 256, ("gemm.hip", "bl_device.h")),
+    "batch_gate_m64": ("k_batch<4, 2, 2, 3>", 216, ("gemv.hip", "bl_device.h")),
+    "batch_down_m64": ("k_batch<4, 1, 2, 7>", 160, ("gemv.hip", "bl_device.h")),
 }
 CALIB_BYTES = 256 << 20   # the calibration kernel reads and writes 256 MiB
 PMC_CMDS = [
@@ -81,7 +83,9 @@ def pmc_drive():
     """The launches the traffic counters are read from: the decode up kernel
     over 16 weight copies (more than the per-XCD L2 holds), a plain
     elementwise pass over 256 MiB (x -> -x: reads and writes 256 MiB, the
-    counters' calibration), and the two prefill GEMMs."""
+    counters' calibration), the two prefill GEMMs, and the batched decode
+    gate and down BitLinears at M=64 over 8 weight copies each."""
+    import numpy as np
     import torch
 
     from bit_gemm_absmax_amd import bitlinear as bl
@@ -113,6 +117,24 @@ def pmc_drive():
     for _ in range(3):
         bl.forward(xq, xs, pu4, su4, x_rowsum=rs, relu2=True, y_out=yu)
         bl.forward(up["q"], up["q_scale"], pd4, sd4, x_rowsum=up["q_rowsum"], y_out=yd)
+    torch.cuda.synchronize()
+    del X, xq, up, yu, yd
+    b = synth.batched_decode()
+    pg, sg = bl.pack_weights(torch.from_numpy(b["W_gate"]).to(dev))
+    pdb, sdb = bl.pack_weights(torch.from_numpy(b["W_down"]).to(dev))
+    gates = [pg.clone() for _ in range(8)]
+    downs = [pdb.clone() for _ in range(8)]
+    x64 = torch.from_numpy(b["X64"]).to(dev)
+    q64, s64, r64 = bl.quant_act(x64)
+    h64 = torch.from_numpy(synth.activations(np.random.default_rng(7), 64, F)).to(dev)
+    q2, s2, r2 = bl.quant_act(h64)
+    yg = torch.empty((64, F), dtype=torch.float32, device=dev)
+    yb = torch.empty((64, H), dtype=torch.float32, device=dev)
+    for _ in range(3):
+        for w in gates:
+            bl.forward(q64, s64, w, sg, x_rowsum=r64, y_out=yg)
+        for w in downs:
+            bl.forward(q2, s2, w, sdb, x_rowsum=r2, y_out=yb)
     torch.cuda.synchronize()
     log("pmc-drive done")
 
