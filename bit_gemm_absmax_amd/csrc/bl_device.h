@@ -278,13 +278,15 @@ __device__ __forceinline__ float quant_row_finish(float4 (&v)[NV], const float4 
         uint32_t packed = 0;
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
-            float t = rintf(e[b] * s);
-            t = t > 127.0f ? 127.0f : t;
-            t = t < -127.0f ? -127.0f : t;
-            const int qi = (int)t;
-            sum += qi;  // slots past the row hold 0 and add 0
-            packed |= ((uint32_t)qi & 0xFFu) << (8 * b);
+            // q = clamp(rint(x * s), -127, 127) (med3 is the clamp), stored as
+            // the byte of q + 128 in 1..255 (an exact float, converted and
+            // inserted in one instruction); flipping bit 7 below turns the
+            // biased byte into the two's-complement int8 q
+            const float t = __builtin_amdgcn_fmed3f(rintf(e[b] * s), -127.0f, 127.0f);
+            packed = __builtin_amdgcn_cvt_pk_u8_f32(t + 128.0f, b, packed);
         }
+        packed ^= 0x80808080u;
+        sum = __builtin_amdgcn_sdot4((int)packed, 0x01010101, sum, false);  // slots past the row hold 0
         if (idx < n4) q4[idx] = (int)packed;
     }
     if (rs_slot != nullptr) {
