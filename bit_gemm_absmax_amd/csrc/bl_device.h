@@ -226,13 +226,15 @@ __device__ __forceinline__ float quant_row_finish(float4 (&v)[NV], const float4 
     }
     float g;
     if (rmsnorm) {
+        // x * x of a binary32 x is exact in binary64, so the fused multiply-add
+        // rounds once, exactly as the separate add of the product would
         double ss = 0.0;
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
-            ss += (double)v[i].x * (double)v[i].x;
-            ss += (double)v[i].y * (double)v[i].y;
-            ss += (double)v[i].z * (double)v[i].z;
-            ss += (double)v[i].w * (double)v[i].w;
+            ss = __builtin_fma((double)v[i].x, (double)v[i].x, ss);
+            ss = __builtin_fma((double)v[i].y, (double)v[i].y, ss);
+            ss = __builtin_fma((double)v[i].z, (double)v[i].z, ss);
+            ss = __builtin_fma((double)v[i].w, (double)v[i].w, ss);
         }
         block_sum_max<NW>(ss, amax, dslot, fslot);
         const float r = (float)(1.0 / sqrt(ss / (double)K + (double)eps));

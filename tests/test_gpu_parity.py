@@ -124,6 +124,40 @@ def test_forward_small(M, K, N):
     assert_y_close(host(out["y"]), ref["y"])
 
 
+@pytest.mark.parametrize("M", [24, 48, 64])
+@pytest.mark.parametrize("K,N,epi", [(1536, 4100, "residual"), (3584, 4098, "mul"), (5120, 200, "none"),
+                                     (6016, 96, "residual"), (8192, 64, "none")])
+def test_forward_batched_shapes(M, K, N, epi):
+    """The batched-decode kernel (int8 rows, 17 <= M <= 64) at every chunk-quad
+    count per wave from 2 to 8 (K = 1536 .. 8192), two column tiles per
+    workgroup with N not a multiple of 32 (and, at N = 4098, rows that are not
+    16-byte aligned: the element-wise epilogue), and the residual or gating
+    epilogue operand; accumulators and outputs element by element."""
+    log(f"[batched] M={M} K={K} N={N} epi={epi}")
+    rng = np.random.default_rng(M * 7 + K + N)
+    X = synth.activations(rng, M, K, outliers=True)
+    W = synth.weights(rng, N, K)
+    aux = rng.standard_normal((M, N)).astype(np.float32)
+    p, s, q, g = check_pack(W, "batched")
+    xq, xs, rs = bl.quant_act(dev(X))
+    kw = {}
+    if epi == "residual":
+        kw = {"residual": dev(aux)}
+    elif epi == "mul":
+        kw = {"mul_by": dev(aux)}
+    out = bl.forward(xq, xs, p, s, x_rowsum=rs, relu2=True, want_acc=True, **kw)
+    rq = oracle.quant_act(X)
+    assert_exact(host(xq), rq[0], "xq")
+    acc = oracle.int_matmul(rq[0], q)
+    assert_exact(host(out["acc"]), acc, "acc")
+    y = oracle.relu2(oracle.dequant(acc, rq[1], g))
+    if epi == "residual":
+        y = oracle.add(aux, y)
+    elif epi == "mul":
+        y = oracle.mul(y, aux)
+    assert_y_close(host(out["y"]), y, "y")
+
+
 def test_forward_rowsum_computed_inside():
     rng = np.random.default_rng(11)
     X = synth.activations(rng, 6, 512)
