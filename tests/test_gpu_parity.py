@@ -246,7 +246,7 @@ def test_quant_forward(M, K, N, rms, gain, relu2, res):
 
 
 def test_gemv_row_equals_gemm_row():
-    """Token independence across kernels: M=1 (skinny decode kernel) equals
+    """Token independence across kernels: M=1 (batched kernel, one token tile) equals
     row 0 of M=80 (tiled GEMM)."""
     rng = np.random.default_rng(21)
     X = synth.activations(rng, 80, 2560, outliers=True)
@@ -373,7 +373,7 @@ def test_ffn_no_prenorm_no_residual():
 @pytest.mark.parametrize("K,N", [(256, 512), (320, 130)])
 def test_forward_mul_epilogue(M, K, N):
     """y = ReLU^2(dequant(acc)) * aux, written in place over aux, through the
-    skinny (M <= 64) and GEMM paths; the fused quantise + forward (M <= 4
+    batched (M <= 64) and GEMM paths; the fused quantise + forward (M <= 4
     one launch) gives the same values."""
     log(f"[mul epilogue] M={M} K={K} N={N}")
     rng = np.random.default_rng(M * 13 + K + N)
@@ -565,7 +565,7 @@ def test_attention_projections():
     """The attention block's BitLinear shapes (q, o 2560->2560; k, v
     2560->640; 2560->3840) at M = 1, 5, 130, through bitlinear_forward and,
     for M <= 4, the fused quantise + forward; every element against the
-    oracle (M = 130 runs the GEMM, M <= 64 the skinny kernel)."""
+    oracle (M = 130 runs the GEMM, M <= 64 the batched kernel)."""
     d = synth.attention_projections()
     for name in ("q", "k", "v", "o", "qkv"):
         W = d[f"W_{name}"]
