@@ -143,7 +143,11 @@ def _workspace(nbytes: int, device) -> Optional[torch.Tensor]:
 
 
 def pack_weights(W: torch.Tensor):
-    """Absmean-ternarise and pack fp32 W [N][K] -> (packed u8 [N][K/4], w_scale f32 [1])."""
+    """Absmean-ternarise and pack fp32 W [N][K] -> (packed u8 [N][K/4], w_scale f32 [1]).
+
+    The packed bytes are grouped by 16-row tiles, not by row (layout in
+    include/bitlinear.h): pass the tensor whole; slicing its rows does not give
+    the packed form of a row subset."""
     lib = load()
     _need(W, torch.float32, 2, "W")
     N, K = W.shape

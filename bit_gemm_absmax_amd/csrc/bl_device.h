@@ -50,6 +50,14 @@ __device__ __forceinline__ void wait_vm() {
 // of the wave writes its 16 bytes at base + 16 i).
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
+// One 16-byte-per-lane direct buffer->LDS load.  A plain (non-template)
+// function, so the builtin's operands are never template-dependent: clang's
+// host pass, which checks them against the host target's limits (sizes 1, 2
+// or 4), would otherwise drop the calling template as a substitution failure.
+__device__ __forceinline__ void dma16(Rsrc r, lds_ptr dst, uint32_t voff, uint32_t soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, soff, 0, 0);
+}
+
 // Wave reductions.  Within each row of 16 lanes, four DPP steps pair lane i
 // with i^1, i^2 (quad permutes), 7-i (half mirror) and 15-i (mirror); after
 // the first two steps the four lanes of a quad agree, so each step combines

@@ -37,34 +37,37 @@ constexpr int kXcds = 8;
 //     so the 16 rows of an MFMA fragment read at one k hit distinct banks;
 //   - weights: one instruction covers 32 rows x both 16-byte chunks of the
 //     stage, chunk-major, so a fragment read (word g of 16 rows) is one
-//     contiguous 256-byte span.
+//     contiguous 256-byte span; in the packed layout (16-row tiles, chunk c
+//     of a tile's rows side by side) that is four 256-byte runs in memory.
 // Rows past M or N are clamped to the last row for loading (never stored).
 
 constexpr int kBK = 128;             // k per stage
 
 // Issue one stage of direct buffer->LDS loads for this wave.  A lane's byte
 // offset is its part inside an 8-row (activations) or 32-row (weights)
-// block, va / vb, fixed for the whole loop; the block's row offset, the tile
-// origin and the stage's k are wave-uniform and go in the scalar offset.
+// block: va fixed for the whole loop; for weights vb[i] + st * vs[i], since
+// a stage's chunks advance by 32 bytes per row of the lane's weight tile
+// (the last tile of a matrix may have fewer than 16 rows).  The block's row
+// offset, the tile origin and (activations) the stage's k are wave-uniform
+// and go in the scalar offset.
 // Reads past the tensor return zero (the descriptor's size), so no row or
 // k clamp is needed: rows past M or N are never stored, and when
 // K % 128 == 64 the second half of the last stage is never read.
 //   activations: A_BLKS instructions, block j = rows 8j..8j+7 of the tile;
 //   weights: B_INS instructions, each 32 rows x both 64-k chunks.
 template <int A_BLKS, int B_INS>
-__device__ __forceinline__ void issue_stage(Rsrc ra, Rsrc rb, uint32_t va, uint32_t vb, uint32_t a_s, uint32_t b_s,
+__device__ __forceinline__ void issue_stage(Rsrc ra, Rsrc rb, uint32_t va, const uint32_t (&vb)[B_INS],
+                                            const uint32_t (&vs)[B_INS], int st, uint32_t a_s, uint32_t b_s,
                                             uint32_t a_blk, uint32_t b_blk, int8_t* base, int a_stage, int wave) {
 #pragma unroll
     for (int i = 0; i < A_BLKS; ++i) {
         const int j = wave * A_BLKS + i;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr)(base + j * 1024), 16, va, a_s + (uint32_t)j * a_blk,
-                                                 0, 0);
+        dma16(ra, (lds_ptr)(base + j * 1024), va, a_s + (uint32_t)j * a_blk);
     }
 #pragma unroll
     for (int i = 0; i < B_INS; ++i) {
         const int j = wave * B_INS + i;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr)(base + a_stage + j * 1024), 16, vb,
-                                                 b_s + (uint32_t)j * b_blk, 0, 0);
+        dma16(rb, (lds_ptr)(base + a_stage + j * 1024), vb[i] + (uint32_t)st * vs[i], b_s + (uint32_t)j * b_blk);
     }
 }
 
@@ -109,20 +112,29 @@ __global__ __launch_bounds__(WM* WN* kWave, OCC) void k_gemm_pipe(
     // 16-byte chunk c ^ r8, stored at slot c of that row in LDS (so the 16
     // rows an MFMA fragment reads at one k sit in distinct banks).  Weights:
     // lane l of a block fetches row l%32, chunk l/32 of the stage
-    // (chunk-major in LDS).
+    // (chunk-major in LDS); in memory that row is row l%16 of weight tile
+    // h = (l%32)/16 of the block, whose chunk c sits at 16 (c R + l%16).
     const Rsrc ra = make_rsrc(Xq, (uint32_t)M * (uint32_t)K);
     const Rsrc rb = make_rsrc(Wp, (uint32_t)N * (uint32_t)C * 16u);
     const uint32_t va = (uint32_t)(lane >> 3) * (uint32_t)K + (uint32_t)((lane & 7) ^ (lane >> 3)) * 16u;
-    const uint32_t vb = (uint32_t)(lane & 31) * (uint32_t)C * 16u + (uint32_t)(lane >> 5) * 16u;
+    uint32_t vb[B_INS], vs[B_INS];
+#pragma unroll
+    for (int i = 0; i < B_INS; ++i) {
+        const int h = (lane & 31) >> 4;
+        const int r0 = n0 + 32 * (wave * B_INS + i) + 16 * h;  // first row of the lane's weight tile
+        const int R = N - r0 < 16 ? N - r0 : 16;               // its rows (<= 0: past the matrix)
+        vb[i] = R > 0 ? (uint32_t)h * 16u * (uint32_t)K / 4u + 16u * (uint32_t)((lane >> 5) * R + (lane & 15)) : kOob;
+        vs[i] = R > 0 ? 32u * (uint32_t)R : 0u;
+    }
     const uint32_t a_blk = 8u * (uint32_t)K, b_blk = 32u * (uint32_t)C * 16u;
     const uint32_t a_base = (uint32_t)m0 * (uint32_t)K, b_base = (uint32_t)n0 * (uint32_t)C * 16u;
     // A stage index past the last one gets a scalar offset past every
     // descriptor: its loads write zeros to LDS without touching memory, so
     // the issue is branch-free (those buffers are never read).
 #define BL_ISSUE(st)                                                                                          \
-    issue_stage<A_BLKS, B_INS>(ra, rb, va, vb, (st) < nst ? a_base + (uint32_t)(st) * kBK : kOob,              \
-                               (st) < nst ? b_base + (uint32_t)(st) * 32u : kOob, a_blk, b_blk,                \
-                               smem + ((st) % NBUF) * STAGE, A_STAGE, wave)
+    issue_stage<A_BLKS, B_INS>(ra, rb, va, vb, vs, (st), (st) < nst ? a_base + (uint32_t)(st) * kBK : kOob,    \
+                               (st) < nst ? b_base : kOob, a_blk, b_blk, smem + ((st) % NBUF) * STAGE,       \
+                               A_STAGE, wave)
 
     v4i acc[FM][FN];
 #pragma unroll
@@ -170,16 +182,15 @@ __global__ __launch_bounds__(WM* WN* kWave, OCC) void k_gemm_pipe(
     // stage, as in issue_stage.
     auto issue_one = [&](int st, int i) {
         const uint32_t as = st < nst ? a_base + (uint32_t)st * kBK : kOob;
-        const uint32_t bs = st < nst ? b_base + (uint32_t)st * 32u : kOob;
+        const uint32_t bs = st < nst ? b_base : kOob;
         int8_t* base = smem + (st % NBUF) * STAGE;
         if (i < A_BLKS) {
             const int j = wave * A_BLKS + i;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr)(base + j * 1024), 16, va,
-                                                     as + (uint32_t)j * a_blk, 0, 0);
+            dma16(ra, (lds_ptr)(base + j * 1024), va, as + (uint32_t)j * a_blk);
         } else {
             const int j = wave * B_INS + (i - A_BLKS);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr)(base + A_STAGE + j * 1024), 16, vb,
-                                                     bs + (uint32_t)j * b_blk, 0, 0);
+            dma16(rb, (lds_ptr)(base + A_STAGE + j * 1024), vb[i - A_BLKS] + (uint32_t)st * vs[i - A_BLKS],
+                  bs + (uint32_t)j * b_blk);
         }
     };
     auto interleave = [&](bool dma) {

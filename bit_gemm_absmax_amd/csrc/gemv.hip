@@ -12,7 +12,10 @@
 //     dropped), so one instruction serves 1..16 tokens; the MFMA does the
 //     k-reduction, and expanding 16 weights costs one shift + mask per 4;
 //   - lane (n, g) holds the whole 64-weight chunk 4s + g of row n (one 16-byte
-//     load) and feeds its four 32-bit words to four MFMAs; the activation
+//     load) and feeds its four 32-bit words to four MFMAs; the packed layout
+//     puts chunk c of a 16-row tile's rows side by side (byte 16 (c R + n) of
+//     the tile, R its row count), so the 16 adjacent lanes of a load read 256
+//     contiguous bytes; the activation
 //     operand of lane (m, g) is the matching 16 bytes of row m, so both
 //     operands follow the same permutation of k and the sum is unchanged;
 //   - per-wave partial tiles meet in LDS in a fixed wave order (exact integer
@@ -76,7 +79,7 @@ __global__ __launch_bounds__(NWV* kWave) void k_decode(const float* __restrict__
         for (int i = 0; i < QMAX; ++i) {
             const int s = wave + i * NWV;
             const int c = 4 * s + fg;
-            w[i] = buf_load16(rw, (s < nq && c < C) ? (uint32_t)(fr * C + c) * 16u : kOob);
+            w[i] = buf_load16(rw, (s < nq && c < C) ? (uint32_t)(c * rows + fr) * 16u : kOob);
         }
     }
     uint4 wg[GATED ? QMAX : 1];
@@ -87,7 +90,7 @@ __global__ __launch_bounds__(NWV* kWave) void k_decode(const float* __restrict__
         for (int i = 0; i < QMAX; ++i) {
             const int s = wave + i * NWV;
             const int c = 4 * s + fg;
-            wg[i] = buf_load16(rg, (s < nq && c < C) ? (uint32_t)(fr * C + c) * 16u : kOob);
+            wg[i] = buf_load16(rg, (s < nq && c < C) ? (uint32_t)(c * rows + fr) * 16u : kOob);
         }
     }
     const int e_m = threadIdx.x / 16, e_n = n0 + (int)(threadIdx.x % 16);
@@ -240,16 +243,16 @@ constexpr int batch_loads_after(int i, int Q, int NS, int MT, int CT) {
 }
 
 template <int MT, int CT, int NS, int Q>
-__device__ __forceinline__ void batch_body(Rsrc ra, const uint32_t (&voff)[MT][2], const Rsrc (&rw)[CT], int wave,
-                                           int fr, int fg, int C, int nq, int8_t* ring, const uint32_t (&rd)[4],
-                                           v4i (&acc)[CT][MT]) {
+__device__ __forceinline__ void batch_body(Rsrc ra, const uint32_t (&voff)[MT][2], const Rsrc (&rw)[CT],
+                                           const int (&rows)[CT], int wave, int fr, int fg, int C, int nq,
+                                           int8_t* ring, const uint32_t (&rd)[4], v4i (&acc)[CT][MT]) {
     constexpr int SB = MT * kTileBytes;  // bytes per stage
     uint4 w[CT][Q];
 #define BL_WT(ii)                                                                                  \
     do {                                                                                           \
         const int c_ = 4 * (wave + (ii) * kBatchWaves) + fg;                                       \
         _Pragma("unroll") for (int ct = 0; ct < CT; ++ct)                                          \
-            w[ct][ii] = buf_load16(rw[ct], c_ < C ? (uint32_t)(fr * C + c_) * 16u : kOob);         \
+            w[ct][ii] = buf_load16(rw[ct], c_ < C ? (uint32_t)(c_ * rows[ct] + fr) * 16u : kOob);  \
     } while (0)
     // quad i (the wave's i-th) -> stage i % NS: per token tile, 4 DMAs of 8 rows x 128 bytes
 #define BL_DMA(ii)                                                                                        \
@@ -260,8 +263,7 @@ __device__ __forceinline__ void batch_body(Rsrc ra, const uint32_t (&voff)[MT][2
         int8_t* st_ = ring + ((ii) % NS) * SB;                                                            \
         _Pragma("unroll") for (int t = 0; t < MT; ++t)                                                    \
         _Pragma("unroll") for (int j = 0; j < 4; ++j)                                                     \
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr)(st_ + t * kTileBytes + j * 1024), 16,  \
-                                                     voff[t][j & 1], k0 + 128u * (uint32_t)(j >> 1), 0, 0);     \
+            dma16(ra, (lds_ptr)(st_ + t * kTileBytes + j * 1024), voff[t][j & 1], k0 + 128u * (uint32_t)(j >> 1)); \
     } while (0)
     // issue order (pinned: the waits below count loads): each of the first
     // NS - 1 quads' DMAs then its weights, then the other weights.  Loads
@@ -360,13 +362,14 @@ __global__ __launch_bounds__(kBatchWaves* kWave) void k_batch(const int8_t* __re
     }
 
     Rsrc rw[CT];
+    int rows[CT];  // rows of each column tile's 16-row weight tile (the last may have fewer)
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) {
         const int r0 = n0 + 16 * ct;
         // readfirstlane: a clamp the compiler leaves in a VGPR would make the
         // descriptor look divergent (and every load a waterfall loop)
-        const int rows = __builtin_amdgcn_readfirstlane(N - r0 < 0 ? 0 : (N - r0 < 16 ? N - r0 : 16));
-        rw[ct] = make_rsrc(Wp + (int64_t)(rows > 0 ? r0 : 0) * (K / 4), (uint32_t)rows * (uint32_t)(K / 4));
+        rows[ct] = __builtin_amdgcn_readfirstlane(N - r0 < 0 ? 0 : (N - r0 < 16 ? N - r0 : 16));
+        rw[ct] = make_rsrc(Wp + (int64_t)(rows[ct] > 0 ? r0 : 0) * (K / 4), (uint32_t)rows[ct] * (uint32_t)(K / 4));
     }
     // DMA lane offsets: lane L moves row 8h + (L >> 3) of token tile t, 16-byte
     // chunk (L & 7) ^ (row / 2) of the 128-byte span (h = half of the tile)
@@ -394,7 +397,7 @@ __global__ __launch_bounds__(kBatchWaves* kWave) void k_batch(const int8_t* __re
     for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
         for (int t = 0; t < MT; ++t) acc[ct][t] = v4i{0, 0, 0, 0};
-    batch_body<MT, CT, NS, QMAX>(ra, voff, rw, wave, fr, fg, C, nq, ring, rd, acc);
+    batch_body<MT, CT, NS, QMAX>(ra, voff, rw, rows, wave, fr, fg, C, nq, ring, rd, acc);
 
     // ---- per-wave partial tiles -> LDS (over the rings, once every wave is
     // done with its own) -> sum over the waves in index order

@@ -9,7 +9,11 @@
 //   2. k_ternary_pack: every block re-reduces the partials in the same fixed
 //      order (a few KB from L2, identical result in every block), forms
 //      gamma_w = max((float)(sum / (N*K)), 1e-5), and turns each group of 16
-//      weights into one 32-bit word of 2-bit codes.
+//      weights into one 32-bit word of 2-bit codes, stored at its place in
+//      the packed layout: rows in tiles of 16 (the last tile has the rows
+//      left), each tile chunk-major, so 16 rows' 16-byte chunks c sit side by
+//      side and a wave's weight loads (one row per adjacent lane) read whole
+//      lines.
 // The partial count depends only on N*K, so the binary64 summation order,
 // and hence gamma_w, is the same on every run.
 #include "bl_device.h"
@@ -48,7 +52,7 @@ __device__ __forceinline__ uint32_t ternary_code(float w, float gamma) {
 }
 
 __global__ __launch_bounds__(kThreads) void k_ternary_pack(const float4* __restrict__ W,
-                                                           int64_t nwords,
+                                                           int64_t nwords, int64_t N, int64_t K,
                                                            const double* __restrict__ partial,
                                                            int nparts, double count,
                                                            uint32_t* __restrict__ packed,
@@ -75,7 +79,14 @@ __global__ __launch_bounds__(kThreads) void k_ternary_pack(const float4* __restr
             word |= ternary_code(v[j].z, gamma) << (16 + 2 * j);
             word |= ternary_code(v[j].w, gamma) << (24 + 2 * j);
         }
-        packed[w] = word;
+        // word w is group g of row n: chunk c = g / 4, word d = g % 4 of it;
+        // tile t = n / 16 (R rows) starts at word t * K, chunk c of tile row
+        // r at word 4 (c R + r)
+        const int64_t gpr = K / 16;
+        const int64_t n = w / gpr, g = w % gpr;
+        const int64_t t = n / 16;
+        const int64_t R = N - 16 * t < 16 ? N - 16 * t : 16;
+        packed[t * K + 4 * ((g / 4) * R + (n % 16)) + (g % 4)] = word;
     }
 }
 
@@ -99,7 +110,7 @@ hipError_t launch_pack(const float* W, int64_t N, int64_t K, uint8_t* packed,
     int64_t blocks = (nwords + kThreads - 1) / kThreads;
     if (blocks > 8192) blocks = 8192;
     hipLaunchKernelGGL(k_ternary_pack, dim3((unsigned)blocks), dim3(kThreads), 0, s,
-                       reinterpret_cast<const float4*>(W), nwords, partial, g,
+                       reinterpret_cast<const float4*>(W), nwords, N, K, partial, g,
                        (double)count, reinterpret_cast<uint32_t*>(packed), w_scale);
     return hipGetLastError();
 }

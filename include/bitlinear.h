@@ -19,12 +19,21 @@
  * call allocates device memory.  Scratch comes from a caller-supplied
  * workspace whose size the matching *_workspace_bytes() query returns.
  *
- * Layouts.  Row-major, no padding:
+ * Layouts.  No padding; all row-major except the packed weights:
  *   W       fp32 [N][K]     latent weights, out x in (y = x . W^T)
- *   packed  u8   [N][K/4]   2-bit codes c = q + 1; inside a row, weights come
- *                           in groups of 16 forming one little-endian 32-bit
- *                           word; weight k = 16g + 4j + b is stored in byte
- *                           4g + b at bits 2j..2j+1.  Code 3 never occurs.
+ *   packed  u8   N*K/4      2-bit codes c = q + 1 (code 3 never occurs),
+ *                           stored as [N][K/4] bytes but grouped by tiles
+ *                           of 16 rows, not by row.  A row's weights come in
+ *                           16-byte chunks of 64: chunk c holds weights
+ *                           64c .. 64c+63, weight 64c + 16d + 4j + b (d, j,
+ *                           b in 0..3) in byte 4d + b at bits 2j..2j+1, so
+ *                           the chunk's little-endian 32-bit word d holds 16
+ *                           consecutive weights.  Tile t holds rows 16t ..
+ *                           16t+R-1 (R = 16, or N - 16t for the last tile)
+ *                           and starts at byte 16t * K/4; inside it, chunk c
+ *                           of tile row r is at byte 16 (c R + r).  A
+ *                           matrix whose N is a multiple of 16 is therefore
+ *                           the concatenation of its tiles' layouts.
  *   X       fp32 [M][K]     activations, one row per token
  *   Xq      int8 [M][K]     quantised activations, in [-127, 127]
  *   Y       fp32 [M][N]     outputs

@@ -113,12 +113,13 @@ def quantize_weights(W):
 
 
 def pack(q) -> np.ndarray:
-    """2-bit encoding of ternary q [N][K] -> uint8 [N][K/4] (layout in oracle.h)."""
+    """2-bit encoding of ternary q [N][K] -> N*K/4 bytes, shaped [N][K/4] (the
+    bytes are grouped by 16-row tiles, not by row: layout in oracle.h)."""
     q = _c(q, np.int8)
     N, K = q.shape
     out = np.empty((N, K // 4), np.uint8)
     if _load().orc_pack(_p(q), N, K, _p(out)) != 0:
-        raise ValueError("pack: K must be a multiple of 16 and q ternary")
+        raise ValueError("pack: K must be a multiple of 64 and q ternary")
     return out
 
 

@@ -41,31 +41,37 @@ void orc_ternarize(const float* W, int64_t N, int64_t K, float gamma, int8_t* q)
     }
 }
 
-/* Position of weight k inside its row: byte 4*(k/16) + k%4, bit 2*((k/4)%4). */
-static int64_t packed_byte(int64_t k) { return 4 * (k / 16) + (k % 4); }
+/* Byte holding weight (n, k) and the bit offset of its code (layout in
+ * oracle.h): rows in tiles of 16 (the last tile has R = N - 16t rows); in a
+ * tile, the 16-byte chunk c = k / 64 of tile row r sits at 16 (c R + r);
+ * inside a chunk, weight 16d + 4j + b sits in byte 4d + b at bit 2j. */
+static int64_t packed_offset(int64_t n, int64_t k, int64_t N, int64_t K) {
+    const int64_t t = n / 16, r = n % 16;
+    const int64_t R = N - 16 * t < 16 ? N - 16 * t : 16;
+    const int64_t c = k / 64, kk = k % 64;
+    return 16 * t * (K / 4) + 16 * (c * R + r) + 4 * (kk / 16) + (kk % 4);
+}
 static int packed_shift(int64_t k) { return (int)(2 * ((k / 4) % 4)); }
 
 int orc_pack(const int8_t* q, int64_t N, int64_t K, uint8_t* packed) {
-    if (K % 16 != 0) return -1;
-    const int64_t row_bytes = K / 4;
-    memset(packed, 0, (size_t)(N * row_bytes));
+    if (K % 64 != 0) return -1;
+    memset(packed, 0, (size_t)(N * (K / 4)));
     for (int64_t n = 0; n < N; ++n) {
         for (int64_t k = 0; k < K; ++k) {
             int v = q[n * K + k];
             if (v < -1 || v > 1) return -1;
             unsigned code = (unsigned)(v + 1);
-            packed[n * row_bytes + packed_byte(k)] |= (uint8_t)(code << packed_shift(k));
+            packed[packed_offset(n, k, N, K)] |= (uint8_t)(code << packed_shift(k));
         }
     }
     return 0;
 }
 
 int orc_unpack(const uint8_t* packed, int64_t N, int64_t K, int8_t* q) {
-    if (K % 16 != 0) return -1;
-    const int64_t row_bytes = K / 4;
+    if (K % 64 != 0) return -1;
     for (int64_t n = 0; n < N; ++n) {
         for (int64_t k = 0; k < K; ++k) {
-            unsigned code = (packed[n * row_bytes + packed_byte(k)] >> packed_shift(k)) & 3u;
+            unsigned code = (packed[packed_offset(n, k, N, K)] >> packed_shift(k)) & 3u;
             if (code == 3u) return -1;
             q[n * K + k] = (int8_t)((int)code - 1);
         }

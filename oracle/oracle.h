@@ -23,10 +23,14 @@
  *
  * Packed weight format (the page names "packed 1.58-bit weights" in section
  * "Model variants" but gives no layout; this is the reading used here):
- *   code = q + 1 in {0, 1, 2}, two bits per weight, row-major [N][K/4] bytes.
- *   Within a row, weights come in groups of 16 (one little-endian 32-bit
- *   word, bytes 4g..4g+3).  Weight k = 16g + 4j + b (j, b in 0..3) sits in
- *   byte 4g + b at bits 2j..2j+1.  K must be a multiple of 16.
+ *   code = q + 1 in {0, 1, 2}, two bits per weight, N*K/4 bytes, no padding.
+ *   A row's weights come in chunks of 64 (16 bytes); chunk c holds weights
+ *   64c .. 64c+63, and weight 64c + 16d + 4j + b (d, j, b in 0..3) sits in
+ *   byte 4d + b of the chunk at bits 2j..2j+1 (so the chunk's 32-bit word d
+ *   holds 16 consecutive weights).  Rows are grouped in tiles of 16: tile t
+ *   holds rows 16t .. 16t+R-1 (R = 16, or N - 16t for the last tile) and
+ *   starts at byte 16t * K/4; inside it, chunk c of tile row r is at byte
+ *   16 (c R + r).  K must be a multiple of 64.
  */
 #ifndef BITNET_ORACLE_H
 #define BITNET_ORACLE_H
@@ -46,7 +50,7 @@ float orc_absmean_scale(const float* W, int64_t N, int64_t K);
 void orc_ternarize(const float* W, int64_t N, int64_t K, float gamma, int8_t* q);
 
 /* 2-bit encoding of ternary q (layout above).  Returns 0, or -1 when K is not
- * a multiple of 16 or a value lies outside {-1, 0, 1}. */
+ * a multiple of 64 or a value lies outside {-1, 0, 1}. */
 int orc_pack(const int8_t* q, int64_t N, int64_t K, uint8_t* packed);
 
 /* Inverse of orc_pack.  Returns 0, or -1 on a bad K or on code 3. */

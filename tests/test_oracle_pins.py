@@ -40,18 +40,33 @@ def test_hand_bitlinear(golden):
 
 
 def test_hand_pack(golden):
-    g = golden("hand_pack_2x16.json")
+    g = golden("hand_pack_2x128.json")
     q = np.array(g["q"], np.int8)
     want = np.array(g["packed"], np.uint8)
     np.testing.assert_array_equal(oracle.pack(q), want)
-    np.testing.assert_array_equal(oracle.unpack(want, 16), q)
+    np.testing.assert_array_equal(oracle.unpack(want, 128), q)
     # the word view: (w >> 2j) & 0x03030303 yields the codes of k = 4j..4j+3
-    w = int.from_bytes(bytes(want[0]), "little")
+    # (the first word of row 0's first chunk: bytes 0..3)
+    w = int.from_bytes(bytes(want[0][:4]), "little")
     codes = []
     for j in range(4):
         v = (w >> (2 * j)) & 0x03030303
         codes += [(v >> (8 * b)) & 0xFF for b in range(4)]
-    assert codes == [int(c) + 1 for c in g["q"][0]]
+    assert codes == [int(c) + 1 for c in g["q"][0][:16]]
+
+
+def test_hand_pack_full_tile():
+    """One +1 weight among -1s (codes 0, zero bytes) in a 32 x 128 matrix:
+    row 17 is row r = 1 of tile t = 1 (R = 16 rows), k = 70 is chunk c = 1,
+    in-chunk weight 6 = 16*0 + 4*1 + 2 (d = 0, j = 1, b = 2).  The tile starts
+    at 16 * 1 * 128/4 = 512, the chunk at 512 + 16 * (1*16 + 1) = 784, the byte
+    at 784 + 4*0 + 2 = 786, holding code 2 at bits 2..3: 8."""
+    q = np.full((32, 128), -1, np.int8)
+    q[17, 70] = 1
+    p = oracle.pack(q).reshape(-1)
+    want = np.zeros(32 * 128 // 4, np.uint8)
+    want[786] = 8
+    np.testing.assert_array_equal(p, want)
 
 
 def test_hand_ties(golden):
@@ -179,12 +194,12 @@ def test_code_offset_identity():
     np.testing.assert_array_equal(oracle.int_matmul(xq, q), lhs)
 
 
-@pytest.mark.parametrize("K", [16, 64, 2560])
-def test_pack_roundtrip_and_no_code3(K):
-    rng = np.random.default_rng(K)
-    q = rng.integers(-1, 2, (7, K)).astype(np.int8)
+@pytest.mark.parametrize("N,K", [(7, 64), (7, 2560), (16, 128), (37, 192)])
+def test_pack_roundtrip_and_no_code3(N, K):
+    rng = np.random.default_rng(K + N)
+    q = rng.integers(-1, 2, (N, K)).astype(np.int8)
     p = oracle.pack(q)
-    assert p.shape == (7, K // 4)
+    assert p.shape == (N, K // 4)
     np.testing.assert_array_equal(oracle.unpack(p, K), q)
     bits = np.unpackbits(p, bitorder="little").reshape(-1, 2)
     assert not np.any((bits[:, 0] == 1) & (bits[:, 1] == 1))
@@ -192,11 +207,11 @@ def test_pack_roundtrip_and_no_code3(K):
 
 def test_pack_rejects_bad_input():
     with pytest.raises(ValueError):
-        oracle.pack(np.zeros((1, 8), np.int8))
+        oracle.pack(np.zeros((1, 32), np.int8))
     with pytest.raises(ValueError):
-        oracle.pack(np.full((1, 16), 2, np.int8))
+        oracle.pack(np.full((1, 64), 2, np.int8))
     with pytest.raises(ValueError):
-        oracle.unpack(np.full((1, 4), 0xFF, np.uint8), 16)
+        oracle.unpack(np.full((1, 16), 0xFF, np.uint8), 64)
 
 
 # ---------------------------------------------------------------- invariants (P6, P7, P14)
