@@ -389,14 +389,68 @@ def tall_decode(torch, bl, d, pu, su, dev, log):
             "weights": "seed-1 up matrix repeated 19x along N; 7 copies rotated"}
 
 
+def bench_latent(torch, bl, synth, dev, log):
+    """Context: BitLinear from latent weights (ternarised inside the call, the
+    training-time forward) at the up shape K=2560, N=6912, fp32 and bf16
+    weights, M = 1 and 4096, rotating copies that exceed twice the Infinity
+    Cache.  The packer reads the latent matrix twice (absmean, then
+    ternarise + pack); GB/s counts one read of the latent bytes."""
+    import numpy as np
+    rng = np.random.default_rng(7)
+    W = torch.from_numpy(synth.weights(rng, F, H)).to(dev)
+    out = []
+    for dtype, name in ((torch.float32, "f32"), (torch.bfloat16, "bf16")):
+        Wd = W.to(dtype)
+        nb = Wd.numel() * Wd.element_size()
+        copies = [Wd] + [Wd.clone() for _ in range(max(1, -(-(2 * MALL_BYTES) // nb)) - 1)]
+        for M in (1, 4096):
+            X = torch.from_numpy(synth.activations(rng, M, H)).to(dev)
+            y = torch.empty((M, F), dtype=torch.float32, device=dev)
+
+            def run():
+                for c in copies:
+                    bl.latent_forward(X, c, relu2=True, y_out=y)
+
+            t, gg = time_graph(torch, run, reps=3)
+            del gg
+            t /= len(copies)
+            log(f"latent forward {name} M={M}: {t * 1e6:.1f} us ({nb / t / 1e9:.0f} GB/s of latent weights)")
+            out.append({"dtype": name, "M": M, "us": round(t * 1e6, 2), "latent_bytes": nb,
+                        "GB_per_s": round(nb / t / 1e9, 1), "copies": len(copies)})
+        del copies, Wd
+        torch.cuda.empty_cache()
+    return {"workload": "BitLinear from latent weights, K=2560, N=6912, +ReLU^2 (seed 7)", "runs": out}
+
+
 def stream_read(torch, dev, log):
-    """Context only: a plain streaming read (torch sum over 1 GiB of fp32)."""
-    buf = torch.ones(1 << 28, dtype=torch.float32, device=dev)
-    t, gg = time_graph(torch, lambda: buf.sum(), reps=20)
-    del gg, buf
-    gbs = (1 << 30) / t / 1e9
-    log(f"streaming read (torch.sum, 1 GiB): {gbs:.0f} GB/s")
-    return round(gbs, 1)
+    """Context only: the read-bandwidth reference.  A plain streaming read of
+    1 GiB (libblbench.so: 16-byte non-temporal loads, 8192 workgroups, every
+    byte read once), and torch's sum over the same bytes for comparison."""
+    import ctypes
+    from bit_gemm_absmax_amd import build as blbuild
+    if not os.path.exists(blbuild.BENCH_LIB):
+        raise RuntimeError(f"{blbuild.BENCH_LIB} is not built (python -m bit_gemm_absmax_amd.build)")
+    lib = ctypes.CDLL(blbuild.BENCH_LIB)
+    lib.blbench_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_void_p]
+    lib.blbench_stream_read.restype = ctypes.c_int
+    nbytes = 1 << 30
+    buf = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    sink = torch.zeros(1024, dtype=torch.int32, device=dev)
+
+    def run():
+        rc = lib.blbench_stream_read(ctypes.c_void_p(buf.data_ptr()), nbytes, ctypes.c_void_p(sink.data_ptr()),
+                                     ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"blbench_stream_read returned {rc}")
+
+    t, gg = time_graph(torch, run, reps=20)
+    del gg
+    ts, gg = time_graph(torch, lambda: buf.sum(), reps=20)
+    del gg, buf, sink
+    gbs, gbs_sum = nbytes / t / 1e9, nbytes / ts / 1e9
+    log(f"streaming read, 1 GiB: {gbs:.0f} GB/s (nt-load read kernel); torch.sum {gbs_sum:.0f} GB/s")
+    return {"GB_per_s": round(gbs, 1), "torch_sum_GB_per_s": round(gbs_sum, 1),
+            "kernel": "k_stream_read: 8192 x 256 threads, 8 x 16-byte nt loads in flight per thread"}
 
 
 def main():
@@ -412,6 +466,7 @@ def main():
     ap.add_argument("--no-shapes", action="store_true", help="skip the per-shape M=1 decode sweep")
     ap.add_argument("--no-batched", action="store_true", help="skip the batched decode (M = 8, 32, 64)")
     ap.add_argument("--no-stack", action="store_true", help="skip the 30-layer stack (M = 1, 32)")
+    ap.add_argument("--no-latent", action="store_true", help="skip the latent-weight forward (M = 1, 4096)")
     ap.add_argument("--pmc-drive", action="store_true",
                     help="only run the launches the HBM traffic counters are read from")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -625,7 +680,11 @@ def main():
     torch.cuda.empty_cache()
     stack = None if args.no_stack else bench_stack(torch, bl, synth, dev, log)
     torch.cuda.empty_cache()
-    read_gbs = stream_read(torch, dev, log)
+    latent = None if args.no_latent else bench_latent(torch, bl, synth, dev, log)
+    torch.cuda.empty_cache()
+    read = stream_read(torch, dev, log)
+    roofline["read_peak_measured_GB_per_s"] = read["GB_per_s"]
+    roofline["frac_of_read_peak"] = round(roofline["achieved"] / read["GB_per_s"], 4)
     tall = tall_decode(torch, bl, d, pu, su, dev, log)
 
     cpu = None if args.no_cpu else cpu_baseline(args.cpu_seconds)
@@ -642,7 +701,7 @@ def main():
                       "gated_step_us": round(gated_s * 1e6, 3),
                       "gated_step_GB_per_s": round(1.5 * PACKED_BYTES_STEP / gated_s / 1e9, 1)},
            "roofline": roofline, "cpu_baseline": cpu, "prefill": prefill, "decode_shapes": shapes,
-           "batched_decode": batched, "stack": stack, "stream_read_GB_per_s": read_gbs,
+           "batched_decode": batched, "stack": stack, "latent_forward": latent, "stream_read": read,
            "decode_tall": tall}
     print(json.dumps(out), flush=True)
 

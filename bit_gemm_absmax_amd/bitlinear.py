@@ -31,6 +31,8 @@ BL_EPI_SUBLN_QUANT = 0x4
 BL_EPI_MUL = 0x8
 BL_FFN_PRE_NORM = 0x1
 BL_FFN_RESIDUAL = 0x2
+BL_DTYPE_F32 = 0
+BL_DTYPE_BF16 = 1
 
 RMS_EPS = 1e-5  # rms_norm_eps of the BitNet config
 
@@ -39,6 +41,7 @@ SYMBOLS = (
     "bitlinear_pack_workspace_bytes", "bitlinear_pack_weights", "bitlinear_quant_act",
     "bitlinear_forward_workspace_bytes", "bitlinear_forward",
     "bitlinear_quant_forward_workspace_bytes", "bitlinear_quant_forward",
+    "bitlinear_latent_forward_workspace_bytes", "bitlinear_latent_forward",
     "bitnet_ffn_workspace_bytes", "bitnet_ffn_forward",
 )
 
@@ -99,6 +102,11 @@ def load(path: str = LIB_PATH):
     lib.bitlinear_quant_forward.argtypes = [P, I64, I64, U32, P, F, P, P, I64, ctypes.POINTER(Epilogue),
                                             P, P, SZ, P]
     lib.bitlinear_quant_forward.restype = I
+    lib.bitlinear_latent_forward_workspace_bytes.argtypes = [I64, I64, I64]
+    lib.bitlinear_latent_forward_workspace_bytes.restype = SZ
+    lib.bitlinear_latent_forward.argtypes = [P, I64, I64, U32, P, F, P, U32, I64, ctypes.POINTER(Epilogue),
+                                             P, P, P, SZ, P]
+    lib.bitlinear_latent_forward.restype = I
     lib.bitnet_ffn_workspace_bytes.argtypes = [I64, I64, I64]
     lib.bitnet_ffn_workspace_bytes.restype = SZ
     lib.bitnet_ffn_forward.argtypes = [ctypes.POINTER(FFNLayer), ctypes.c_int32, P, I64, I64, I64,
@@ -274,6 +282,39 @@ def quant_forward(X: torch.Tensor, packed: torch.Tensor, w_scale: torch.Tensor, 
                   mul_by: Optional[torch.Tensor] = None):
     """Quantise fp32 X [M][K] and apply the BitLinear in one call; returns Y [M][N]."""
     return QuantForward(packed, w_scale, X.shape[0], rmsnorm, norm_gain, eps, relu2)(X, residual, y_out, mul_by)
+
+
+def latent_forward(X: torch.Tensor, W: torch.Tensor, rmsnorm: bool = False,
+                   norm_gain: Optional[torch.Tensor] = None, eps: float = RMS_EPS, relu2: bool = False,
+                   residual: Optional[torch.Tensor] = None, mul_by: Optional[torch.Tensor] = None,
+                   y_out: Optional[torch.Tensor] = None, w_scale_out: Optional[torch.Tensor] = None):
+    """BitLinear from latent fp32 or bf16 weights W [N][K] (ternarised inside
+    the call) on fp32 X [M][K]; returns Y [M][N] (the fake-quant forward)."""
+    lib = load()
+    _need(X, torch.float32, 2, "X")
+    if W.dtype not in (torch.float32, torch.bfloat16) or W.dim() != 2 or not W.is_contiguous():
+        raise ValueError("W must be a contiguous 2-D float32 or bfloat16 tensor")
+    M, K = X.shape
+    N = W.shape[0]
+    if W.shape[1] != K:
+        raise ValueError(f"W has {W.shape[1]} columns, X has K = {K}")
+    dev = X.device
+    y = y_out if y_out is not None else torch.empty((M, N), dtype=torch.float32, device=dev)
+    epi = Epilogue()
+    epi.flags = ((BL_EPI_RELU2 if relu2 else 0) | (BL_EPI_RESIDUAL if residual is not None else 0)
+                 | (BL_EPI_MUL if mul_by is not None else 0))
+    if residual is not None:
+        _need(residual, torch.float32, 2, "residual")
+        epi.residual = residual.data_ptr()
+    if mul_by is not None:
+        _need(mul_by, torch.float32, 2, "mul_by")
+        epi.mul_by = mul_by.data_ptr()
+    ws = _workspace(lib.bitlinear_latent_forward_workspace_bytes(M, K, N), dev)
+    dt = BL_DTYPE_BF16 if W.dtype == torch.bfloat16 else BL_DTYPE_F32
+    _check(lib.bitlinear_latent_forward(_p(X), M, K, BL_QUANT_RMSNORM if rmsnorm else 0, _p(norm_gain), float(eps),
+                                        _p(W), dt, N, ctypes.byref(epi), _p(y), _p(w_scale_out), _p(ws),
+                                        0 if ws is None else ws.numel(), _stream(dev)))
+    return y
 
 
 def make_layers(layers: Sequence[dict]):

@@ -1,4 +1,6 @@
-"""Builds libbitlinear.so (HIP, gfx950) in-tree with hipcc.
+"""Builds libbitlinear.so (HIP, gfx950) in-tree with hipcc, and beside it
+libblbench.so, the benchmark's streaming-read reference kernel (csrc/bench;
+measurement support, not part of the BitLinear path).
 
 Usage: ``python -m bit_gemm_absmax_amd.build`` or :func:`build` from Python.
 Every call recompiles all sources.
@@ -16,6 +18,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libbitlinear.so")
+BENCH_LIB = os.path.join(PKG, "libblbench.so")
+BENCH_SRC = os.path.join(CSRC, "bench")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
 ARCH = "gfx950"
@@ -47,14 +51,8 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    if shutil.which(HIPCC) is None and not os.path.exists(HIPCC):
-        raise RuntimeError(f"hipcc not found at {HIPCC}")
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    srcs = sources()
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str) -> None:
+    tmp = lib + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
@@ -63,9 +61,22 @@ def build(verbose: bool = False) -> str:
     # compiler failed to emit shows up here instead of on the GPU machine.
     import ctypes
     ctypes.CDLL(tmp)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    if shutil.which(HIPCC) is None and not os.path.exists(HIPCC):
+        raise RuntimeError(f"hipcc not found at {HIPCC}")
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    srcs = sources()
+    bench_srcs = sorted(os.path.join(BENCH_SRC, f) for f in os.listdir(BENCH_SRC) if f.endswith(".hip"))
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs) + len(bench_srcs))) as ex:
+        objs = list(ex.map(_compile, srcs + bench_srcs))
+    _link(objs[:len(srcs)], LIB)
+    _link(objs[len(srcs):], BENCH_LIB)
     if verbose:
         print(f"built {LIB}")
+        print(f"built {BENCH_LIB}")
     return LIB
 
 

@@ -150,7 +150,7 @@ int bitlinear_pack_weights(const float* W, int64_t N, int64_t K, uint8_t* packed
     if (!aligned(W, 16) || !aligned(packed, 16) || !aligned(w_scale, 4))
         return fail(BL_ERR_ALIGN, "pack: W and packed need 16-byte alignment, w_scale 4-byte");
     if (int r = check_workspace(ws, ws_bytes, bitlinear_pack_workspace_bytes(N, K))) return r;
-    return hip_status(bl::launch_pack(W, N, K, packed, w_scale, static_cast<double*>(ws), stream),
+    return hip_status(bl::launch_pack(W, false, N, K, packed, w_scale, static_cast<double*>(ws), stream),
                       "pack");
 }
 
@@ -251,44 +251,109 @@ size_t bitlinear_quant_forward_workspace_bytes(int64_t M, int64_t K, int64_t N) 
     return c.off;
 }
 
-int bitlinear_quant_forward(const float* X, int64_t M, int64_t K, uint32_t quant_flags, const float* norm_gain,
-                            float norm_eps, const uint8_t* packed, const float* w_scale, int64_t N,
-                            const bl_epilogue* epi, float* Y, void* ws, size_t ws_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+// Checks shared by bitlinear_quant_forward and bitlinear_latent_forward (the
+// weight operand is checked by each caller).
+int check_quant_forward(const char* who, const float* X, int64_t M, int64_t K, uint32_t quant_flags,
+                        const float* norm_gain, int64_t N, const bl_epilogue* epi, float* Y) {
     const uint32_t flags = epi ? epi->flags : 0u;
-    if (!X || !packed || !w_scale || !Y)
-        return fail(BL_ERR_NULL, "quant_forward: X, packed, w_scale and Y are required");
-    if (quant_flags & ~BL_QUANT_RMSNORM)
-        return fail(BL_ERR_UNSUPPORTED, "quant_forward: unknown quant flags 0x%x", quant_flags);
+    if (!X || !Y) return fail(BL_ERR_NULL, "%s: X and Y are required", who);
+    if (quant_flags & ~BL_QUANT_RMSNORM) return fail(BL_ERR_UNSUPPORTED, "%s: unknown quant flags 0x%x", who, quant_flags);
     if (flags & ~(BL_EPI_RELU2 | BL_EPI_RESIDUAL | BL_EPI_MUL))
-        return fail(BL_ERR_UNSUPPORTED, "quant_forward: epilogue flags 0x%x not supported", flags);
-    if (int r = epi ? check_aux(epi, flags, "quant_forward") : BL_OK) return r;
-    if (M < 0) return fail(BL_ERR_SHAPE, "quant_forward: M = %lld must be >= 0", (long long)M);
-    if (N < 1) return fail(BL_ERR_SHAPE, "quant_forward: N = %lld must be >= 1", (long long)N);
-    if (int r = check_k(K, "quant_forward: K")) return r;
-    if (!bl::quant_supported(K))
-        return fail(BL_ERR_UNSUPPORTED, "quant_forward: K = %lld above 32768", (long long)K);
+        return fail(BL_ERR_UNSUPPORTED, "%s: epilogue flags 0x%x not supported", who, flags);
+    if (int r = epi ? check_aux(epi, flags, who) : BL_OK) return r;
+    if (M < 0) return fail(BL_ERR_SHAPE, "%s: M = %lld must be >= 0", who, (long long)M);
+    if (N < 1) return fail(BL_ERR_SHAPE, "%s: N = %lld must be >= 1", who, (long long)N);
+    if (int r = check_k(K, who)) return r;
+    if (!bl::quant_supported(K)) return fail(BL_ERR_UNSUPPORTED, "%s: K = %lld above 32768", who, (long long)K);
     if (M * K >= kLimit || M * N >= kLimit || N * K >= kLimit * 4)
-        return fail(BL_ERR_SHAPE, "quant_forward: sizes exceed 2^31 elements");
-    if (!aligned(X, 16) || !aligned(packed, 16) || !aligned(Y, 16) || !aligned(w_scale, 4) || !aligned(norm_gain, 16))
-        return fail(BL_ERR_ALIGN, "quant_forward: X, packed, Y, gain need 16-byte alignment");
-    const bool fused = bl::decode_supported(M, K, N);
-    if (int r = check_workspace(ws, ws_bytes, M == 0 || fused ? 0 : bitlinear_quant_forward_workspace_bytes(M, K, N)))
-        return r;
-    if (M == 0) return ok();
+        return fail(BL_ERR_SHAPE, "%s: sizes exceed 2^31 elements", who);
+    if (!aligned(X, 16) || !aligned(Y, 16) || !aligned(norm_gain, 16))
+        return fail(BL_ERR_ALIGN, "%s: X, Y, gain need 16-byte alignment", who);
+    return BL_OK;
+}
+
+// Quantise X and run the BitLinear on packed weights: one fused launch for
+// M <= 4 (no workspace), else the quantiser into `ws` then the contraction.
+int run_quant_forward(const char* who, const float* X, int64_t M, int64_t K, uint32_t quant_flags,
+                      const float* norm_gain, float norm_eps, const uint8_t* packed, const float* w_scale, int64_t N,
+                      const bl_epilogue* epi, float* Y, void* ws, hipStream_t stream) {
     const bool rms = (quant_flags & BL_QUANT_RMSNORM) != 0;
     const bl::Epi ke = kernel_epi(epi);
-    if (fused)
+    if (bl::decode_supported(M, K, N))
         return hip_status(bl::launch_decode_bitlinear(X, M, K, rms, rms ? norm_gain : nullptr, norm_eps, packed,
                                                       w_scale, N, ke.flags, ke.aux, Y, stream),
-                          "quant_forward: fused decode kernel");
+                          who);
     Carver c(ws);
     int8_t* xq = c.take<int8_t>((size_t)(M * K));
     float* xs = c.take<float>((size_t)M);
     int32_t* rs = c.take<int32_t>((size_t)M);
     hipError_t e = bl::launch_quant(X, M, K, rms, rms ? norm_gain : nullptr, norm_eps, xq, xs, rs, stream);
-    if (e != hipSuccess) return hip_status(e, "quant_forward: quant");
-    e = bl::launch_contract(xq, xs, rs, M, K, packed, w_scale, N, ke, Y, nullptr, stream);
-    return hip_status(e, "quant_forward: contraction");
+    if (e != hipSuccess) return hip_status(e, who);
+    return hip_status(bl::launch_contract(xq, xs, rs, M, K, packed, w_scale, N, ke, Y, nullptr, stream), who);
+}
+
+size_t quant_forward_ws(int64_t M, int64_t K, int64_t N) {
+    if (M < 1 || K < 1 || bl::decode_supported(M, K, N)) return 0;
+    Carver c(nullptr);
+    c.take<int8_t>((size_t)(M * K));
+    c.take<float>((size_t)M);
+    c.take<int32_t>((size_t)M);
+    return c.off;
+}
+}  // namespace
+
+extern "C" {
+
+int bitlinear_quant_forward(const float* X, int64_t M, int64_t K, uint32_t quant_flags, const float* norm_gain,
+                            float norm_eps, const uint8_t* packed, const float* w_scale, int64_t N,
+                            const bl_epilogue* epi, float* Y, void* ws, size_t ws_bytes, hipStream_t stream) {
+    const char* who = "quant_forward";
+    if (int r = check_quant_forward(who, X, M, K, quant_flags, norm_gain, N, epi, Y)) return r;
+    if (!packed || !w_scale) return fail(BL_ERR_NULL, "quant_forward: packed and w_scale are required");
+    if (!aligned(packed, 16) || !aligned(w_scale, 4))
+        return fail(BL_ERR_ALIGN, "quant_forward: packed needs 16-byte alignment, w_scale 4-byte");
+    if (int r = check_workspace(ws, ws_bytes, M == 0 ? 0 : quant_forward_ws(M, K, N))) return r;
+    if (M == 0) return ok();
+    return run_quant_forward(who, X, M, K, quant_flags, norm_gain, norm_eps, packed, w_scale, N, epi, Y, ws, stream);
+}
+
+// ---------------------------------------------------------------- forward from latent weights
+
+size_t bitlinear_latent_forward_workspace_bytes(int64_t M, int64_t K, int64_t N) {
+    if (M < 1 || K < 1 || N < 1) return 0;
+    Carver c(nullptr);
+    c.take<uint8_t>((size_t)(N * K / 4));
+    c.take<float>(1);
+    c.take<double>((size_t)bl::pack_partial_blocks(N * K));
+    c.take<uint8_t>(quant_forward_ws(M, K, N));
+    return c.off;
+}
+
+int bitlinear_latent_forward(const float* X, int64_t M, int64_t K, uint32_t quant_flags, const float* norm_gain,
+                             float norm_eps, const void* W, uint32_t w_dtype, int64_t N, const bl_epilogue* epi,
+                             float* Y, float* w_scale, void* ws, size_t ws_bytes, hipStream_t stream) {
+    const char* who = "latent_forward";
+    if (int r = check_quant_forward(who, X, M, K, quant_flags, norm_gain, N, epi, Y)) return r;
+    if (!W) return fail(BL_ERR_NULL, "latent_forward: W is required");
+    if (w_dtype != BL_DTYPE_F32 && w_dtype != BL_DTYPE_BF16)
+        return fail(BL_ERR_UNSUPPORTED, "latent_forward: w_dtype %u is neither BL_DTYPE_F32 nor BL_DTYPE_BF16", w_dtype);
+    if (!aligned(W, 16) || !aligned(w_scale, 4))
+        return fail(BL_ERR_ALIGN, "latent_forward: W needs 16-byte alignment, w_scale 4-byte");
+    if (int r = check_workspace(ws, ws_bytes, M == 0 ? 0 : bitlinear_latent_forward_workspace_bytes(M, K, N)))
+        return r;
+    if (M == 0) return ok();
+    Carver c(ws);
+    uint8_t* packed = c.take<uint8_t>((size_t)(N * K / 4));
+    float* gw = c.take<float>(1);
+    double* partial = c.take<double>((size_t)bl::pack_partial_blocks(N * K));
+    void* qws = c.take<uint8_t>(quant_forward_ws(M, K, N));
+    if (w_scale) gw = w_scale;
+    hipError_t e = bl::launch_pack(W, w_dtype == BL_DTYPE_BF16, N, K, packed, gw, partial, stream);
+    if (e != hipSuccess) return hip_status(e, "latent_forward: pack");
+    return run_quant_forward(who, X, M, K, quant_flags, norm_gain, norm_eps, packed, gw, N, epi, Y, qws, stream);
 }
 
 // ---------------------------------------------------------------- FFN stack

@@ -23,10 +23,11 @@ constexpr uint32_t kEpiMul = 0x4u;
 // ---- launchers (return hipError_t of the launch) ----------------------------
 
 // Weight packing: partial binary64 sums of |W| into `partial` (count returned
-// by pack_partial_blocks), then ternarise + pack.
+// by pack_partial_blocks), then ternarise + pack.  W is fp32, or bf16 when
+// `bf16` (widened exactly to fp32 before any arithmetic).
 int pack_partial_blocks(int64_t count);
-hipError_t launch_pack(const float* W, int64_t N, int64_t K, uint8_t* packed,
-                       float* w_scale, double* partial, hipStream_t s);
+hipError_t launch_pack(const void* W, bool bf16, int64_t N, int64_t K, uint8_t* packed, float* w_scale,
+                       double* partial, hipStream_t s);
 
 // Per-row absmax quantisation with optional RMSNorm (gain may be null).
 hipError_t launch_quant(const float* X, int64_t M, int64_t K, bool rmsnorm,

@@ -252,7 +252,7 @@ __device__ __forceinline__ void batch_body(Rsrc ra, const uint32_t (&voff)[MT][2
     do {                                                                                           \
         const int c_ = 4 * (wave + (ii) * kBatchWaves) + fg;                                       \
         _Pragma("unroll") for (int ct = 0; ct < CT; ++ct)                                          \
-            w[ct][ii] = buf_load16(rw[ct], c_ < C ? (uint32_t)(c_ * rows[ct] + fr) * 16u : kOob);  \
+            w[ct][ii] = buf_load16_nt(rw[ct], c_ < C ? (uint32_t)(c_ * rows[ct] + fr) * 16u : kOob); \
     } while (0)
     // quad i (the wave's i-th) -> stage i % NS: per token tile, 4 DMAs of 8 rows x 128 bytes
 #define BL_DMA(ii)                                                                                        \

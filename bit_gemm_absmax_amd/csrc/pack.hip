@@ -1,5 +1,5 @@
-// Weight packer: absmean ternarisation and 2-bit packing of latent fp32
-// weights (transformers "BitNet" page, "Model details" / Quantization:
+// Weight packer: absmean ternarisation and 2-bit packing of latent fp32 or
+// bf16 weights (transformers "BitNet" page, "Model details" / Quantization:
 // ternary {-1, 0, +1} weights by absmean quantisation; "Model variants":
 // packed 1.58-bit weights for deployment).
 //
@@ -25,14 +25,30 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kMaxPartials = 1024;
 
-__global__ __launch_bounds__(kThreads) void k_absmean_partial(const float4* __restrict__ W,
-                                                              int64_t n4,
+// Latent weight element types: load4(W, i) returns weights 4i..4i+3 as fp32.
+// A bf16 value is the upper half of the fp32 with the same bits, so widening
+// is exact and both types go through the same arithmetic.
+struct InF32 {
+    static __device__ __forceinline__ float4 load4(const void* W, int64_t i) {
+        return reinterpret_cast<const float4*>(W)[i];
+    }
+};
+struct InBF16 {
+    static __device__ __forceinline__ float4 load4(const void* W, int64_t i) {
+        const uint2 u = reinterpret_cast<const uint2*>(W)[i];  // little-endian: element 2j in the low half
+        return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xFFFF0000u),
+                           __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xFFFF0000u));
+    }
+};
+
+template <typename In>
+__global__ __launch_bounds__(kThreads) void k_absmean_partial(const void* __restrict__ W, int64_t n4,
                                                               double* __restrict__ partial) {
     __shared__ double slot[kThreads / kWave];
     double s = 0.0;
     const int64_t stride = (int64_t)gridDim.x * kThreads;
     for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n4; i += stride) {
-        const float4 v = W[i];
+        const float4 v = In::load4(W, i);
         s += fabs((double)v.x);
         s += fabs((double)v.y);
         s += fabs((double)v.z);
@@ -51,7 +67,8 @@ __device__ __forceinline__ uint32_t ternary_code(float w, float gamma) {
     return (uint32_t)((int)r + 1);
 }
 
-__global__ __launch_bounds__(kThreads) void k_ternary_pack(const float4* __restrict__ W,
+template <typename In>
+__global__ __launch_bounds__(kThreads) void k_ternary_pack(const void* __restrict__ W,
                                                            int64_t nwords, int64_t N, int64_t K,
                                                            const double* __restrict__ partial,
                                                            int nparts, double count,
@@ -69,7 +86,7 @@ __global__ __launch_bounds__(kThreads) void k_ternary_pack(const float4* __restr
     for (int64_t w = (int64_t)blockIdx.x * kThreads + threadIdx.x; w < nwords; w += stride) {
         float4 v[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) v[j] = W[4 * w + j];
+        for (int j = 0; j < 4; ++j) v[j] = In::load4(W, 4 * w + j);
         uint32_t word = 0;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -100,19 +117,26 @@ int pack_partial_blocks(int64_t count) {
     return (int)g;
 }
 
-hipError_t launch_pack(const float* W, int64_t N, int64_t K, uint8_t* packed,
-                       float* w_scale, double* partial, hipStream_t s) {
+namespace {
+template <typename In>
+hipError_t go_pack(const void* W, int64_t N, int64_t K, uint8_t* packed, float* w_scale, double* partial,
+                   hipStream_t s) {
     const int64_t count = N * K;
     const int g = pack_partial_blocks(count);
-    hipLaunchKernelGGL(k_absmean_partial, dim3(g), dim3(kThreads), 0, s,
-                       reinterpret_cast<const float4*>(W), count / 4, partial);
+    hipLaunchKernelGGL(k_absmean_partial<In>, dim3(g), dim3(kThreads), 0, s, W, count / 4, partial);
     const int64_t nwords = count / 16;
     int64_t blocks = (nwords + kThreads - 1) / kThreads;
     if (blocks > 8192) blocks = 8192;
-    hipLaunchKernelGGL(k_ternary_pack, dim3((unsigned)blocks), dim3(kThreads), 0, s,
-                       reinterpret_cast<const float4*>(W), nwords, N, K, partial, g,
-                       (double)count, reinterpret_cast<uint32_t*>(packed), w_scale);
+    hipLaunchKernelGGL(k_ternary_pack<In>, dim3((unsigned)blocks), dim3(kThreads), 0, s, W, nwords, N, K,
+                       partial, g, (double)count, reinterpret_cast<uint32_t*>(packed), w_scale);
     return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_pack(const void* W, bool bf16, int64_t N, int64_t K, uint8_t* packed, float* w_scale,
+                       double* partial, hipStream_t s) {
+    return bf16 ? go_pack<InBF16>(W, N, K, packed, w_scale, partial, s)
+                : go_pack<InF32>(W, N, K, packed, w_scale, partial, s);
 }
 
 }  // namespace bl

@@ -36,6 +36,21 @@ def weights(rng: np.random.Generator, n: int, k: int, std: float = W_STD) -> np.
     return (rng.standard_normal((n, k)) * std).astype(np.float32)
 
 
+def to_bf16(a: np.ndarray):
+    """Round fp32 values to bfloat16 (nearest, ties to even; inputs finite).
+    Returns (bits, values): the uint16 bit patterns and the same numbers as
+    fp32 (exact: a bfloat16 is the upper half of an fp32)."""
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    bits = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+    values = (bits.astype(np.uint32) << 16).view(np.float32)
+    return bits, values
+
+
+def weights_bf16(rng: np.random.Generator, n: int, k: int, std: float = W_STD):
+    """Latent bfloat16 weight [n][k] ~ N(0, std), as (bits, fp32 values)."""
+    return to_bf16(weights(rng, n, k, std))
+
+
 def activations(rng: np.random.Generator, m: int, k: int, outliers: bool = False,
                 frac: float = 0.01, factor: float = 20.0) -> np.ndarray:
     """fp32 activations [m][k] ~ N(0, 1); with outliers, round(frac*k) distinct

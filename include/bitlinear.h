@@ -90,7 +90,7 @@ const char* bitlinear_last_error(void);
 
 /* ABI version of this header, (major << 16) | minor. */
 int bitlinear_abi_version(void);
-#define BITLINEAR_ABI_VERSION ((1 << 16) | 1)
+#define BITLINEAR_ABI_VERSION ((1 << 16) | 2)
 
 /* ------------------------------------------------------------------------
  * Weight packing ("Model details" / Quantization: absmean ternary weights).
@@ -213,6 +213,41 @@ int bitlinear_quant_forward(const float* X, int64_t M, int64_t K, uint32_t quant
                             const uint8_t* packed, const float* w_scale, int64_t N,
                             const bl_epilogue* epi, float* Y,
                             void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * BitLinear from latent weights, the forward pass of quantisation-aware
+ * training ("Model details" / Quantization: the weights are quantised to
+ * ternary by absmean and the activations per token by absmax inside the
+ * forward pass; the latent weights stay in high precision):
+ *
+ *   gamma_w, q = absmean-ternarise(W)          exactly as bitlinear_pack_weights
+ *   Y          = BitLinear(X; q, gamma_w)      exactly as bitlinear_quant_forward
+ *
+ * Y is the dequantised ("fake-quant") product: in real arithmetic
+ * Y[m][n] = sum_k (xq[m][k] * gamma_x[m] / 127) * (q[n][k] * gamma_w) (+ epilogue);
+ * the integer sum is exact and rounding enters only in the scaling.
+ *
+ * X           in  fp32 [M][K]; quant_flags / norm_gain / norm_eps as in
+ *                 bitlinear_quant_act
+ * W           in  latent weights [N][K], fp32 (w_dtype BL_DTYPE_F32) or bf16
+ *                 (BL_DTYPE_BF16, widened exactly to fp32); 16-byte aligned
+ * epi         in  host pointer or NULL; BL_EPI_RELU2, BL_EPI_RESIDUAL and
+ *                 BL_EPI_MUL as in bitlinear_quant_forward
+ * Y           out fp32 [M][N]
+ * w_scale     out fp32 [1], gamma_w, or NULL (kept in the workspace)
+ * ws          scratch of bitlinear_latent_forward_workspace_bytes(M, K, N):
+ *             the packed weights (N*K/4 bytes) and the quantised rows
+ * BL_ERR_UNSUPPORTED for another w_dtype; other errors as bitlinear_quant_forward.
+ * ---------------------------------------------------------------------- */
+#define BL_DTYPE_F32 0u
+#define BL_DTYPE_BF16 1u
+
+size_t bitlinear_latent_forward_workspace_bytes(int64_t M, int64_t K, int64_t N);
+int bitlinear_latent_forward(const float* X, int64_t M, int64_t K, uint32_t quant_flags,
+                             const float* norm_gain, float norm_eps,
+                             const void* W, uint32_t w_dtype, int64_t N,
+                             const bl_epilogue* epi, float* Y, float* w_scale,
+                             void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * BitNet feed-forward stack: for each layer in order, on hidden [M][H]

@@ -46,7 +46,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.bitlinear_abi_version() == (1 << 16) | 1
+    assert lib.bitlinear_abi_version() == (1 << 16) | 2
     for s in range(-6, 1):
         assert lib.bitlinear_status_string(s)
     assert lib.bitlinear_status_string(-99) == b"unknown status"
@@ -179,3 +179,34 @@ def test_quant_forward_validation(lib):
     assert f(A, 1, 64, 0, None, 1e-5, B, C, 8, nul, MIS, None, 0, None) == bl.BL_ERR_ALIGN
     assert f(A, 0, 64, 0, None, 1e-5, B, C, 8, nul, D, None, 0, None) == bl.BL_OK
     assert lib.bitlinear_quant_forward_workspace_bytes(64, 2560, 6912) >= 64 * 2560
+
+
+def test_latent_forward_validation(lib):
+    f = lib.bitlinear_latent_forward
+    nul = ctypes.POINTER(bl.Epilogue)()
+    F32, BF16 = bl.BL_DTYPE_F32, bl.BL_DTYPE_BF16
+    assert f(A, 1, 64, 0, None, 1e-5, None, F32, 8, nul, D, None, None, 0, None) == bl.BL_ERR_NULL
+    assert f(None, 1, 64, 0, None, 1e-5, B, F32, 8, nul, D, None, None, 0, None) == bl.BL_ERR_NULL
+    assert f(A, 1, 64, 0, None, 1e-5, B, 7, 8, nul, D, None, None, 0, None) == bl.BL_ERR_UNSUPPORTED
+    assert f(A, 1, 96, 0, None, 1e-5, B, BF16, 8, nul, D, None, None, 0, None) == bl.BL_ERR_SHAPE
+    assert f(A, 1, 64, 0, None, 1e-5, MIS, F32, 8, nul, D, None, None, 0, None) == bl.BL_ERR_ALIGN
+    assert f(A, 1, 64, 0, None, 1e-5, B, F32, 8, nul, D, None, None, 0, None) == bl.BL_ERR_WORKSPACE
+    assert f(A, 0, 64, 0, None, 1e-5, B, F32, 8, nul, D, None, None, 0, None) == bl.BL_OK
+    need = lib.bitlinear_latent_forward_workspace_bytes(4096, 2560, 6912)
+    assert need >= 6912 * 2560 // 4 + 4096 * 2560
+    assert lib.bitlinear_latent_forward_workspace_bytes(0, 2560, 6912) == 0
+
+
+def test_bench_library_exports_stream_read():
+    """The benchmark's read-bandwidth kernel library: built beside the main
+    one, exports its one call, and rejects sizes before launching anything."""
+    from bit_gemm_absmax_amd import build
+    if not os.path.exists(build.BENCH_LIB):
+        build.build()
+    blib = ctypes.CDLL(build.BENCH_LIB)
+    f = blib.blbench_stream_read
+    f.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_void_p]
+    f.restype = ctypes.c_int
+    assert f(None, 3, None, None) == -2
+    assert f(None, (256 << 20) + 64, None, None) == -2
+    assert f(None, 4 << 30, None, None) == -2

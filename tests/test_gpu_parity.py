@@ -476,6 +476,69 @@ def test_ffn_gated_block(M):
     assert np.abs(host(hs) - ref).max() <= 1e-3 * np.abs(ref).max()
 
 
+# ------------------------------------------------------------------ forward from latent weights
+
+def latent_weights(rng, N, K, dtype):
+    """(device tensor in the given dtype, the same numbers as fp32 numpy)."""
+    if dtype == "bf16":
+        bits, W = synth.weights_bf16(rng, N, K)
+        return torch.from_numpy(bits.view(np.int16)).to(DEV).view(torch.bfloat16), W
+    W = synth.weights(rng, N, K)
+    return dev(W), W
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("M,K,N,epi", [(1, 256, 130, "relu2"), (3, 2560, 6912, None), (8, 320, 512, "residual"),
+                                        (70, 512, 200, "mul"), (300, 1024, 272, "relu2")])
+def test_latent_forward(M, K, N, epi, dtype):
+    """BitLinear from latent fp32 / bf16 weights (ternarised inside the call)
+    through the fused decode (M <= 4), batched and GEMM paths: gamma_w and Y
+    exactly those of pack + quant_forward on the same numbers, Y against the
+    oracle, and without an epilogue within 1e-6 of the binary64 fake-quant
+    product of the dequantised operands."""
+    log(f"[latent forward] M={M} K={K} N={N} epi={epi} {dtype}")
+    rng = np.random.default_rng(4100 + M + K + N + (dtype == "bf16"))
+    Wt, W = latent_weights(rng, N, K, dtype)
+    X = synth.activations(rng, M, K, outliers=True)
+    A = synth.activations(rng, M, N)
+    kw = dict(relu2=epi == "relu2", residual=dev(A) if epi == "residual" else None,
+              mul_by=dev(A) if epi == "mul" else None)
+    gw_t = torch.empty(1, dtype=torch.float32, device=DEV)
+    y = bl.latent_forward(dev(X), Wt, w_scale_out=gw_t, **kw)
+    p, s, q, gw = check_pack(W, "latent forward")
+    assert host(gw_t)[0] == host(s)[0], "gamma_w of the latent forward vs the packer"
+    y2 = bl.quant_forward(dev(X), p, s, **kw)
+    assert_exact(host(y), host(y2), "latent forward vs pack + quant_forward")
+    xq, gx, _ = oracle.quant_act(X)
+    acc = oracle.int_matmul(xq, q)
+    want = oracle.dequant(acc, gx, gw)
+    if epi == "relu2":
+        want = oracle.relu2(want)
+    elif epi == "residual":
+        want = oracle.add(A.copy(), want)
+    elif epi == "mul":
+        want = oracle.mul(want, A)
+    assert_y_close(host(y), want, "latent forward y")
+    if epi is None:
+        fake = (xq.astype(np.float64) * (gx.astype(np.float64)[:, None] / 127.0)) @ \
+            (q.astype(np.float64) * float(gw)).T
+        scale = np.abs(fake).max(axis=1, keepdims=True)
+        assert np.all(np.abs(host(y) - fake) <= 1e-6 * np.maximum(np.abs(fake), 1e-6 * scale))
+
+
+def test_latent_forward_bf16_equals_f32_of_same_values():
+    """bf16 latent weights give bit-identical results to the fp32 tensor of
+    the same numbers (the widening is exact), at the model's up shape."""
+    rng = np.random.default_rng(4200)
+    bits, W = synth.weights_bf16(rng, synth.FFN, synth.HIDDEN)
+    Wb = torch.from_numpy(bits.view(np.int16)).to(DEV).view(torch.bfloat16)
+    X = dev(synth.activations(rng, 2, synth.HIDDEN, outliers=True))
+    ya = bl.latent_forward(X, Wb, relu2=True)
+    yb = bl.latent_forward(X, dev(W), relu2=True)
+    assert_exact(host(ya), host(yb), "bf16 vs fp32 latent weights")
+    assert torch.equal(Wb.float().cpu(), torch.from_numpy(W))  # torch's widening agrees
+
+
 # ------------------------------------------------------------------ the five workloads
 
 def test_workload_single_bitlinear():

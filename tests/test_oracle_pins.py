@@ -508,3 +508,21 @@ def test_gated_token_independence():
     for r in (0, 3):
         one = oracle.ffn_layer_gated(X[r:r + 1], *args)
         assert np.array_equal(one[0], full[r])
+
+
+# ---------------------------------------------------------------- bf16 latent weights (input widening)
+
+def test_bf16_inputs_round_to_nearest_even():
+    """The bf16 input generator rounds to nearest, ties to even, and its fp32
+    values are exactly the bf16 numbers, so the oracle run on them is the
+    oracle of the bf16 weights."""
+    a = np.array([1.0, 1.00390625, 1.01171875, 1.0 + 2.0 ** -8 + 2.0 ** -20, -3.140625, 0.0, -0.0],
+                 dtype=np.float32)
+    bits, vals = synth.to_bf16(a)
+    assert bits.tolist() == [0x3F80, 0x3F80, 0x3F82, 0x3F81, 0xC049, 0x0000, 0x8000]
+    assert vals.tolist() == [1.0, 1.0, 1.015625, 1.0078125, -3.140625, 0.0, -0.0]
+    rng = np.random.default_rng(11)
+    w = synth.weights(rng, 64, 64)
+    b2, v2 = synth.to_bf16(w)
+    assert np.all(np.abs(v2 - w) <= np.abs(w) * 2.0 ** -8)
+    assert np.array_equal(synth.to_bf16(v2)[0], b2)  # bf16 values are fixed points
