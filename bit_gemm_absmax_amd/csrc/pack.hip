@@ -58,13 +58,17 @@ __global__ __launch_bounds__(kThreads) void k_absmean_partial(const void* __rest
     if (threadIdx.x == 0) partial[blockIdx.x] = s;
 }
 
-// code = clamp(rint(w / gamma), -1, 1) + 1, with one correctly rounded divide
-// and round-half-to-even (v_rndne_f32).
+// code = clamp(rint(w / gamma), -1, 1) + 1 (binary32 quotient, ties to
+// even), computed without the divide.  rint of the rounded quotient |w|/gamma
+// is nonzero exactly when that quotient exceeds 0.5, i.e. when |w|/gamma lies
+// above the midpoint 0.5 + 2^-25 between 0.5 and the next binary32 (at the
+// midpoint the tie goes to 0.5, whose significand is even): 2|w| > gamma
+// (1 + 2^-24).  For binary32 gamma = m 2^e (2^23 <= m < 2^24) the next
+// binary32 above gamma is gamma (1 + 1/m) > gamma (1 + 2^-24), and 2|w| is an
+// exact binary32, so that holds exactly when 2|w| > gamma.  The clip then
+// leaves the sign of w.
 __device__ __forceinline__ uint32_t ternary_code(float w, float gamma) {
-    float r = rintf(w / gamma);
-    r = r > 1.0f ? 1.0f : r;
-    r = r < -1.0f ? -1.0f : r;
-    return (uint32_t)((int)r + 1);
+    return 2.0f * fabsf(w) > gamma ? (w > 0.0f ? 2u : 0u) : 1u;
 }
 
 template <typename In>

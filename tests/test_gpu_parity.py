@@ -56,6 +56,41 @@ def test_pack_small(N, K):
     check_pack(synth.weights(rng, N, K), "small")
 
 
+@pytest.mark.parametrize("seed", range(3))
+def test_pack_rounding_boundaries(seed):
+    """Entries at gamma/2 and 3 gamma/2 and up to 4 ulps either side, both
+    signs, inside an N(0, 0.02) matrix: the packed codes equal the oracle's
+    rint-and-clip of the binary32 quotient exactly.  gamma moves with the
+    probes, so they are re-placed around the oracle's gamma until it stops
+    changing."""
+    rng = np.random.default_rng(5200 + seed)
+    N, K = 96, 1024
+    W = synth.weights(rng, N, K)
+    pos = rng.choice(N * K, 72, replace=False)
+    g = oracle.quantize_weights(W)[1]
+    for _ in range(6):
+        vals = []
+        for centre in (np.float32(g) / np.float32(2), np.float32(g) * np.float32(1.5)):
+            w = centre
+            for _ in range(4):
+                w = np.nextafter(w, np.float32(0))
+            for _ in range(9):
+                vals.append(w)
+                w = np.nextafter(w, np.float32(np.inf))
+        vals = np.array(vals + [-v for v in vals], dtype=np.float32)
+        Wp = W.copy().reshape(-1)
+        Wp[pos[:len(vals)]] = vals
+        Wp = Wp.reshape(N, K)
+        g2 = oracle.quantize_weights(Wp)[1]
+        if g2 == g:
+            break
+        g = g2
+    assert g2 == g, "probe placement did not settle"
+    half = np.float32(g) / np.float32(2)
+    assert half in Wp and np.nextafter(half, np.float32(np.inf)) in Wp
+    check_pack(Wp, "rounding boundaries")
+
+
 def test_pack_special_values():
     W = np.zeros((5, 128), np.float32)
     p, s = gpu_pack(W)

@@ -152,6 +152,34 @@ def test_ternary_threshold_form(seed):
 
 
 @pytest.mark.parametrize("seed", range(4))
+def test_ternary_threshold_form_at_ties(seed):
+    """At and around the rounding boundaries (w = gamma/2 and 3 gamma/2,
+    a few ulps either side, both signs), rint-and-clip of the binary32
+    quotient W/gamma equals sign(W)*[2|W| > gamma] exactly: the quotient's
+    rounding never moves a binary32 2|W| across gamma."""
+    rng = np.random.default_rng(260 + seed)
+    gammas = np.concatenate([rng.uniform(1e-5, 1.0, 6), [1e-5, 0.5, 1.0, 0.75]]).astype(np.float32)
+    for g in gammas:
+        ws = []
+        for centre in (np.float32(g) / np.float32(2), np.float32(g) * np.float32(1.5)):
+            w = centre
+            for _ in range(4):
+                w = np.nextafter(w, np.float32(0))
+            for _ in range(9):
+                ws.append(w)
+                w = np.nextafter(w, np.float32(np.inf))
+        W = np.array(ws + [-x for x in ws] + [0.0, -0.0], dtype=np.float32)[None, :]
+        q = oracle.ternarize(W, g)
+        want = (np.sign(W) * (2.0 * np.abs(W.astype(np.float64)) > float(g))).astype(np.int8)
+        np.testing.assert_array_equal(q, want)
+        # the boundary itself: w = gamma/2 exactly gives 0, its successor +-1
+        half = np.float32(g) / np.float32(2)
+        assert oracle.ternarize(np.array([[half, -half]], np.float32), g).tolist() == [[0, 0]]
+        nxt = np.nextafter(half, np.float32(np.inf))
+        assert oracle.ternarize(np.array([[nxt, -nxt]], np.float32), g).tolist() == [[1, -1]]
+
+
+@pytest.mark.parametrize("seed", range(4))
 def test_absmax_nearest_integer(seed):
     """xq is the integer nearest to x*127/gamma_x (checked in binary64)."""
     rng = np.random.default_rng(300 + seed)
