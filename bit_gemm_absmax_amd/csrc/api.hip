@@ -266,7 +266,8 @@ int check_quant_forward(const char* who, const float* X, int64_t M, int64_t K, u
     if (int r = epi ? check_aux(epi, flags, who) : BL_OK) return r;
     if (M < 0) return fail(BL_ERR_SHAPE, "%s: M = %lld must be >= 0", who, (long long)M);
     if (N < 1) return fail(BL_ERR_SHAPE, "%s: N = %lld must be >= 1", who, (long long)N);
-    if (int r = check_k(K, who)) return r;
+    if (K < 64 || K % 64 != 0)
+        return fail(BL_ERR_SHAPE, "%s: K = %lld must be a positive multiple of 64", who, (long long)K);
     if (!bl::quant_supported(K)) return fail(BL_ERR_UNSUPPORTED, "%s: K = %lld above 32768", who, (long long)K);
     if (M * K >= kLimit || M * N >= kLimit || N * K >= kLimit * 4)
         return fail(BL_ERR_SHAPE, "%s: sizes exceed 2^31 elements", who);
