@@ -318,6 +318,50 @@ def bench_batched(torch, bl, synth, dev, log):
             "roofline": "max(packed bytes / 8 TB/s, int8 ops / 5 POPS) over the measured time", "runs": out}
 
 
+def bench_ffn_layers(torch, bl, synth, dev, log):
+    """Context: one FFN layer through bitnet_ffn_forward at M = 8, 32, 64
+    (pre-norm, residual), plain (up, down) and gated (gate and up in one
+    launch, then down), over rotating copies that exceed twice the Infinity
+    Cache; GB/s counts the packed bytes of the layer's matrices."""
+    import numpy as np
+    rng = np.random.default_rng(8)
+    packs = {}
+    for name, (n, k) in (("gate", (F, H)), ("up", (F, H)), ("down", (H, F))):
+        Wt = torch.from_numpy(synth.weights(rng, n, k)).to(dev)
+        packs[name] = bl.pack_weights(Wt)
+        del Wt
+    out = []
+    for gated in (False, True):
+        nb = (3 if gated else 2) * PACKED_BYTES_MATRIX
+        R = max(2, -(-(2 * MALL_BYTES) // nb))
+        layers = []
+        for _ in range(R):
+            L = {"up": packs["up"][0].clone(), "up_scale": packs["up"][1],
+                 "down": packs["down"][0].clone(), "down_scale": packs["down"][1]}
+            if gated:
+                L.update(gate=packs["gate"][0].clone(), gate_scale=packs["gate"][1])
+            layers.append(L)
+        for M in (8, 32, 64):
+            stacks = [bl.FFNStack([L], H, F, M, dev) for L in layers]
+            h = torch.from_numpy(synth.activations(rng, M, H)).to(dev)
+
+            def run():
+                for st in stacks:
+                    st(h)
+
+            t, gg = time_graph(torch, run, reps=3)
+            del gg
+            t /= R
+            log(f"FFN layer {'gated' if gated else 'plain'} M={M}: {t * 1e6:.2f} us -> {nb / t / 1e9:.0f} GB/s")
+            out.append({"gated": gated, "M": M, "us": round(t * 1e6, 2), "packed_bytes": nb,
+                        "GB_per_s": round(nb / t / 1e9, 1)})
+            del stacks
+        del layers
+        torch.cuda.empty_cache()
+    return {"workload": "one FFN layer (pre-norm, residual), hidden 2560, intermediate 6912, seed 8",
+            "copies_rotated": "packed bytes over twice the Infinity Cache", "runs": out}
+
+
 def bench_stack(torch, bl, synth, dev, log, passes=8):
     """The 30-layer FFN stack (seed 4) with pre-norm and residual, at M=1 and
     M=32, all layers' packed weights resident; the timed passes rotate over
@@ -680,6 +724,8 @@ def main():
     torch.cuda.empty_cache()
     stack = None if args.no_stack else bench_stack(torch, bl, synth, dev, log)
     torch.cuda.empty_cache()
+    ffn_layers = None if args.no_batched else bench_ffn_layers(torch, bl, synth, dev, log)
+    torch.cuda.empty_cache()
     latent = None if args.no_latent else bench_latent(torch, bl, synth, dev, log)
     torch.cuda.empty_cache()
     read = stream_read(torch, dev, log)
@@ -701,7 +747,7 @@ def main():
                       "gated_step_us": round(gated_s * 1e6, 3),
                       "gated_step_GB_per_s": round(1.5 * PACKED_BYTES_STEP / gated_s / 1e9, 1)},
            "roofline": roofline, "cpu_baseline": cpu, "prefill": prefill, "decode_shapes": shapes,
-           "batched_decode": batched, "stack": stack, "latent_forward": latent, "stream_read": read,
+           "batched_decode": batched, "stack": stack, "ffn_layer_batched": ffn_layers, "latent_forward": latent, "stream_read": read,
            "decode_tall": tall}
     print(json.dumps(out), flush=True)
 

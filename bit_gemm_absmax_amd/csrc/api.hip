@@ -428,10 +428,16 @@ int bitnet_ffn_forward(const bitnet_ffn_layer* layers, int32_t n_layers, float* 
                                         xq1, s1, rs1, stream);
         if (e != hipSuccess) return hip_status(e, "ffn: input quant");
         const bool gated = L.gate != nullptr;
-        e = bl::launch_contract(xq1, s1, rs1, M, H, L.up, L.up_scale, F,
-                                bl::Epi{gated ? 0u : bl::kEpiRelu2, nullptr}, y1, nullptr, stream);
-        if (e != hipSuccess) return hip_status(e, "ffn: up");
-        if (gated) {
+        if (gated && bl::gemv_supported(M, H, F)) {
+            // few tokens: gate and up streamed by one launch
+            e = bl::launch_gemv_gated(xq1, s1, rs1, M, H, L.up, L.up_scale, L.gate, L.gate_scale, F, y1, stream);
+            if (e != hipSuccess) return hip_status(e, "ffn: gate and up");
+        } else {
+            e = bl::launch_contract(xq1, s1, rs1, M, H, L.up, L.up_scale, F,
+                                    bl::Epi{gated ? 0u : bl::kEpiRelu2, nullptr}, y1, nullptr, stream);
+            if (e != hipSuccess) return hip_status(e, "ffn: up");
+        }
+        if (gated && !bl::gemv_supported(M, H, F)) {
             e = bl::launch_contract(xq1, s1, rs1, M, H, L.gate, L.gate_scale, F,
                                     bl::Epi{bl::kEpiRelu2 | bl::kEpiMul, y1}, y1, nullptr, stream);
             if (e != hipSuccess) return hip_status(e, "ffn: gate");

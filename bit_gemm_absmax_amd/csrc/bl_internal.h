@@ -51,6 +51,12 @@ hipError_t launch_gemv(const int8_t* Xq, const float* xs, const int32_t* rs, int
                        int64_t K, const uint8_t* packed, const float* ws, int64_t N, Epi epi,
                        float* Y, int32_t* acc_out, hipStream_t s);
 
+// The gated pair ReLU^2(BitLinear(x; gate)) * BitLinear(x; up) in one
+// skinny launch (same shapes as launch_gemv).
+hipError_t launch_gemv_gated(const int8_t* Xq, const float* xs, const int32_t* rs, int64_t M, int64_t K,
+                             const uint8_t* up, const float* up_scale, const uint8_t* gate, const float* gate_scale,
+                             int64_t N, float* Y, hipStream_t s);
+
 // int8 MFMA GEMM for any M.
 hipError_t launch_gemm(const int8_t* Xq, const float* xs, const int32_t* rs, int64_t M,
                        int64_t K, const uint8_t* packed, const float* ws, int64_t N, Epi epi,

@@ -314,33 +314,42 @@ __device__ __forceinline__ void batch_body(Rsrc ra, const uint32_t (&voff)[MT][2
 #undef BL_WT
 }
 
-template <int MT, int CT, int NS, int QMAX>
+// GATED (CT = 2): the two column tiles are the same 16 output rows of the up
+// matrix Wp (tile 0) and of the gate matrix Wg (tile 1), sharing every
+// activation fragment, and the output is ReLU^2(gate) * up.
+template <int MT, int CT, int NS, int QMAX, bool GATED = false>
 __global__ __launch_bounds__(kBatchWaves* kWave) void k_batch(const int8_t* __restrict__ Xq,
                                                                const float* __restrict__ x_scale,
                                                                const int32_t* __restrict__ x_rowsum, int M, int K,
                                                                const uint8_t* __restrict__ Wp,
                                                                const float* __restrict__ w_scale, int N,
                                                                uint32_t epi_flags, const float* aux, float* Y,
-                                                               int32_t* __restrict__ acc_out) {
+                                                               int32_t* __restrict__ acc_out,
+                                                               const uint8_t* __restrict__ Wg,
+                                                               const float* __restrict__ g_scale) {
+    static_assert(!GATED || CT == 2, "a gated tile pairs one up and one gate tile");
     constexpr int NWV = kBatchWaves;
     constexpr int NT = NWV * kWave;
-    constexpr int COLS = 16 * CT;
-    constexpr int GROUPS = 16 * MT * COLS / 4;          // epilogue: 4 adjacent outputs of one row per group
+    constexpr int COLS = 16 * CT;                        // accumulated columns per workgroup
+    constexpr int OCOLS = GATED ? 16 : COLS;             // output columns per workgroup
+    constexpr int GROUPS = 16 * MT * OCOLS / 4;         // epilogue: 4 adjacent outputs of one row per group
     constexpr int EPG = (GROUPS + NT - 1) / NT;          // groups per thread
     constexpr int RING = NS * MT * kTileBytes;           // bytes per wave
     static_assert(NWV * 16 * MT * COLS * 4 <= NWV * RING, "partial tiles fit in the rings");
     __shared__ __align__(1024) int8_t lds[NWV * RING];   // activation rings, then partial tiles [NWV][M][COLS]
     __shared__ float sdq[16 * MT];  // per-row dequantisation factor (x_scale * w_scale) / 127
+    __shared__ float sdqg[GATED ? 16 * MT : 1];  // the same with the gate's scale
     __shared__ int srs[16 * MT];
 
     const int lane = threadIdx.x % kWave;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int fr = lane & 15;  // activation row of the A operand / output column of the tile
     const int fg = lane >> 4;  // k group
-    const int n0 = blockIdx.x * COLS;
+    const int n0 = blockIdx.x * OCOLS;
     const int C = K / 64;
     const int nq = (C + 3) / 4;
     const float ws = *w_scale;
+    const float gws = GATED ? *g_scale : 0.0f;
 
     // ---- the epilogue's operands, loaded first: the rows' scales and sums
     // (thread t < M takes row t) and the residual or multiplier of every
@@ -350,11 +359,11 @@ __global__ __launch_bounds__(kBatchWaves* kWave) void k_batch(const int8_t* __re
     const int p_rs = buf_load4i(make_rsrc(x_rowsum, (uint32_t)M * 4u), (uint32_t)threadIdx.x * 4u);
     float e_aux[EPG][4];
     {
-        const Rsrc rx = make_rsrc(aux, (epi_flags & (kEpiResidual | kEpiMul)) ? 0x7FFFFFFFu : 0u);
+        const Rsrc rx = make_rsrc(aux, (!GATED && (epi_flags & (kEpiResidual | kEpiMul))) ? 0x7FFFFFFFu : 0u);
 #pragma unroll
         for (int e = 0; e < EPG; ++e) {
             const int g = threadIdx.x + e * NT;
-            const int m = g / (COLS / 4), n = n0 + 4 * (g % (COLS / 4));
+            const int m = g / (OCOLS / 4), n = n0 + 4 * (g % (OCOLS / 4));
 #pragma unroll
             for (int j = 0; j < 4; ++j)
                 e_aux[e][j] = buf_load4f(rx, (m < M && n + j < N) ? (uint32_t)((int64_t)m * N + n + j) * 4u : kOob);
@@ -365,11 +374,12 @@ __global__ __launch_bounds__(kBatchWaves* kWave) void k_batch(const int8_t* __re
     int rows[CT];  // rows of each column tile's 16-row weight tile (the last may have fewer)
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) {
-        const int r0 = n0 + 16 * ct;
+        const int r0 = GATED ? n0 : n0 + 16 * ct;
+        const uint8_t* W = GATED && ct == 1 ? Wg : Wp;
         // readfirstlane: a clamp the compiler leaves in a VGPR would make the
         // descriptor look divergent (and every load a waterfall loop)
         rows[ct] = __builtin_amdgcn_readfirstlane(N - r0 < 0 ? 0 : (N - r0 < 16 ? N - r0 : 16));
-        rw[ct] = make_rsrc(Wp + (int64_t)(rows[ct] > 0 ? r0 : 0) * (K / 4), (uint32_t)rows[ct] * (uint32_t)(K / 4));
+        rw[ct] = make_rsrc(W + (int64_t)(rows[ct] > 0 ? r0 : 0) * (K / 4), (uint32_t)rows[ct] * (uint32_t)(K / 4));
     }
     // DMA lane offsets: lane L moves row 8h + (L >> 3) of token tile t, 16-byte
     // chunk (L & 7) ^ (row / 2) of the 128-byte span (h = half of the tile)
@@ -403,6 +413,7 @@ __global__ __launch_bounds__(kBatchWaves* kWave) void k_batch(const int8_t* __re
     // done with its own) -> sum over the waves in index order
     if ((int)threadIdx.x < 16 * MT) {
         sdq[threadIdx.x] = (p_xs * ws) / 127.0f;
+        if constexpr (GATED) sdqg[threadIdx.x] = (p_xs * gws) / 127.0f;
         srs[threadIdx.x] = p_rs;
     }
     __syncthreads();
@@ -419,21 +430,26 @@ __global__ __launch_bounds__(kBatchWaves* kWave) void k_batch(const int8_t* __re
     __syncthreads();
     // all partial-tile reads first (16 bytes: 4 adjacent columns), then the
     // arithmetic; a group past M reads row M - 1 and stores nothing
-    int4 part[EPG][NWV];
+    int4 part[EPG][NWV], partg[GATED ? EPG : 1][NWV];
 #pragma unroll
     for (int e = 0; e < EPG; ++e) {
         const int g = threadIdx.x + e * NT;
-        const int m = g / (COLS / 4) < M ? g / (COLS / 4) : M - 1;
-        const int c = 4 * (g % (COLS / 4));
+        const int m = g / (OCOLS / 4) < M ? g / (OCOLS / 4) : M - 1;
+        const int c = 4 * (g % (OCOLS / 4));
 #pragma unroll
         for (int q = 0; q < NWV; ++q) part[e][q] = *reinterpret_cast<const int4*>(red + (q * M + m) * COLS + c);
+        if constexpr (GATED) {
+#pragma unroll
+            for (int q = 0; q < NWV; ++q)
+                partg[e][q] = *reinterpret_cast<const int4*>(red + (q * M + m) * COLS + 16 + c);
+        }
     }
     const bool vec = (N & 3) == 0;  // rows start 16-byte aligned
 #pragma unroll
     for (int e = 0; e < EPG; ++e) {
         const int g = threadIdx.x + e * NT;
-        const int m = g / (COLS / 4);
-        const int n = n0 + 4 * (g % (COLS / 4));
+        const int m = g / (OCOLS / 4);
+        const int n = n0 + 4 * (g % (OCOLS / 4));
         if (m < M && n < N) {
             int a[4] = {0, 0, 0, 0};
 #pragma unroll
@@ -446,17 +462,38 @@ __global__ __launch_bounds__(kBatchWaves* kWave) void k_batch(const int8_t* __re
             const int rsum = srs[m];
             const float dq = sdq[m];
             float y[4];
+            if constexpr (GATED) {
+                int ag[4] = {0, 0, 0, 0};
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                a[j] -= rsum;
-                float v = (float)a[j] * dq;
-                if (epi_flags & kEpiRelu2) {
-                    const float tt = v > 0.0f ? v : 0.0f;
-                    v = tt * tt;
+                for (int q = 0; q < NWV; ++q) {
+                    ag[0] += partg[e][q].x;
+                    ag[1] += partg[e][q].y;
+                    ag[2] += partg[e][q].z;
+                    ag[3] += partg[e][q].w;
                 }
-                if (epi_flags & kEpiMul) v = v * e_aux[e][j];
-                else if (epi_flags & kEpiResidual) v = v + e_aux[e][j];
-                y[j] = v;
+                const float dqg = sdqg[m];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    // ReLU^2(gate) * up, in that order
+                    a[j] -= rsum;
+                    const float u = (float)a[j] * dq;
+                    float t = (float)(ag[j] - rsum) * dqg;
+                    t = t > 0.0f ? t : 0.0f;
+                    y[j] = (t * t) * u;
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    a[j] -= rsum;
+                    float v = (float)a[j] * dq;
+                    if (epi_flags & kEpiRelu2) {
+                        const float tt = v > 0.0f ? v : 0.0f;
+                        v = tt * tt;
+                    }
+                    if (epi_flags & kEpiMul) v = v * e_aux[e][j];
+                    else if (epi_flags & kEpiResidual) v = v + e_aux[e][j];
+                    y[j] = v;
+                }
             }
             const int64_t o = (int64_t)m * N + n;
             if (vec) {  // n + 3 < N as well
@@ -551,24 +588,25 @@ bool gemv_supported(int64_t M, int64_t K, int64_t N) {
     return M * N < (1LL << 29) && batch_shape(M, K, N, q, mt, ct);
 }
 
-template <int MT, int CT, int Q>
+template <int MT, int CT, int Q, bool G = false>
 static hipError_t go_batch(const int8_t* Xq, const float* xs, const int32_t* rs, int64_t M, int64_t K,
                            const uint8_t* packed, const float* ws, int64_t N, Epi epi, float* Y, int32_t* acc_out,
-                           hipStream_t s) {
+                           hipStream_t s, const uint8_t* gate = nullptr, const float* gate_scale = nullptr) {
     constexpr int NS = MT == 1 ? 4 : MT == 2 ? 3 : 2;
-    const unsigned blocks = (unsigned)((N + 16 * CT - 1) / (16 * CT));
-    hipLaunchKernelGGL((k_batch<MT, CT, NS, Q>), dim3(blocks), dim3(kBatchWaves * kWave), 0, s, Xq, xs, rs, (int)M,
-                       (int)K, packed, ws, (int)N, epi.flags, epi.aux, Y, acc_out);
+    const int64_t cols = G ? 16 : 16 * CT;
+    const unsigned blocks = (unsigned)((N + cols - 1) / cols);
+    hipLaunchKernelGGL((k_batch<MT, CT, NS, Q, G>), dim3(blocks), dim3(kBatchWaves * kWave), 0, s, Xq, xs, rs, (int)M,
+                       (int)K, packed, ws, (int)N, epi.flags, epi.aux, Y, acc_out, gate, gate_scale);
     return hipGetLastError();
 }
 
-template <int MT, int CT>
+template <int MT, int CT, bool G = false>
 static hipError_t go_batch_q(int q, const int8_t* Xq, const float* xs, const int32_t* rs, int64_t M, int64_t K,
                              const uint8_t* packed, const float* ws, int64_t N, Epi epi, float* Y, int32_t* acc_out,
-                             hipStream_t s) {
+                             hipStream_t s, const uint8_t* gate = nullptr, const float* gate_scale = nullptr) {
     switch (q) {
 #define BL_BQ(Q) \
-    case Q: return go_batch<MT, CT, Q>(Xq, xs, rs, M, K, packed, ws, N, epi, Y, acc_out, s);
+    case Q: return go_batch<MT, CT, Q, G>(Xq, xs, rs, M, K, packed, ws, N, epi, Y, acc_out, s, gate, gate_scale);
         BL_BQ(1) BL_BQ(2) BL_BQ(3) BL_BQ(4) BL_BQ(5) BL_BQ(6) BL_BQ(7) BL_BQ(8)
 #undef BL_BQ
         default: return hipErrorInvalidValue;
@@ -586,6 +624,22 @@ hipError_t launch_gemv(const int8_t* Xq, const float* xs, const int32_t* rs, int
         case 5: return go_batch_q<2, 2>(q, Xq, xs, rs, M, K, packed, ws, N, epi, Y, acc_out, s);
         case 8: return go_batch_q<4, 1>(q, Xq, xs, rs, M, K, packed, ws, N, epi, Y, acc_out, s);
         case 9: return go_batch_q<4, 2>(q, Xq, xs, rs, M, K, packed, ws, N, epi, Y, acc_out, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+// The gated pair in one launch: one workgroup per 16 output rows, streaming
+// those rows of up and of gate against one pass over the activations.
+hipError_t launch_gemv_gated(const int8_t* Xq, const float* xs, const int32_t* rs, int64_t M, int64_t K,
+                             const uint8_t* up, const float* up_scale, const uint8_t* gate, const float* gate_scale,
+                             int64_t N, float* Y, hipStream_t s) {
+    int q, mt, ct;
+    if (!batch_shape(M, K, N, q, mt, ct)) return hipErrorInvalidValue;
+    const Epi none{0u, nullptr};
+    switch (mt) {
+        case 1: return go_batch_q<1, 2, true>(q, Xq, xs, rs, M, K, up, up_scale, N, none, Y, nullptr, s, gate, gate_scale);
+        case 2: return go_batch_q<2, 2, true>(q, Xq, xs, rs, M, K, up, up_scale, N, none, Y, nullptr, s, gate, gate_scale);
+        case 4: return go_batch_q<4, 2, true>(q, Xq, xs, rs, M, K, up, up_scale, N, none, Y, nullptr, s, gate, gate_scale);
         default: return hipErrorInvalidValue;
     }
 }

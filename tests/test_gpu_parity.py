@@ -486,11 +486,12 @@ def gated_layer_teacher_forced(h_in, G, O, pre=True, residual=True):
     return host(h), flips
 
 
-@pytest.mark.parametrize("M", [1, 3, 20])
+@pytest.mark.parametrize("M", [1, 3, 8, 20, 33, 64])
 def test_ffn_gated_block(M):
     """Gated FFN layers (ReLU^2(gate) * up): teacher-forced stage by stage,
-    then the stack call (fused decode kernels for M <= 4, staged kernels
-    otherwise) exactly equal to the staged calls, twice in a row."""
+    then the stack call (gate and up in one launch: the decode kernel for
+    M <= 4, the batched kernel up to 64, then the staged kernels) exactly
+    equal to the staged calls, twice in a row."""
     log(f"[ffn gated] M={M}")
     rng = np.random.default_rng(1900 + M)
     H, F, L = 256, 640, 2
@@ -509,6 +510,21 @@ def test_ffn_gated_block(M):
         ref = oracle.ffn_layer_gated(ref, O["q_gate"], O["gamma_gate"], O["q_up"], O["gamma_up"], O["q_down"],
                                      O["gamma_down"], pre_gain=O["pre_gain"], sub_gain=O["sub_gain"])
     assert np.abs(host(hs) - ref).max() <= 1e-3 * np.abs(ref).max()
+
+
+@pytest.mark.parametrize("M", [16, 64])
+def test_ffn_gated_model_width(M):
+    """A gated layer at hidden 2560 / intermediate 6912 with gains, pre-norm
+    and residual, M = 16 and 64 (one batched launch streams gate and up):
+    exactly the staged calls, and the staged calls against the oracle."""
+    log(f"[ffn gated, model width] M={M}")
+    rng = np.random.default_rng(2700 + M)
+    gl, ol = to_gpu_gated(gated_layers_np(rng, 1, synth.HIDDEN, synth.FFN, gains=True))
+    h0 = synth.activations(rng, M, synth.HIDDEN)
+    h, _ = gated_layer_teacher_forced(h0, gl[0], ol[0])
+    hs = dev(h0)
+    bl.FFNStack(gl, synth.HIDDEN, synth.FFN, M, DEV)(hs)
+    assert_exact(host(hs), h, "gated stack vs staged calls")
 
 
 # ------------------------------------------------------------------ forward from latent weights
