@@ -68,8 +68,8 @@ TRAFFIC_KERNELS = {
     "decode_up_m1": ("k_decode<4, 4, false, 3>", 432, ("gemv.hip", "bl_device.h")),
     "gemm_up_m4096": ("k_gemm_pipe<256, 256, 2, 4, 4, 1>", 432, ("gemm.hip", "bl_device.h")),
     "gemm_down_m4096": ("k_gemm_pipe<256, 160, 4, 2, 4, 1>", 256, ("gemm.hip", "bl_device.h")),
-    "batch_gate_m64": ("k_batch<4, 2, 2, 3>", 216, ("gemv.hip", "bl_device.h")),
-    "batch_down_m64": ("k_batch<4, 1, 2, 7>", 160, ("gemv.hip", "bl_device.h")),
+    "batch_gate_m64": ("k_batch<4, 2, 2, 3, false>", 216, ("gemv.hip", "bl_device.h")),
+    "batch_down_m64": ("k_batch<4, 1, 2, 7, false>", 160, ("gemv.hip", "bl_device.h")),
 }
 CALIB_BYTES = 256 << 20   # the calibration kernel reads and writes 256 MiB
 PMC_CMDS = [
