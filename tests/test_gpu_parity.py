@@ -540,7 +540,8 @@ def latent_weights(rng, N, K, dtype):
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("M,K,N,epi", [(1, 256, 130, "relu2"), (3, 2560, 6912, None), (8, 320, 512, "residual"),
-                                        (70, 512, 200, "mul"), (300, 1024, 272, "relu2")])
+                                        (70, 512, 200, "mul"), (300, 1024, 272, "relu2"), (2, 512, 96, "rms"),
+                                        (40, 768, 160, "rms")])
 def test_latent_forward(M, K, N, epi, dtype):
     """BitLinear from latent fp32 / bf16 weights (ternarised inside the call)
     through the fused decode (M <= 4), batched and GEMM paths: gamma_w and Y
@@ -552,15 +553,21 @@ def test_latent_forward(M, K, N, epi, dtype):
     Wt, W = latent_weights(rng, N, K, dtype)
     X = synth.activations(rng, M, K, outliers=True)
     A = synth.activations(rng, M, N)
+    G = synth.gains(rng, K)
     kw = dict(relu2=epi == "relu2", residual=dev(A) if epi == "residual" else None,
-              mul_by=dev(A) if epi == "mul" else None)
+              mul_by=dev(A) if epi == "mul" else None, rmsnorm=epi == "rms",
+              norm_gain=dev(G) if epi == "rms" else None)
     gw_t = torch.empty(1, dtype=torch.float32, device=DEV)
     y = bl.latent_forward(dev(X), Wt, w_scale_out=gw_t, **kw)
     p, s, q, gw = check_pack(W, "latent forward")
     assert host(gw_t)[0] == host(s)[0], "gamma_w of the latent forward vs the packer"
     y2 = bl.quant_forward(dev(X), p, s, **kw)
     assert_exact(host(y), host(y2), "latent forward vs pack + quant_forward")
-    xq, gx, _ = oracle.quant_act(X)
+    z = oracle.rmsnorm(X, G) if epi == "rms" else X
+    if epi == "rms":  # the GPU's own quantised rows decide near-ties (same precision, explained flips)
+        xq_g, xs_g, rs_g = bl.quant_act(dev(X), rmsnorm=True, norm_gain=dev(G))
+        check_requant(z, host(xq_g), host(xs_g), host(rs_g), "latent forward rmsnorm quant")
+    xq, gx, _ = oracle.quant_act(z)
     acc = oracle.int_matmul(xq, q)
     want = oracle.dequant(acc, gx, gw)
     if epi == "relu2":
