@@ -527,6 +527,53 @@ def test_ffn_gated_model_width(M):
     assert_exact(host(hs), h, "gated stack vs staged calls")
 
 
+# ------------------------------------------------------------------ seeded shape sweep
+
+def _sweep_cases(n=40, seed=6100):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        M = int(rng.choice([1, 2, 3, 4, 5, 8, 13, 16, 17, 31, 33, 48, 64, 65, 100, 129, 200, 300]))
+        K = 64 * int(rng.integers(1, 65))          # 64 .. 4096
+        N = int(rng.integers(1, 3001))
+        epi = str(rng.choice(["none", "relu2", "residual", "mul", "relu2+residual"]))
+        cases.append((i, M, K, N, epi))
+    return cases
+
+
+@pytest.mark.parametrize("i,M,K,N,epi", _sweep_cases())
+def test_forward_shape_sweep(i, M, K, N, epi):
+    """40 seeded shapes over the decode (M <= 4), batched (M <= 64) and GEMM
+    paths, ragged N, K up to 4096, with the epilogue flags: int32 acc bit-exact
+    and Y within 1e-5 of the oracle; quant_forward equal to quant_act +
+    forward bit for bit."""
+    log(f"[sweep {i}] M={M} K={K} N={N} epi={epi}")
+    rng = np.random.default_rng(6200 + i)
+    X = synth.activations(rng, M, K, outliers=bool(i % 2))
+    W = synth.weights(rng, N, K)
+    A = synth.activations(rng, M, N)
+    p, s, q, gw = check_pack(W, f"sweep {i}")
+    relu2 = "relu2" in epi
+    res = dev(A) if "residual" in epi else None
+    mul = dev(A) if epi == "mul" else None
+    xq, xs, rs = bl.quant_act(dev(X))
+    out = bl.forward(xq, xs, p, s, x_rowsum=rs, relu2=relu2, residual=res, mul_by=mul, want_acc=True)
+    oq, og, _ = oracle.quant_act(X)
+    assert_exact(host(xq), oq, "sweep xq")
+    acc = oracle.int_matmul(oq, q)
+    assert_exact(host(out["acc"]), acc, "sweep acc")
+    want = oracle.dequant(acc, og, gw)
+    if relu2:
+        want = oracle.relu2(want)
+    if "residual" in epi:
+        want = oracle.add(A.copy(), want)
+    elif epi == "mul":
+        want = oracle.mul(want, A)
+    assert_y_close(host(out["y"]), want, "sweep y")
+    y2 = bl.quant_forward(dev(X), p, s, relu2=relu2, residual=res, mul_by=mul)
+    assert_exact(host(y2), host(out["y"]), "sweep quant_forward vs quant_act + forward")
+
+
 # ------------------------------------------------------------------ forward from latent weights
 
 def latent_weights(rng, N, K, dtype):
