@@ -574,6 +574,39 @@ def test_forward_shape_sweep(i, M, K, N, epi):
     assert_exact(host(y2), host(out["y"]), "sweep quant_forward vs quant_act + forward")
 
 
+def _ffn_sweep_cases(n=12, seed=6300):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        M = int(rng.choice([1, 2, 4, 6, 19, 40, 64, 80, 150]))
+        H = 64 * int(rng.integers(1, 25))
+        F = 64 * int(rng.integers(1, 25))
+        out.append((i, M, H, F, bool(rng.integers(0, 2)), bool(rng.integers(0, 2)), bool(rng.integers(0, 2))))
+    return out
+
+
+@pytest.mark.parametrize("i,M,H,F,gated,pre,residual", _ffn_sweep_cases())
+def test_ffn_shape_sweep(i, M, H, F, gated, pre, residual):
+    """12 seeded FFN layer shapes, plain and gated, with and without pre-norm
+    and residual, across the decode, batched and GEMM paths: the stack call
+    exactly equals the staged calls, which are checked stage by stage
+    against the oracle."""
+    log(f"[ffn sweep {i}] M={M} H={H} F={F} gated={gated} pre={pre} residual={residual}")
+    rng = np.random.default_rng(6400 + i)
+    if gated:
+        gl, ol = to_gpu_gated(gated_layers_np(rng, 1, H, F, gains=True))
+    else:
+        gl, ol = to_gpu_layers(ffn_layers_np(rng, 1, H, F, gains=True))
+    h0 = synth.activations(rng, M, H)
+    if gated:
+        h, _ = gated_layer_teacher_forced(h0, gl[0], ol[0], pre=pre, residual=residual)
+    else:
+        h, _ = layer_teacher_forced(h0, gl[0], ol[0], M, pre=pre, residual=residual)
+    hs = dev(h0)
+    bl.ffn_forward(gl, hs, pre_norm=pre, residual=residual)
+    assert_exact(host(hs), h, "ffn sweep: stack vs staged calls")
+
+
 # ------------------------------------------------------------------ forward from latent weights
 
 def latent_weights(rng, N, K, dtype):
