@@ -39,7 +39,9 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 // depth for K, at most QMAX by the plan below).  GATED: a second matrix Wg
 // (the gate) of the same shape is streamed by the same lanes against the
 // same quantised rows, and the output is ReLU^2(gate) * up (Wp is up).
-template <int NWV, int QMAX, bool GATED, int NV>
+// CT > 1 (very tall matrices): the workgroup owns CT adjacent 16-row tiles,
+// so one quantisation of the rows serves 16 CT outputs.
+template <int NWV, int QMAX, bool GATED, int NV, int CT = 1>
 __global__ __launch_bounds__(NWV* kWave) void k_decode(const float* __restrict__ X, int M, int K, int rmsnorm,
                                                         const float* __restrict__ gain, float eps,
                                                         const uint8_t* __restrict__ Wp,
@@ -47,7 +49,10 @@ __global__ __launch_bounds__(NWV* kWave) void k_decode(const float* __restrict__
                                                         uint32_t epi_flags, const float* aux, float* Y,
                                                         const uint8_t* __restrict__ Wg,
                                                         const float* __restrict__ g_scale) {
+    static_assert(!GATED || CT == 1, "a gated launch streams one tile of each matrix");
+    static_assert(4 * 16 * CT <= NWV * kWave, "one epilogue thread per output");
     constexpr int NT = NWV * kWave;
+    constexpr int COLS = 16 * CT;
     extern __shared__ __align__(16) int8_t lds[];  // [xq: M <= 4 rows of K] [partials]
     __shared__ double dslot[NWV];
     __shared__ float fslot[NWV], fslot2[NWV];
@@ -58,7 +63,7 @@ __global__ __launch_bounds__(NWV* kWave) void k_decode(const float* __restrict__
     const int wave = threadIdx.x / kWave;
     const int fr = lane & 15;      // column (output row) of the tile / activation row of the A operand
     const int fg = lane >> 4;      // k group
-    const int n0 = blockIdx.x * 16;
+    const int n0 = blockIdx.x * COLS;
     const int C = K / 64;          // 64-weight chunks per row
     const int nq = (C + 3) / 4;    // chunk quads
     const float ws = *w_scale;
@@ -71,15 +76,19 @@ __global__ __launch_bounds__(NWV* kWave) void k_decode(const float* __restrict__
     const bool has_gain = rmsnorm != 0 && gain != nullptr;
     quant_row_load<NT, NV>(X, has_gain ? gain : nullptr, K, v, gv);
     __builtin_amdgcn_sched_barrier(0);  // keep these loads ahead of the weights'
-    uint4 w[QMAX];
-    {
-        const int rows = N - n0 < 16 ? N - n0 : 16;
-        const Rsrc rw = make_rsrc(Wp + (int64_t)n0 * (K / 4), (uint32_t)rows * (uint32_t)(K / 4));
+    uint4 w[CT][QMAX];
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+        const int r0 = n0 + 16 * ct;
+        // readfirstlane: a clamp left in a VGPR would make the descriptor look
+        // divergent (and every load a waterfall loop)
+        const int rows = __builtin_amdgcn_readfirstlane(N - r0 < 0 ? 0 : (N - r0 < 16 ? N - r0 : 16));
+        const Rsrc rw = make_rsrc(Wp + (int64_t)(rows > 0 ? r0 : 0) * (K / 4), (uint32_t)rows * (uint32_t)(K / 4));
 #pragma unroll
         for (int i = 0; i < QMAX; ++i) {
             const int s = wave + i * NWV;
             const int c = 4 * s + fg;
-            w[i] = buf_load16(rw, (s < nq && c < C) ? (uint32_t)(c * rows + fr) * 16u : kOob);
+            w[ct][i] = buf_load16(rw, (s < nq && c < C) ? (uint32_t)(c * rows + fr) * 16u : kOob);
         }
     }
     uint4 wg[GATED ? QMAX : 1];
@@ -93,8 +102,8 @@ __global__ __launch_bounds__(NWV* kWave) void k_decode(const float* __restrict__
             wg[i] = buf_load16(rg, (s < nq && c < C) ? (uint32_t)(c * rows + fr) * 16u : kOob);
         }
     }
-    const int e_m = threadIdx.x / 16, e_n = n0 + (int)(threadIdx.x % 16);
-    const bool e_ok = (int)threadIdx.x < M * 16 && e_n < N;
+    const int e_m = threadIdx.x / COLS, e_n = n0 + (int)(threadIdx.x % COLS);
+    const bool e_ok = (int)threadIdx.x < M * COLS && e_n < N;
     const float e_res = buf_load4f(make_rsrc(aux, (epi_flags & (kEpiResidual | kEpiMul)) ? 0x7FFFFFFFu : 0u),
                                    e_ok ? (uint32_t)((int64_t)e_m * N + e_n) * 4u : kOob);
 
@@ -120,19 +129,24 @@ __global__ __launch_bounds__(NWV* kWave) void k_decode(const float* __restrict__
     // ---- contraction.  A chunk past the row end has zero weights (its load
     // was out of range), so its activation offset is clamped to 0 and it adds
     // nothing.
-    v4i acc = v4i{0, 0, 0, 0}, accg = v4i{0, 0, 0, 0};
+    v4i acc[CT], accg = v4i{0, 0, 0, 0};
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) acc[ct] = v4i{0, 0, 0, 0};
 #pragma unroll
     for (int i = 0; i < QMAX; ++i) {
         const int s = wave + i * NWV;
         if (s < nq) {
             const int c = 4 * s + fg;
             const int koff = c < C ? 64 * c : 0;
-            const uint32_t wd[4] = {w[i].x, w[i].y, w[i].z, w[i].w};
 #pragma unroll
             for (int d = 0; d < 4; ++d) {
-                const v4i b = v4i{codes4(wd[d], 0), codes4(wd[d], 1), codes4(wd[d], 2), codes4(wd[d], 3)};
                 const v4i a = *reinterpret_cast<const v4i*>(arow + koff + 16 * d);
-                acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, acc, 0, 0, 0);
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) {
+                    const uint32_t wd = d == 0 ? w[ct][i].x : d == 1 ? w[ct][i].y : d == 2 ? w[ct][i].z : w[ct][i].w;
+                    const v4i b = v4i{codes4(wd, 0), codes4(wd, 1), codes4(wd, 2), codes4(wd, 3)};
+                    acc[ct] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, acc[ct], 0, 0, 0);
+                }
                 if constexpr (GATED) {
                     const uint32_t g4 = d == 0 ? wg[i].x : d == 1 ? wg[i].y : d == 2 ? wg[i].z : wg[i].w;
                     const v4i bg = v4i{codes4(g4, 0), codes4(g4, 1), codes4(g4, 2), codes4(g4, 3)};
@@ -144,22 +158,23 @@ __global__ __launch_bounds__(NWV* kWave) void k_decode(const float* __restrict__
 
     // ---- per-wave partial tiles -> LDS (a region of its own) -> epilogue,
     // summing the waves in index order
-    int* red = reinterpret_cast<int*>(lds + 4 * K);  // [NWV][16 tokens][16], gate after it
+    int* red = reinterpret_cast<int*>(lds + 4 * K);  // [NWV][16 tokens][COLS], gate after it
     int* redg = red + NWV * 16 * 16;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         const int m = 4 * fg + r;
         if (m < M) {
-            red[(wave * 16 + m) * 16 + fr] = acc[r];
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) red[(wave * 16 + m) * COLS + 16 * ct + fr] = acc[ct][r];
             if constexpr (GATED) redg[(wave * 16 + m) * 16 + fr] = accg[r];
         }
     }
     __syncthreads();
     if (e_ok) {
-        const int m = e_m, col = (int)threadIdx.x % 16;
+        const int m = e_m, col = (int)threadIdx.x % COLS;
         int a = 0, ag = 0;
 #pragma unroll
-        for (int q = 0; q < NWV; ++q) a += red[(q * 16 + m) * 16 + col];
+        for (int q = 0; q < NWV; ++q) a += red[(q * 16 + m) * COLS + col];
         if constexpr (GATED) {
 #pragma unroll
             for (int q = 0; q < NWV; ++q) ag += redg[(q * 16 + m) * 16 + col];
@@ -531,17 +546,22 @@ bool plan(int64_t K, Plan& p) {
     return true;
 }
 
-template <int NWV, int Q, bool G, int NV>
+template <int NWV, int Q, bool G, int NV, int CT = 1>
 hipError_t go_decode(const float* X, int64_t M, int64_t K, bool rms, const float* gain, float eps,
                      const uint8_t* packed, const float* ws, int64_t N, uint32_t epi, const float* aux, float* Y,
                      const uint8_t* gate, const float* gate_scale, hipStream_t s) {
-    const unsigned blocks = (unsigned)((N + 15) / 16);
-    const size_t red = (size_t)NWV * 16 * 16 * sizeof(int) * (G ? 2 : 1);
+    const unsigned blocks = (unsigned)((N + 16 * CT - 1) / (16 * CT));
+    const size_t red = (size_t)NWV * 16 * 16 * sizeof(int) * (G ? 2 : CT);
     const size_t lds = 4 * (size_t)K + red;
-    hipLaunchKernelGGL((k_decode<NWV, Q, G, NV>), dim3(blocks), dim3(NWV * kWave), lds, s, X, (int)M, (int)K,
+    hipLaunchKernelGGL((k_decode<NWV, Q, G, NV, CT>), dim3(blocks), dim3(NWV * kWave), lds, s, X, (int)M, (int)K,
                        rms ? 1 : 0, gain, eps, packed, ws, (int)N, epi, aux, Y, gate, gate_scale);
     return hipGetLastError();
 }
+
+// Very tall matrices (at least 2048 tiles of 16 rows, eight per CU): four
+// tiles per workgroup, so the per-workgroup quantisation is amortised over
+// 64 rows while thousands of workgroups remain.
+constexpr int64_t kTallTiles = 2048;
 
 // The quantiser's depth for K (which the plan bounds by qmax) picks NV.
 template <bool G>
@@ -550,9 +570,12 @@ hipError_t go_decode_plan(const Plan& p, const float* X, int64_t M, int64_t K, b
                           const float* aux, float* Y, hipStream_t s, const uint8_t* gate = nullptr,
                           const float* gate_scale = nullptr) {
     const int nv = quant_depth(K);
-#define BL_DEC(NWV, Q, NV)                                                                                 \
-    if (p.nw == NWV && p.qmax == Q && nv == NV)                                                            \
-        return go_decode<NWV, Q, G, NV>(X, M, K, rms, gain, eps, packed, ws, N, epi, aux, Y, gate, gate_scale, s);
+    const bool tall = !G && (N + 15) / 16 >= kTallTiles;
+#define BL_DEC(NWV, Q, NV)                                                                                     \
+    if (p.nw == NWV && p.qmax == Q && nv == NV)                                                                \
+        return tall ? go_decode<NWV, Q, G, NV, G ? 1 : 4>(X, M, K, rms, gain, eps, packed, ws, N, epi, aux, Y, gate, \
+                                                          gate_scale, s)                                      \
+                    : go_decode<NWV, Q, G, NV>(X, M, K, rms, gain, eps, packed, ws, N, epi, aux, Y, gate, gate_scale, s);
     BL_DEC(4, 2, 1)
     BL_DEC(4, 2, 2)
     BL_DEC(4, 4, 3)

@@ -527,6 +527,38 @@ def test_ffn_gated_model_width(M):
     assert_exact(host(hs), h, "gated stack vs staged calls")
 
 
+# ------------------------------------------------------------------ very tall matrices at decode
+
+@pytest.mark.parametrize("M,K,N,epi", [(1, 2560, 40008, "relu2"), (3, 256, 33000, "residual"),
+                                        (4, 512, 32768, "none"), (2, 1024, 36880, "mul")])
+def test_decode_tall(M, K, N, epi):
+    """At 2048 or more 16-row tiles the fused quantise + BitLinear launch
+    gives each workgroup four tiles (one quantisation for 64 rows), the last
+    group ragged or partly empty: Y against the oracle, and bit for bit
+    against the two-step path (quantiser + batched kernel)."""
+    log(f"[decode tall] M={M} K={K} N={N} epi={epi}")
+    rng = np.random.default_rng(7000 + M + N)
+    X = synth.activations(rng, M, K, outliers=True)
+    W = synth.weights(rng, N, K)
+    A = synth.activations(rng, M, N)
+    p, s, q, gw = check_pack(W, "decode tall")
+    kw = dict(relu2=epi == "relu2", residual=dev(A) if epi == "residual" else None,
+              mul_by=dev(A) if epi == "mul" else None)
+    y = bl.quant_forward(dev(X), p, s, **kw)
+    xq, gx, _ = oracle.quant_act(X)
+    want = oracle.dequant(oracle.int_matmul(xq, q), gx, gw)
+    if epi == "relu2":
+        want = oracle.relu2(want)
+    elif epi == "residual":
+        want = oracle.add(A.copy(), want)
+    elif epi == "mul":
+        want = oracle.mul(want, A)
+    assert_y_close(host(y), want, "tall decode y")
+    a, b, r = bl.quant_act(dev(X))
+    two = bl.forward(a, b, p, s, x_rowsum=r, **kw)
+    assert_exact(host(y), host(two["y"]), "tall decode vs quantiser + batched kernel")
+
+
 # ------------------------------------------------------------------ seeded shape sweep
 
 def _sweep_cases(n=40, seed=6100):
