@@ -65,7 +65,7 @@ def traffic_from_profile(kernel_key, sources):
 # Kernels whose HBM traffic is taken from rocprofv3 counters: key -> (kernel
 # name prefix in the trace, workgroups, sources whose hash the figures belong to)
 TRAFFIC_KERNELS = {
-    "decode_up_m1": ("k_decode<4, 4, false, 3>", 432, ("gemv.hip", "bl_device.h")),
+    "decode_up_m1": ("k_decode<4, 4, false, 3, 1>", 432, ("gemv.hip", "bl_device.h")),
     "gemm_up_m4096": ("k_gemm_pipe<256, 256, 2, 4, 4, 1>", 432, ("gemm.hip", "bl_device.h")),
     "gemm_down_m4096": ("k_gemm_pipe<256, 160, 4, 2, 4, 1>", 256, ("gemm.hip", "bl_device.h")),
     "batch_gate_m64": ("k_batch<4, 2, 2, 3, false>", 216, ("gemv.hip", "bl_device.h")),
@@ -636,7 +636,7 @@ def main():
     traffic = traffic_from_profile("decode_up_m1", ["gemv.hip", "bl_device.h"])
     roofline = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": "k_decode<4,4,false,3> (absmax quant + up BitLinear + ReLU^2, M=1, K=2560, N=6912)",
+                "kernel": "k_decode<4,4,false,3,1> (absmax quant + up BitLinear + ReLU^2, M=1, K=2560, N=6912)",
                 "bytes_per_launch": PACKED_BYTES_MATRIX, "us_per_launch": round(gemv_s * 1e6, 3),
                 "down_us_per_launch": round(gemv_dn_s * 1e6, 3)}
     del layers, stacks, ups, dns, gstacks
