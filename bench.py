@@ -72,10 +72,12 @@ TRAFFIC_KERNELS = {
     "batch_down_m64": ("k_batch<4, 1, 2, 7, false>", 160, ("gemv.hip", "bl_device.h")),
 }
 CALIB_BYTES = 256 << 20   # the calibration kernel reads and writes 256 MiB
+# The three commands behind profiles/traffic.json ({fetch} and {write} are the
+# counter output directories, the two arguments of --traffic-from).
 PMC_CMDS = [
-    "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o p -- python3 bench.py --pmc-drive",
-    "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o p -- python3 bench.py --pmc-drive",
-    "python3 bench.py --traffic-from gpurun_out/pmc_fetch gpurun_out/pmc_write",
+    "rocprofv3 --pmc FETCH_SIZE --output-format csv -d {fetch} -o p -- python3 bench.py --pmc-drive",
+    "rocprofv3 --pmc WRITE_SIZE --output-format csv -d {write} -o p -- python3 bench.py --pmc-drive",
+    "python3 bench.py --traffic-from {fetch} {write}",
 ]
 
 
@@ -181,7 +183,7 @@ def traffic_from(fetch_dir, write_dir):
     ff, fw = calib(fetch), calib(write)
     rec = {"calibration": {"pass": "torch.neg over 256 MiB fp32 (reads and writes 268,435,456 B)",
                            "fetch_factor": round(ff, 4), "write_factor": round(fw, 4)},
-           "commands": PMC_CMDS}
+           "commands": [c.format(fetch=fetch_dir, write=write_dir) for c in PMC_CMDS]}
     rows = []
     for key, (prefix, wgs, srcs) in TRAFFIC_KERNELS.items():
         fb = find(fetch, prefix, wgs) * ff

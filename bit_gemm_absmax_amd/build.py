@@ -58,7 +58,7 @@ def _link(objs, lib: str) -> None:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
     # dlopen resolves every symbol now: a kernel whose host stub the
-    # compiler failed to emit shows up here instead of on the GPU machine.
+    # compiler failed to emit shows up here, at build time, not at first use.
     import ctypes
     ctypes.CDLL(tmp)
     os.replace(tmp, lib)
