@@ -57,6 +57,9 @@ hipError_t launch_gemv_gated(const int8_t* Xq, const float* xs, const int32_t* r
                              const uint8_t* up, const float* up_scale, const uint8_t* gate, const float* gate_scale,
                              int64_t N, float* Y, hipStream_t s);
 
+// Compute units of the current device (looked up once per device).
+int cu_count();
+
 // int8 MFMA GEMM for any M.
 hipError_t launch_gemm(const int8_t* Xq, const float* xs, const int32_t* rs, int64_t M,
                        int64_t K, const uint8_t* packed, const float* ws, int64_t N, Epi epi,

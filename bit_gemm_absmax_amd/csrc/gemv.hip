@@ -205,6 +205,171 @@ __global__ __launch_bounds__(NWV* kWave) void k_decode(const float* __restrict__
     }
 }
 
+// Very tall matrices (thousands of 16-row tiles, e.g. an output layer over a
+// large vocabulary), M <= 4, no gate: a persistent launch of about as many
+// workgroups as fit on the device at once.  Each quantises the rows once
+// (as k_decode does) and then walks the groups of CT tiles g = blockIdx.x,
+// blockIdx.x + gridDim.x, ...; the weight loads (and epilogue operand) of
+// the next group go out before the current group's MFMAs and epilogue, so
+// every workgroup keeps one group in flight while it works and the launch
+// streams the matrix with no second round of workgroups.
+constexpr bool kStreamNT = true;  // non-temporal weight loads in the streaming launch
+
+template <int NWV, int NV, int CT>
+__global__ __launch_bounds__(NWV* kWave) void k_decode_stream(const float* __restrict__ X, int M, int K,
+                                                               int rmsnorm, const float* __restrict__ gain,
+                                                               float eps, const uint8_t* __restrict__ Wp,
+                                                               const float* __restrict__ w_scale, int N,
+                                                               uint32_t epi_flags, const float* aux, float* Y) {
+    static_assert(4 * 16 * CT <= NWV * kWave, "one epilogue thread per output");
+    constexpr int NT = NWV * kWave;
+    constexpr int COLS = 16 * CT;
+    // Chunk quads per wave: K <= 4 NT NV = 256 NWV NV, so NV covers them.
+    constexpr int QMAX = NV;
+    extern __shared__ __align__(16) int8_t lds[];  // [xq: M <= 4 rows of K] [partials]
+    __shared__ double dslot[NWV];
+    __shared__ float fslot[NWV], fslot2[NWV];
+    __shared__ int islot[4][NWV];
+    __shared__ float gx[4];
+
+    const int lane = threadIdx.x % kWave;
+    const int wave = threadIdx.x / kWave;
+    const int fr = lane & 15;
+    const int fg = lane >> 4;
+    const int C = K / 64;
+    const int groups = (N + COLS - 1) / COLS;
+    const float ws = *w_scale;
+    const bool has_aux = (epi_flags & (kEpiResidual | kEpiMul)) != 0;
+    const Rsrc raux = make_rsrc(aux, has_aux ? 0x7FFFFFFFu : 0u);
+    const int e_m = threadIdx.x / COLS, e_col = (int)threadIdx.x % COLS;
+
+    // This lane's chunk c of load i (quad wave + i NWV): byte offset 16 (c R
+    // + fr) in a tile of R rows; past the row the top bit puts it past every
+    // descriptor, so the load returns zeros (and adds nothing).
+    uint32_t c16[QMAX], oob[QMAX];
+#pragma unroll
+    for (int i = 0; i < QMAX; ++i) {
+        const int c = 4 * (wave + i * NWV) + fg;
+        c16[i] = 16u * (uint32_t)c;
+        oob[i] = c < C ? 0u : kOob;
+    }
+    // Weights of group g (a group past the matrix reads nothing: zero rows)
+    // and this thread's epilogue operand for it.  Straight-line: no load
+    // sits under a branch, so the loads of the next group can stay in
+    // flight while the current one is contracted.
+    auto load_group = [&](int g, uint4 (&w)[CT][QMAX], float& res) {
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+            const int r0 = g * COLS + 16 * ct;
+            const int rows = __builtin_amdgcn_readfirstlane(N - r0 < 0 ? 0 : (N - r0 < 16 ? N - r0 : 16));
+            const Rsrc rw = make_rsrc(Wp + (int64_t)(rows > 0 ? r0 : 0) * (K / 4), (uint32_t)rows * (uint32_t)(K / 4));
+#pragma unroll
+            for (int i = 0; i < QMAX; ++i)
+                w[ct][i] = kStreamNT ? buf_load16_nt(rw, (c16[i] * (uint32_t)rows + 16u * (uint32_t)fr) | oob[i])
+                                     : buf_load16(rw, (c16[i] * (uint32_t)rows + 16u * (uint32_t)fr) | oob[i]);
+        }
+        const int e_n = g * COLS + e_col;
+        const bool ok = (int)threadIdx.x < M * COLS && e_n < N;
+        res = buf_load4f(raux, ok ? (uint32_t)((int64_t)e_m * N + e_n) * 4u : kOob);
+    };
+
+    float4 v[NV], gv[NV];
+    const bool has_gain = rmsnorm != 0 && gain != nullptr;
+    quant_row_load<NT, NV>(X, has_gain ? gain : nullptr, K, v, gv);
+    __builtin_amdgcn_sched_barrier(0);  // keep these loads ahead of the weights'
+    uint4 wa[CT][QMAX], wb[CT][QMAX];
+    float ra, rb;
+    int g = blockIdx.x;
+    load_group(g, wa, ra);
+
+    int8_t* xq = lds;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        if (m == 0 || m < M) {
+            if (m > 0) {
+                __syncthreads();  // the reduction slots are reused
+                quant_row_load_x<NT, NV>(X + (int64_t)m * K, K, v);
+            }
+            const float gq = quant_row_finish<NT, NV>(v, gv, K, rmsnorm != 0, has_gain, eps, xq + m * K, dslot,
+                                                        fslot, fslot2, islot[m]);
+            if (threadIdx.x == 0) gx[m] = gq;
+        }
+    }
+    __syncthreads();
+    const int8_t* arow = xq + (fr < M ? fr : M - 1) * K;
+    int rs_m = 0;
+    float d_m = 0.0f;
+    if ((int)threadIdx.x < M * COLS) {
+#pragma unroll
+        for (int q = 0; q < NWV; ++q) rs_m += islot[e_m][q];
+        d_m = (gx[e_m] * ws) / 127.0f;
+    }
+    int* red = reinterpret_cast<int*>(lds + 4 * K);  // [NWV][16 tokens][COLS]
+
+    // One group: contraction, per-wave partial tiles summed in wave order,
+    // epilogue.  Ends with a barrier, so the next group may reuse `red`.
+    auto process = [&](int gg, const uint4 (&w)[CT][QMAX], float res) {
+        v4i acc[CT];
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) acc[ct] = v4i{0, 0, 0, 0};
+#pragma unroll
+        for (int i = 0; i < QMAX; ++i) {
+            // every load is consumed (a wave short of quads multiplies zeros),
+            // so no use of a load sits under a branch
+            const int c = 4 * (wave + i * NWV) + fg;
+            const int koff = c < C ? 64 * c : 0;
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                const v4i a = *reinterpret_cast<const v4i*>(arow + koff + 16 * d);
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) {
+                    const uint32_t wd = d == 0 ? w[ct][i].x : d == 1 ? w[ct][i].y : d == 2 ? w[ct][i].z : w[ct][i].w;
+                    const v4i b = v4i{codes4(wd, 0), codes4(wd, 1), codes4(wd, 2), codes4(wd, 3)};
+                    acc[ct] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, acc[ct], 0, 0, 0);
+                }
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int m = 4 * fg + r;
+            if (m < M) {
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) red[(wave * 16 + m) * COLS + 16 * ct + fr] = acc[ct][r];
+            }
+        }
+        __syncthreads();
+        const int e_n = gg * COLS + e_col;
+        if ((int)threadIdx.x < M * COLS && e_n < N) {
+            int a = 0;
+#pragma unroll
+            for (int q = 0; q < NWV; ++q) a += red[(q * 16 + e_m) * COLS + e_col];
+            a -= rs_m;
+            float y = (float)a * d_m;
+            if (epi_flags & kEpiRelu2) {
+                const float tt = y > 0.0f ? y : 0.0f;
+                y = tt * tt;
+            }
+            if (epi_flags & kEpiMul) y = y * res;
+            else if (epi_flags & kEpiResidual) y = y + res;
+            Y[(int64_t)e_m * N + e_n] = y;
+        }
+        __syncthreads();
+    };
+
+    // Two register sets alternate: while one group is contracted the next
+    // group's loads are in flight.
+    while (true) {
+        load_group(g + (int)gridDim.x, wb, rb);
+        process(g, wa, ra);
+        g += gridDim.x;
+        if (g >= groups) break;
+        load_group(g + (int)gridDim.x, wa, ra);
+        process(g, wb, rb);
+        g += gridDim.x;
+        if (g >= groups) break;
+    }
+}
+
 // int8 rows from the standalone quantiser, M <= 64 tokens (batched decode).
 // A workgroup owns 16 * CT output rows (CT column tiles) and all M tokens
 // (MT token tiles of 16).  Its four waves split K in chunk quads (256 k),
@@ -558,10 +723,29 @@ hipError_t go_decode(const float* X, int64_t M, int64_t K, bool rms, const float
     return hipGetLastError();
 }
 
-// Very tall matrices (at least 2048 tiles of 16 rows, eight per CU): four
-// tiles per workgroup, so the per-workgroup quantisation is amortised over
-// 64 rows while thousands of workgroups remain.
+// Very tall matrices (at least 2048 tiles of 16 rows, eight per CU): the
+// persistent streaming launch, kStreamCT tiles per group (0: the one-shot
+// launch with four tiles per workgroup instead).
 constexpr int64_t kTallTiles = 2048;
+constexpr int kStreamCT = 1;
+
+template <int NWV, int NV, int CT>
+hipError_t go_decode_stream(const float* X, int64_t M, int64_t K, bool rms, const float* gain, float eps,
+                            const uint8_t* packed, const float* ws, int64_t N, uint32_t epi, const float* aux,
+                            float* Y, hipStream_t s) {
+    const size_t lds = 4 * (size_t)K + (size_t)NWV * 16 * 16 * CT * sizeof(int);
+    int occ = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, k_decode_stream<NWV, NV, CT>, NWV * kWave, lds) !=
+            hipSuccess ||
+        occ < 1)
+        occ = 1;
+    const int64_t groups = (N + 16 * CT - 1) / (16 * CT);
+    const int64_t resident = (int64_t)cu_count() * occ;
+    const unsigned blocks = (unsigned)(groups < resident ? groups : resident);
+    hipLaunchKernelGGL((k_decode_stream<NWV, NV, CT>), dim3(blocks), dim3(NWV * kWave), lds, s, X, (int)M,
+                       (int)K, rms ? 1 : 0, gain, eps, packed, ws, (int)N, epi, aux, Y);
+    return hipGetLastError();
+}
 
 // The quantiser's depth for K (which the plan bounds by qmax) picks NV.
 template <bool G>
@@ -573,9 +757,11 @@ hipError_t go_decode_plan(const Plan& p, const float* X, int64_t M, int64_t K, b
     const bool tall = !G && (N + 15) / 16 >= kTallTiles;
 #define BL_DEC(NWV, Q, NV)                                                                                     \
     if (p.nw == NWV && p.qmax == Q && nv == NV)                                                                \
-        return tall ? go_decode<NWV, Q, G, NV, G ? 1 : 4>(X, M, K, rms, gain, eps, packed, ws, N, epi, aux, Y, gate, \
-                                                          gate_scale, s)                                      \
-                    : go_decode<NWV, Q, G, NV>(X, M, K, rms, gain, eps, packed, ws, N, epi, aux, Y, gate, gate_scale, s);
+        return !tall ? go_decode<NWV, Q, G, NV>(X, M, K, rms, gain, eps, packed, ws, N, epi, aux, Y, gate, gate_scale, s) \
+               : kStreamCT > 0                                                                                 \
+                   ? go_decode_stream<NWV, NV, (kStreamCT > 0 ? kStreamCT : 1)>(X, M, K, rms, gain, eps, packed, ws, N, epi, aux, Y, s) \
+                   : go_decode<NWV, Q, G, NV, G ? 1 : 4>(X, M, K, rms, gain, eps, packed, ws, N, epi, aux, Y, gate,   \
+                                                         gate_scale, s);
     BL_DEC(4, 2, 1)
     BL_DEC(4, 2, 2)
     BL_DEC(4, 4, 3)

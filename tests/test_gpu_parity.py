@@ -530,12 +530,14 @@ def test_ffn_gated_model_width(M):
 # ------------------------------------------------------------------ very tall matrices at decode
 
 @pytest.mark.parametrize("M,K,N,epi", [(1, 2560, 40008, "relu2"), (3, 256, 33000, "residual"),
-                                        (4, 512, 32768, "none"), (2, 1024, 36880, "mul")])
+                                        (4, 512, 32768, "none"), (2, 1024, 36880, "mul"),
+                                        (1, 256, 200_008, "relu2"), (2, 6912, 32776, "residual")])
 def test_decode_tall(M, K, N, epi):
     """At 2048 or more 16-row tiles the fused quantise + BitLinear launch
-    gives each workgroup four tiles (one quantisation for 64 rows), the last
-    group ragged or partly empty: Y against the oracle, and bit for bit
-    against the two-step path (quantiser + batched kernel)."""
+    is persistent: each workgroup quantises the rows once and walks groups
+    of tiles (many per workgroup at N = 200,008), the last group ragged or
+    partly empty: Y against the oracle, and bit for bit against the two-step
+    path (quantiser + batched kernel)."""
     log(f"[decode tall] M={M} K={K} N={N} epi={epi}")
     rng = np.random.default_rng(7000 + M + N)
     X = synth.activations(rng, M, K, outliers=True)
