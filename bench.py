@@ -70,6 +70,7 @@ TRAFFIC_KERNELS = {
     "gemm_down_m4096": ("k_gemm_pipe<256, 160, 4, 2, 4, 1>", 256, ("gemm.hip", "bl_device.h")),
     "batch_gate_m64": ("k_batch<4, 2, 2, 3, false>", 216, ("gemv.hip", "bl_device.h")),
     "batch_down_m64": ("k_batch<4, 1, 2, 7, false>", 160, ("gemv.hip", "bl_device.h")),
+    "decode_tall_m1": ("k_decode_stream<4, 3, 1>", None, ("gemv.hip", "bl_device.h")),
 }
 CALIB_BYTES = 256 << 20   # the calibration kernel reads and writes 256 MiB
 # The three commands behind profiles/traffic.json ({fetch} and {write} are the
@@ -137,6 +138,17 @@ def pmc_drive():
             bl.forward(q64, s64, w, sg, x_rowsum=r64, y_out=yg)
         for w in downs:
             bl.forward(q2, s2, w, sdb, x_rowsum=r2, y_out=yb)
+    torch.cuda.synchronize()
+    del gates, downs
+    # the tall decode (2560 -> 131,328, persistent streaming launch) over 3
+    # copies of its 84 MB matrix
+    tall = pu.repeat(19, 1)
+    talls = [tall] + [tall.clone() for _ in range(2)]
+    qts = [bl.QuantForward(c, su, 1, relu2=True) for c in talls]
+    yt = torch.empty((1, tall.shape[0]), dtype=torch.float32, device=dev)
+    for _ in range(3):
+        for q in qts:
+            q(x, y_out=yt)
     torch.cuda.synchronize()
     log("pmc-drive done")
 
@@ -432,6 +444,8 @@ def tall_decode(torch, bl, d, pu, su, dev, log):
     log(f"decode M=1 2560->{N} (tall, {nb / 1e6:.0f} MB): {t * 1e6:.2f} us -> {nb / t / 1e9:.0f} GB/s")
     return {"K": 2560, "N": N, "packed_bytes": nb, "us_per_launch": round(t * 1e6, 2),
             "GB_per_s": round(nb / t / 1e9, 1), "frac_hbm": round(nb / t / 1e9 / HBM_PEAK_GBS, 4),
+            "kernel": "k_decode_stream<4,3,1> (persistent: rows quantised once per workgroup, tiles streamed)",
+            "traffic": traffic_from_profile("decode_tall_m1", ("gemv.hip", "bl_device.h")),
             "weights": "seed-1 up matrix repeated 19x along N; 7 copies rotated"}
 
 
