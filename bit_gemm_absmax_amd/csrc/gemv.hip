@@ -26,6 +26,8 @@
 // into LDS (the same quant_row_* as the standalone quantiser, so the same
 // int8 values), which removes the quantiser launch from the decode chain.
 // k_batch (M <= 64) takes the standalone quantiser's int8 rows.
+#include <atomic>
+
 #include "bl_device.h"
 #include "bl_internal.h"
 
@@ -734,11 +736,23 @@ hipError_t go_decode_stream(const float* X, int64_t M, int64_t K, bool rms, cons
                             const uint8_t* packed, const float* ws, int64_t N, uint32_t epi, const float* aux,
                             float* Y, hipStream_t s) {
     const size_t lds = 4 * (size_t)K + (size_t)NWV * 16 * 16 * CT * sizeof(int);
+    // Resident workgroups per CU from the runtime's occupancy query, kept per
+    // device for the last LDS size asked (one entry: lds << 16 | occupancy).
+    static std::atomic<int64_t> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = -1;
     int occ = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, k_decode_stream<NWV, NV, CT>, NWV * kWave, lds) !=
-            hipSuccess ||
-        occ < 1)
-        occ = 1;
+    const int64_t hit = dev >= 0 ? cache[dev].load(std::memory_order_relaxed) : 0;
+    if (hit != 0 && (size_t)(hit >> 16) == lds) {
+        occ = (int)(hit & 0xFFFF);
+    } else {
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, k_decode_stream<NWV, NV, CT>, NWV * kWave, lds) !=
+                hipSuccess ||
+            occ < 1)
+            occ = 1;
+        if (occ > 0xFFFF) occ = 0xFFFF;
+        if (dev >= 0) cache[dev].store(((int64_t)lds << 16) | occ, std::memory_order_relaxed);
+    }
     const int64_t groups = (N + 16 * CT - 1) / (16 * CT);
     const int64_t resident = (int64_t)cu_count() * occ;
     const unsigned blocks = (unsigned)(groups < resident ? groups : resident);
