@@ -6,13 +6,19 @@ the product path (HIP library and its binding) never does, and the two share
 no code.
 
 The arithmetic lives in ``oracle.c`` (plain C, built with gcc); this module
-only builds it, loads it and marshals numpy arrays.  Method source: the
+only builds it, loads it and marshals numpy arrays.  The C file is built
+twice: ``liboracle.so`` runs on one core, ``liboracle_mt.so`` (``-fopenmp``)
+splits the outermost loop of each step over threads with the per-element
+code unchanged, so it returns identical results (pinned by a test).  Calls go
+to the one-core build unless :func:`set_threads` (or :func:`parallel`) asks
+for more threads.  Method source: the
 transformers documentation page "BitNet", section "Model details"
 (Architecture and Quantization bullets) and section "BitNetConfig"
 (rms_norm_eps, model shapes).
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 import subprocess
@@ -22,28 +28,83 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
+_LIB_MT = os.path.join(_HERE, "liboracle_mt.so")
 
 CFLAGS = ["-O2", "-fno-tree-vectorize", "-ffp-contract=off", "-fno-fast-math",
           "-std=c11", "-fPIC", "-shared", "-Wall", "-Wextra"]
+# (extra flags, output) of the two builds of oracle.c
+_BUILDS = {"serial": (["-Wno-unknown-pragmas"], _LIB), "mt": (["-fopenmp"], _LIB_MT)}
 
-_lib = None
+_libs = {}
+_threads = 1
+
+
+def _compile(which: str) -> str:
+    extra, out = _BUILDS[which]
+    tmp = out + ".tmp"
+    subprocess.run(["gcc", *CFLAGS, *extra, "-o", tmp, _SRC, "-lm"], check=True)
+    os.replace(tmp, out)
+    return out
 
 
 def build() -> str:
-    """Compile oracle.c into liboracle.so with gcc (always recompiles)."""
-    tmp = _LIB + ".tmp"
-    subprocess.run(["gcc", *CFLAGS, "-o", tmp, _SRC, "-lm"], check=True)
-    os.replace(tmp, _LIB)
+    """Compile oracle.c into liboracle.so and liboracle_mt.so with gcc (always
+    recompiles both)."""
+    for which in _BUILDS:
+        _compile(which)
     return _LIB
 
 
-def _load():
-    global _lib
-    if _lib is not None:
-        return _lib
-    if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-        build()
-    lib = ctypes.CDLL(_LIB)
+def default_threads() -> int:
+    """Host threads for the OpenMP build: OMP_NUM_THREADS if set, else the
+    cores this process may run on."""
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    if env.isdigit() and int(env) > 0:
+        return int(env)
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover - non-Linux
+        return os.cpu_count() or 1
+
+
+def set_threads(n: int) -> int:
+    """Route later calls to the one-core build (n == 1) or to the OpenMP build
+    with n threads; returns the thread count in force."""
+    global _threads
+    n = max(1, int(n))
+    if n > 1:
+        got = _load("mt").orc_set_threads(n)
+        _threads = max(1, int(got))
+    else:
+        _threads = 1
+    return _threads
+
+
+def threads() -> int:
+    return _threads
+
+
+@contextlib.contextmanager
+def parallel(n=None):
+    """Run the enclosed oracle calls on the OpenMP build with n threads
+    (default: default_threads())."""
+    prev = _threads
+    set_threads(default_threads() if n is None else n)
+    try:
+        yield _threads
+    finally:
+        set_threads(prev)
+
+
+def _load(which: str = None):
+    if which is None:
+        which = "mt" if _threads > 1 else "serial"
+    if which in _libs:
+        return _libs[which]
+    path = _BUILDS[which][1]
+    if not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(_SRC):
+        _compile(which)
+    lib = ctypes.CDLL(path)
     P = ctypes.c_void_p
     I64 = ctypes.c_int64
     F = ctypes.c_float
@@ -74,7 +135,13 @@ def _load():
     lib.orc_ffn_layer_gated.argtypes = [P, I64, I64, I64, P, F, P, F, P, F, P, F, P, F, ctypes.c_int, P, P, P]
     lib.orc_ffn_layer_gated.restype = None
     lib.orc_ffn_layer.restype = None
-    _lib = lib
+    lib.orc_pack_canonical.argtypes = [P, I64, I64, P]
+    lib.orc_pack_canonical.restype = ctypes.c_int
+    lib.orc_unpack_canonical.argtypes = [P, I64, I64, P]
+    lib.orc_unpack_canonical.restype = ctypes.c_int
+    lib.orc_set_threads.argtypes = [ctypes.c_int]
+    lib.orc_set_threads.restype = ctypes.c_int
+    _libs[which] = lib
     return lib
 
 
@@ -129,6 +196,26 @@ def unpack(packed, K) -> np.ndarray:
     q = np.empty((N, K), np.int8)
     if _load().orc_unpack(_p(packed), N, K, _p(q)) != 0:
         raise ValueError("unpack: bad K or code 3 present")
+    return q
+
+
+def pack_canonical(q) -> np.ndarray:
+    """Plain 2-bit form of ternary q [N][K]: row-major [N][K/4] bytes, weight
+    k in byte k/4 at bits 2(k%4), code q + 1 (orc_pack_canonical)."""
+    q = _c(q, np.int8)
+    N, K = q.shape
+    out = np.empty((N, K // 4), np.uint8)
+    if _load().orc_pack_canonical(_p(q), N, K, _p(out)) != 0:
+        raise ValueError("pack_canonical: K must be a multiple of 4 and q ternary")
+    return out
+
+
+def unpack_canonical(b, K) -> np.ndarray:
+    b = _c(b, np.uint8)
+    N = b.shape[0]
+    q = np.empty((N, K), np.int8)
+    if _load().orc_unpack_canonical(_p(b), N, K, _p(q)) != 0:
+        raise ValueError("unpack_canonical: bad K or code 3 present")
     return q
 
 

@@ -6,13 +6,32 @@
  *
  * Build: gcc -O2 -fno-tree-vectorize -ffp-contract=off -fPIC -shared
  * (x86-64 SSE arithmetic: binary32 operations are correctly rounded and no
- * multiply-add is fused).
+ * multiply-add is fused).  Built twice from this one file: without OpenMP
+ * (liboracle.so, one core; the pragmas below are then inert) and with
+ * -fopenmp (liboracle_mt.so).  The pragmas only split the outermost loop of a
+ * step over threads (tokens, or tokens x output rows): every element is still
+ * computed by the same inner loop in the same order, so both builds give
+ * identical results.  Sums whose order spans the split loop (the absmean)
+ * stay serial.
  */
 #include "oracle.h"
 
 #include <math.h>
 #include <stdlib.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+int orc_set_threads(int n) {
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+    return omp_get_max_threads();
+#else
+    (void)n;
+    return 1;
+#endif
+}
 
 /* "Model details" / Quantization: weights are scaled by their absmean.
  * The page does not fix the granularity; one scale per weight tensor. */
@@ -32,6 +51,7 @@ float orc_absmean_scale(const float* W, int64_t N, int64_t K) {
 /* "Model details" / Quantization: ternary {-1, 0, +1} from W / absmean,
  * rounded to the nearest integer (ties to even) and clipped. */
 void orc_ternarize(const float* W, int64_t N, int64_t K, float gamma, int8_t* q) {
+#pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < N * K; ++i) {
         float t = W[i] / gamma;
         float r = rintf(t);
@@ -79,11 +99,42 @@ int orc_unpack(const uint8_t* packed, int64_t N, int64_t K, int8_t* q) {
     return 0;
 }
 
+/* The plain 2-bit form of ternary weights: row-major, four consecutive
+ * weights per byte, weight k of row n in byte n*(K/4) + k/4 at bits
+ * 2*(k%4) (lowest first), code q + 1.  The page names packed 1.58-bit
+ * weights ("Model variants") without a layout; this is the form a caller
+ * outside this library is most likely to hold. */
+int orc_pack_canonical(const int8_t* q, int64_t N, int64_t K, uint8_t* bytes) {
+    if (K % 4 != 0) return -1;
+    memset(bytes, 0, (size_t)(N * (K / 4)));
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t k = 0; k < K; ++k) {
+            int v = q[n * K + k];
+            if (v < -1 || v > 1) return -1;
+            bytes[n * (K / 4) + k / 4] |= (uint8_t)((unsigned)(v + 1) << (2 * (k % 4)));
+        }
+    }
+    return 0;
+}
+
+int orc_unpack_canonical(const uint8_t* bytes, int64_t N, int64_t K, int8_t* q) {
+    if (K % 4 != 0) return -1;
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t k = 0; k < K; ++k) {
+            unsigned code = (bytes[n * (K / 4) + k / 4] >> (2 * (k % 4))) & 3u;
+            if (code == 3u) return -1;
+            q[n * K + k] = (int8_t)((int)code - 1);
+        }
+    }
+    return 0;
+}
+
 /* "Model details" / Quantization: activations to 8-bit integers by absmax,
  * one scale per token.  Range [-127, 127] so that the largest entry of every
  * token maps to exactly +-127. */
 void orc_quant_act(const float* X, int64_t M, int64_t K,
                    int8_t* xq, float* gamma_x, int32_t* rowsum) {
+#pragma omp parallel for schedule(static)
     for (int64_t m = 0; m < M; ++m) {
         const float* x = X + m * K;
         float amax = 0.0f;
@@ -111,6 +162,7 @@ void orc_quant_act(const float* X, int64_t M, int64_t K,
  * "BitNetConfig": rms_norm_eps.  Root-mean-square normalisation with a gain. */
 void orc_rmsnorm(const float* V, int64_t M, int64_t K, const float* gain,
                  float eps, float* Z) {
+#pragma omp parallel for schedule(static)
     for (int64_t m = 0; m < M; ++m) {
         const float* v = V + m * K;
         double ss = 0.0;
@@ -127,6 +179,7 @@ void orc_rmsnorm(const float* V, int64_t M, int64_t K, const float* gain,
 /* W1.58A8 contraction: int8 activations times ternary weights, int32 sum. */
 void orc_int_matmul(const int8_t* xq, int64_t M, int64_t K,
                     const int8_t* q, int64_t N, int32_t* acc) {
+#pragma omp parallel for collapse(2) schedule(static)
     for (int64_t m = 0; m < M; ++m) {
         for (int64_t n = 0; n < N; ++n) {
             int32_t s = 0;
@@ -140,6 +193,7 @@ void orc_int_matmul(const int8_t* xq, int64_t M, int64_t K,
 /* Undo both scales: x ~ xq * gamma_x / 127 and w ~ q * gamma_w. */
 void orc_dequant(const int32_t* acc, int64_t M, int64_t N,
                  const float* gamma_x, float gamma_w, float* Y) {
+#pragma omp parallel for schedule(static)
     for (int64_t m = 0; m < M; ++m) {
         float d = (gamma_x[m] * gamma_w) / 127.0f;
         for (int64_t n = 0; n < N; ++n) Y[m * N + n] = (float)acc[m * N + n] * d;
@@ -148,6 +202,7 @@ void orc_dequant(const int32_t* acc, int64_t M, int64_t N,
 
 /* "Model details": squared ReLU activation in the feed-forward layers. */
 void orc_relu2(float* Y, int64_t count) {
+#pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < count; ++i) {
         float r = Y[i] > 0.0f ? Y[i] : 0.0f;
         Y[i] = r * r;
@@ -155,6 +210,7 @@ void orc_relu2(float* Y, int64_t count) {
 }
 
 void orc_add(float* H, const float* Y, int64_t count) {
+#pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < count; ++i) H[i] = H[i] + Y[i];
 }
 
@@ -199,6 +255,7 @@ void orc_ffn_layer(float* H, int64_t M, int64_t Hd, int64_t F,
 
 /* Gating product of the gated FFN: elementwise, binary32. */
 void orc_mul(float* a, const float* b, int64_t n) {
+#pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < n; ++i) a[i] = a[i] * b[i];
 }
 

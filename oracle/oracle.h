@@ -56,6 +56,17 @@ int orc_pack(const int8_t* q, int64_t N, int64_t K, uint8_t* packed);
 /* Inverse of orc_pack.  Returns 0, or -1 on a bad K or on code 3. */
 int orc_unpack(const uint8_t* packed, int64_t N, int64_t K, int8_t* q);
 
+/* Plain row-major 2-bit form: code q + 1 of weight k of row n in byte
+ * n*(K/4) + k/4 at bits 2*(k%4) (four consecutive weights per byte, the
+ * lowest first).  K must be a multiple of 4.  Returns 0, or -1 on a bad K,
+ * a non-ternary value (pack) or code 3 (unpack). */
+int orc_pack_canonical(const int8_t* q, int64_t N, int64_t K, uint8_t* bytes);
+int orc_unpack_canonical(const uint8_t* bytes, int64_t N, int64_t K, int8_t* q);
+
+/* Threads of the OpenMP build (liboracle_mt.so): sets the count when n > 0
+ * and returns the count in force; the one-core build returns 1. */
+int orc_set_threads(int n);
+
 /* Per-token absmax quantisation of X[M][K]:
  *   gamma_x[m] = max(max_k |X[m][k]|, 1e-5)
  *   s          = 127 / gamma_x[m]                (binary32 divide)

@@ -39,6 +39,50 @@ def test_hand_bitlinear(golden):
     assert np.all(np.abs(r["y"].astype(np.float64) - exact) <= 2.0 ** -22 * np.abs(exact))
 
 
+def test_hand_canonical_bytes(golden):
+    """The plain row-major form of the hand-worked 2 x 4 matrix: bytes 0x16
+    and 0x89 (four consecutive codes per byte, lowest bits first), and back."""
+    g = golden("hand_bitlinear_2x4.json")
+    q = np.array(g["q"], np.int8)
+    want = np.array(g["packed_canonical"], np.uint8)
+    assert [int(b) for b in want.ravel()] == [0x16, 0x89]
+    np.testing.assert_array_equal(oracle.pack_canonical(q), want)
+    np.testing.assert_array_equal(oracle.unpack_canonical(want, 4), q)
+
+
+@pytest.mark.parametrize("N,K", [(3, 4), (17, 64), (33, 2560)])
+def test_canonical_roundtrip_and_tile_layout_agree(N, K):
+    """Both 2-bit forms hold the same ternary matrix: each round-trips, code 3
+    never appears, and a byte carries exactly the four consecutive weights
+    4i..4i+3 of its row (checked one weight at a time through the one-hot
+    matrices)."""
+    rng = np.random.default_rng(N * K)
+    q = rng.integers(-1, 2, (N, K)).astype(np.int8)
+    b = oracle.pack_canonical(q)
+    assert b.shape == (N, K // 4)
+    np.testing.assert_array_equal(oracle.unpack_canonical(b, K), q)
+    assert not np.any((b & 0x03) == 3) and not np.any((b >> 6) == 3)
+    if K % 64 == 0:
+        np.testing.assert_array_equal(oracle.unpack(oracle.pack(q), K), oracle.unpack_canonical(b, K))
+    # a single +1 among zeros (codes 1) changes exactly one byte of row n, byte k // 4
+    base = oracle.pack_canonical(np.zeros((N, K), np.int8))
+    assert np.all(base == 0x55)
+    for n, k in [(0, 0), (N - 1, K - 1), (N // 2, K // 2 + 1)]:
+        e = np.zeros((N, K), np.int8)
+        e[n, k] = 1
+        diff = np.argwhere(oracle.pack_canonical(e) != base)
+        assert diff.tolist() == [[n, k // 4]]
+
+
+def test_canonical_rejects_bad_input():
+    with pytest.raises(ValueError):
+        oracle.pack_canonical(np.zeros((2, 6), np.int8))
+    with pytest.raises(ValueError):
+        oracle.pack_canonical(np.full((2, 4), 2, np.int8))
+    with pytest.raises(ValueError):
+        oracle.unpack_canonical(np.full((1, 1), 0xFF, np.uint8), 4)
+
+
 def test_hand_pack(golden):
     g = golden("hand_pack_2x128.json")
     q = np.array(g["q"], np.int8)
