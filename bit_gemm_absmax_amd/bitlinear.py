@@ -38,7 +38,9 @@ RMS_EPS = 1e-5  # rms_norm_eps of the BitNet config
 
 SYMBOLS = (
     "bitlinear_status_string", "bitlinear_last_error", "bitlinear_abi_version",
-    "bitlinear_pack_workspace_bytes", "bitlinear_pack_weights", "bitlinear_quant_act",
+    "bitlinear_pack_workspace_bytes", "bitlinear_pack_weights",
+    "bitlinear_import_canonical", "bitlinear_export_canonical", "bitlinear_unpack_weights",
+    "bitlinear_quant_act",
     "bitlinear_forward_workspace_bytes", "bitlinear_forward",
     "bitlinear_quant_forward_workspace_bytes", "bitlinear_quant_forward",
     "bitlinear_latent_forward_workspace_bytes", "bitlinear_latent_forward",
@@ -90,6 +92,9 @@ def load(path: str = LIB_PATH):
     lib.bitlinear_pack_workspace_bytes.restype = SZ
     lib.bitlinear_pack_weights.argtypes = [P, I64, I64, P, P, P, SZ, P]
     lib.bitlinear_pack_weights.restype = I
+    for name in ("bitlinear_import_canonical", "bitlinear_export_canonical", "bitlinear_unpack_weights"):
+        getattr(lib, name).argtypes = [P, I64, I64, P, P]
+        getattr(lib, name).restype = I
     lib.bitlinear_quant_act.argtypes = [P, I64, I64, U32, P, F, P, P, P, P]
     lib.bitlinear_quant_act.restype = I
     lib.bitlinear_forward_workspace_bytes.argtypes = [I64, I64, I64, U32]
@@ -134,14 +139,31 @@ def _stream(device=None):
 def _need(t: torch.Tensor, dtype, ndim: int, name: str):
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
-    if not t.is_cuda:
-        raise ValueError(f"{name} must be a GPU tensor")
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if t.dim() != ndim:
         raise ValueError(f"{name} must have {ndim} dims, got {t.dim()}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+
+
+def _on_gpu(*ts):
+    """Every given tensor (None skipped) must live on the GPU; checked after
+    the dtype and shape checks, right before a call into the library."""
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError(f"a {tuple(t.shape)} {t.dtype} argument is not a GPU tensor")
+
+
+def _shape(t: Optional[torch.Tensor], dtype, shape, name: str):
+    """Exact dtype and shape of an optional tensor argument (the C library
+    trusts M, K and N, so a wrong-sized tensor would be read or written past
+    its end)."""
+    if t is None:
+        return
+    _need(t, dtype, len(shape), name)
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
 
 
 def _workspace(nbytes: int, device) -> Optional[torch.Tensor]:
@@ -158,6 +180,7 @@ def pack_weights(W: torch.Tensor):
     the packed form of a row subset."""
     lib = load()
     _need(W, torch.float32, 2, "W")
+    _on_gpu(W)
     N, K = W.shape
     packed = torch.empty((N, K // 4), dtype=torch.uint8, device=W.device)
     w_scale = torch.empty(1, dtype=torch.float32, device=W.device)
@@ -165,6 +188,39 @@ def pack_weights(W: torch.Tensor):
     _check(lib.bitlinear_pack_weights(_p(W), N, K, _p(packed), _p(w_scale), _p(ws),
                                       0 if ws is None else ws.numel(), _stream(W.device)))
     return packed, w_scale
+
+
+def _relayout(fn_name: str, src: torch.Tensor, N: int, K: int, out: torch.Tensor):
+    lib = load()
+    _check(getattr(lib, fn_name)(_p(src), N, K, _p(out), _stream(src.device)))
+    return out
+
+
+def import_canonical(canonical: torch.Tensor) -> torch.Tensor:
+    """Plain row-major 2-bit weights u8 [N][K/4] (four consecutive codes q + 1
+    per byte, lowest bits first) -> this library's packed layout u8 [N][K/4]."""
+    _need(canonical, torch.uint8, 2, "canonical")
+    _on_gpu(canonical)
+    N, K = canonical.shape[0], canonical.shape[1] * 4
+    return _relayout("bitlinear_import_canonical", canonical, N, K,
+                     torch.empty_like(canonical))
+
+
+def export_canonical(packed: torch.Tensor) -> torch.Tensor:
+    """The inverse of import_canonical."""
+    _need(packed, torch.uint8, 2, "packed")
+    _on_gpu(packed)
+    N, K = packed.shape[0], packed.shape[1] * 4
+    return _relayout("bitlinear_export_canonical", packed, N, K, torch.empty_like(packed))
+
+
+def unpack_weights(packed: torch.Tensor) -> torch.Tensor:
+    """Packed layout u8 [N][K/4] -> ternary q int8 [N][K]."""
+    _need(packed, torch.uint8, 2, "packed")
+    _on_gpu(packed)
+    N, K = packed.shape[0], packed.shape[1] * 4
+    return _relayout("bitlinear_unpack_weights", packed, N, K,
+                     torch.empty((N, K), dtype=torch.int8, device=packed.device))
 
 
 def quant_act(X: torch.Tensor, rmsnorm: bool = False, norm_gain: Optional[torch.Tensor] = None,
@@ -179,8 +235,11 @@ def quant_act(X: torch.Tensor, rmsnorm: bool = False, norm_gain: Optional[torch.
                torch.empty(M, dtype=torch.float32, device=X.device),
                torch.empty(M, dtype=torch.int32, device=X.device))
     xq, xs, rs = out
-    if norm_gain is not None:
-        _need(norm_gain, torch.float32, 1, "norm_gain")
+    _shape(xq, torch.int8, (M, K), "Xq")
+    _shape(xs, torch.float32, (M,), "x_scale")
+    _shape(rs, torch.int32, (M,), "x_rowsum")
+    _shape(norm_gain, torch.float32, (K,), "norm_gain")
+    _on_gpu(X, xq, xs, rs, norm_gain)
     _check(lib.bitlinear_quant_act(_p(X), M, K, BL_QUANT_RMSNORM if rmsnorm else 0, _p(norm_gain),
                                    float(eps), _p(xq), _p(xs), _p(rs), _stream(X.device)))
     return xq, xs, rs
@@ -202,6 +261,14 @@ def forward(xq: torch.Tensor, x_scale: torch.Tensor, packed: torch.Tensor, w_sca
     N = packed.shape[0]
     if packed.shape[1] * 4 != K:
         raise ValueError(f"packed has {packed.shape[1]} bytes per row, expected K/4 = {K // 4}")
+    _shape(x_scale, torch.float32, (M,), "x_scale")
+    _shape(x_rowsum, torch.int32, (M,), "x_rowsum")
+    _shape(w_scale, torch.float32, (1,), "w_scale")
+    for t, name in ((residual, "residual"), (mul_by, "mul_by"), (y_out, "y_out")):
+        _shape(t, torch.float32, (M, N), name)
+    if subln:
+        _shape(norm_gain, torch.float32, (N,), "norm_gain")
+    _on_gpu(xq, x_scale, x_rowsum, packed, w_scale, residual, mul_by, y_out, norm_gain)
     dev = xq.device
     flags = 0
     epi = Epilogue()
@@ -209,11 +276,9 @@ def forward(xq: torch.Tensor, x_scale: torch.Tensor, packed: torch.Tensor, w_sca
     if relu2:
         flags |= BL_EPI_RELU2
     if residual is not None:
-        _need(residual, torch.float32, 2, "residual")
         flags |= BL_EPI_RESIDUAL
         epi.residual = residual.data_ptr()
     if mul_by is not None:
-        _need(mul_by, torch.float32, 2, "mul_by")
         flags |= BL_EPI_MUL
         epi.mul_by = mul_by.data_ptr()
     if subln:
@@ -251,6 +316,9 @@ class QuantForward:
         _need(packed, torch.uint8, 2, "packed")
         self.packed, self.w_scale = packed, w_scale
         self.N, self.K = packed.shape[0], packed.shape[1] * 4
+        _shape(w_scale, torch.float32, (1,), "w_scale")
+        _shape(norm_gain, torch.float32, (self.K,), "norm_gain")
+        _on_gpu(packed, w_scale, norm_gain)
         self.qflags = BL_QUANT_RMSNORM if rmsnorm else 0
         self.gain, self.eps, self.relu2 = norm_gain, float(eps), relu2
         self.ws = _workspace(self.lib.bitlinear_quant_forward_workspace_bytes(max_m, self.K, self.N),
@@ -260,6 +328,11 @@ class QuantForward:
                  y_out: Optional[torch.Tensor] = None, mul_by: Optional[torch.Tensor] = None) -> torch.Tensor:
         _need(X, torch.float32, 2, "X")
         M = X.shape[0]
+        if X.shape[1] != self.K:
+            raise ValueError(f"X has {X.shape[1]} columns, the weights K = {self.K}")
+        for t, name in ((residual, "residual"), (mul_by, "mul_by"), (y_out, "y_out")):
+            _shape(t, torch.float32, (M, self.N), name)
+        _on_gpu(X, residual, mul_by, y_out)
         y = y_out if y_out is not None else torch.empty((M, self.N), dtype=torch.float32, device=X.device)
         epi = Epilogue()
         epi.flags = ((BL_EPI_RELU2 if self.relu2 else 0) | (BL_EPI_RESIDUAL if residual is not None else 0)
@@ -267,7 +340,6 @@ class QuantForward:
         if residual is not None:
             epi.residual = residual.data_ptr()
         if mul_by is not None:
-            _need(mul_by, torch.float32, 2, "mul_by")
             epi.mul_by = mul_by.data_ptr()
         _check(self.lib.bitlinear_quant_forward(_p(X), M, self.K, self.qflags, _p(self.gain), self.eps,
                                                 _p(self.packed), _p(self.w_scale), self.N, ctypes.byref(epi),
@@ -298,16 +370,19 @@ def latent_forward(X: torch.Tensor, W: torch.Tensor, rmsnorm: bool = False,
     N = W.shape[0]
     if W.shape[1] != K:
         raise ValueError(f"W has {W.shape[1]} columns, X has K = {K}")
+    for t, name in ((residual, "residual"), (mul_by, "mul_by"), (y_out, "y_out")):
+        _shape(t, torch.float32, (M, N), name)
+    _shape(norm_gain, torch.float32, (K,), "norm_gain")
+    _shape(w_scale_out, torch.float32, (1,), "w_scale_out")
+    _on_gpu(X, W, residual, mul_by, y_out, norm_gain, w_scale_out)
     dev = X.device
     y = y_out if y_out is not None else torch.empty((M, N), dtype=torch.float32, device=dev)
     epi = Epilogue()
     epi.flags = ((BL_EPI_RELU2 if relu2 else 0) | (BL_EPI_RESIDUAL if residual is not None else 0)
                  | (BL_EPI_MUL if mul_by is not None else 0))
     if residual is not None:
-        _need(residual, torch.float32, 2, "residual")
         epi.residual = residual.data_ptr()
     if mul_by is not None:
-        _need(mul_by, torch.float32, 2, "mul_by")
         epi.mul_by = mul_by.data_ptr()
     ws = _workspace(lib.bitlinear_latent_forward_workspace_bytes(M, K, N), dev)
     dt = BL_DTYPE_BF16 if W.dtype == torch.bfloat16 else BL_DTYPE_F32
@@ -317,12 +392,22 @@ def latent_forward(X: torch.Tensor, W: torch.Tensor, rmsnorm: bool = False,
     return y
 
 
-def make_layers(layers: Sequence[dict]):
+def make_layers(layers: Sequence[dict], H: Optional[int] = None, F: Optional[int] = None):
     """Host array of FFN layer descriptors from dicts of device tensors
     (keys: up, up_scale, down, down_scale, optional gate, gate_scale, pre_norm_gain,
-    sub_norm_gain)."""
+    sub_norm_gain); with H and F, every tensor's shape is checked."""
     arr = (FFNLayer * len(layers))()
     for i, L in enumerate(layers):
+        if H is not None and F is not None:
+            _shape(L["up"], torch.uint8, (F, H // 4), f"layer {i} up")
+            _shape(L["down"], torch.uint8, (H, F // 4), f"layer {i} down")
+            _shape(L.get("gate"), torch.uint8, (F, H // 4), f"layer {i} gate")
+            for k in ("up_scale", "down_scale", "gate_scale"):
+                _shape(L.get(k), torch.float32, (1,), f"layer {i} {k}")
+            _shape(L.get("pre_norm_gain"), torch.float32, (H,), f"layer {i} pre_norm_gain")
+            _shape(L.get("sub_norm_gain"), torch.float32, (F,), f"layer {i} sub_norm_gain")
+            _on_gpu(*(L.get(k) for k in ("up", "down", "gate", "up_scale", "down_scale", "gate_scale",
+                                         "pre_norm_gain", "sub_norm_gain")))
         arr[i].pre_norm_gain = None if L.get("pre_norm_gain") is None else L["pre_norm_gain"].data_ptr()
         arr[i].up = L["up"].data_ptr()
         arr[i].up_scale = L["up_scale"].data_ptr()
@@ -342,7 +427,7 @@ class FFNStack:
                  pre_norm: bool = True, residual: bool = True, eps: float = RMS_EPS):
         self.lib = load()
         self._keep = list(layers)
-        self.arr = make_layers(layers)
+        self.arr = make_layers(layers, H, F)
         self.n = len(layers)
         self.H, self.F = H, F
         self.flags = (BL_FFN_PRE_NORM if pre_norm else 0) | (BL_FFN_RESIDUAL if residual else 0)
@@ -352,11 +437,13 @@ class FFNStack:
     def __call__(self, hidden: torch.Tensor) -> torch.Tensor:
         _need(hidden, torch.float32, 2, "hidden")
         M = hidden.shape[0]
+        if hidden.shape[1] != self.H:
+            raise ValueError(f"hidden has {hidden.shape[1]} columns, the stack's H = {self.H}")
+        _on_gpu(hidden)
         _check(self.lib.bitnet_ffn_forward(self.arr, self.n, _p(hidden), M, self.H, self.F, self.flags,
                                            self.eps, _p(self.ws), 0 if self.ws is None else self.ws.numel(),
                                            _stream(hidden.device)))
         return hidden
-
 
 
 def ffn_forward(layers: Sequence[dict], hidden: torch.Tensor, pre_norm: bool = True,

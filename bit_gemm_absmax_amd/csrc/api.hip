@@ -31,6 +31,14 @@ int hip_status(hipError_t e, const char* where) {
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
+// Whether the byte ranges [a, a + na) and [b, b + nb) share a byte (NULL or
+// empty ranges share none).
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+    if (!a || !b || na == 0 || nb == 0) return false;
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return x < y + nb && y < x + na;
+}
+
 constexpr int64_t kLimit = (int64_t)1 << 31;
 constexpr size_t kWsAlign = 256;
 
@@ -154,6 +162,45 @@ int bitlinear_pack_weights(const float* W, int64_t N, int64_t K, uint8_t* packed
                       "pack");
 }
 
+// ---------------------------------------------------------------- packed-layout conversion
+
+}  // extern "C"
+
+namespace {
+int check_layout(const char* who, const void* in, size_t in_align, const void* out, size_t out_align,
+                 size_t out_elem, int64_t N, int64_t K) {
+    if (!in || !out) return fail(BL_ERR_NULL, "%s: input and output are required", who);
+    if (N < 1) return fail(BL_ERR_SHAPE, "%s: N = %lld must be >= 1", who, (long long)N);
+    if (K < 64 || K % 64 != 0)
+        return fail(BL_ERR_SHAPE, "%s: K = %lld must be a positive multiple of 64", who, (long long)K);
+    if (N * K >= kLimit * 4) return fail(BL_ERR_SHAPE, "%s: N*K too large", who);
+    if (!aligned(in, in_align) || !aligned(out, out_align))
+        return fail(BL_ERR_ALIGN, "%s: input needs %zu-byte, output %zu-byte alignment", who, in_align, out_align);
+    if (overlap(in, (size_t)(N * K / 4), out, (size_t)(N * K) * out_elem / 4))
+        return fail(BL_ERR_UNSUPPORTED, "%s: input and output overlap", who);
+    return BL_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int bitlinear_import_canonical(const uint8_t* canonical, int64_t N, int64_t K, uint8_t* packed,
+                               hipStream_t stream) {
+    if (int r = check_layout("import_canonical", canonical, 4, packed, 16, 1, N, K)) return r;
+    return hip_status(bl::launch_relayout(canonical, N, K, true, packed, stream), "import_canonical");
+}
+
+int bitlinear_export_canonical(const uint8_t* packed, int64_t N, int64_t K, uint8_t* canonical,
+                               hipStream_t stream) {
+    if (int r = check_layout("export_canonical", packed, 16, canonical, 4, 1, N, K)) return r;
+    return hip_status(bl::launch_relayout(packed, N, K, false, canonical, stream), "export_canonical");
+}
+
+int bitlinear_unpack_weights(const uint8_t* packed, int64_t N, int64_t K, int8_t* q, hipStream_t stream) {
+    if (int r = check_layout("unpack_weights", packed, 16, q, 16, 4, N, K)) return r;
+    return hip_status(bl::launch_unpack(packed, N, K, q, stream), "unpack_weights");
+}
+
 // ---------------------------------------------------------------- quantiser
 
 int bitlinear_quant_act(const float* X, int64_t M, int64_t K, uint32_t flags, const float* norm_gain,
@@ -168,6 +215,18 @@ int bitlinear_quant_act(const float* X, int64_t M, int64_t K, uint32_t flags, co
     if (!aligned(X, 16) || !aligned(Xq, 16) || !aligned(x_scale, 4) || !aligned(x_rowsum, 4) ||
         !aligned(norm_gain, 16))
         return fail(BL_ERR_ALIGN, "quant: X, Xq, norm_gain need 16-byte alignment, scales 4-byte");
+    {
+        const void* outs[3] = {Xq, x_scale, x_rowsum};
+        const size_t ob[3] = {(size_t)(M * K), (size_t)M * 4, (size_t)M * 4};
+        for (int o = 0; o < 3; ++o) {
+            if (overlap(outs[o], ob[o], X, (size_t)(M * K) * 4) ||
+                overlap(outs[o], ob[o], (flags & BL_QUANT_RMSNORM) ? norm_gain : nullptr, (size_t)K * 4))
+                return fail(BL_ERR_UNSUPPORTED, "quant: an output overlaps X or the norm gain");
+            for (int o2 = o + 1; o2 < 3; ++o2)
+                if (overlap(outs[o], ob[o], outs[o2], ob[o2]))
+                    return fail(BL_ERR_UNSUPPORTED, "quant: two outputs overlap");
+        }
+    }
     if (M == 0) return ok();
     const bool rms = (flags & BL_QUANT_RMSNORM) != 0;
     return hip_status(bl::launch_quant(X, M, K, rms, rms ? norm_gain : nullptr, norm_eps, Xq,
@@ -215,6 +274,26 @@ int bitlinear_forward(const int8_t* Xq, const float* x_scale, const int32_t* x_r
     if (subln && (!aligned(epi->out_q, 16) || !aligned(epi->out_q_scale, 4) ||
                   !aligned(epi->out_q_rowsum, 4) || !aligned(epi->norm_gain, 16)))
         return fail(BL_ERR_ALIGN, "forward: subln outputs/gain misaligned");
+    {
+        // outputs must not overlap the inputs, except Y == residual / mul_by
+        const size_t xb = (size_t)(M * K), yb = (size_t)(M * N) * 4, wb = (size_t)(N * K / 4);
+        const void* outs[5] = {Y, acc_out, subln ? epi->out_q : nullptr, subln ? epi->out_q_scale : nullptr,
+                               subln ? epi->out_q_rowsum : nullptr};
+        const size_t ob[5] = {yb, yb, (size_t)(M * N), (size_t)M * 4, (size_t)M * 4};
+        const void* ins[5] = {Xq, x_scale, x_rowsum, packed, w_scale};
+        const size_t ib[5] = {xb, (size_t)M * 4, (size_t)M * 4, wb, 4};
+        for (int o = 0; o < 5; ++o) {
+            for (int i = 0; i < 5; ++i)
+                if (overlap(outs[o], ob[o], ins[i], ib[i]))
+                    return fail(BL_ERR_UNSUPPORTED, "forward: an output overlaps an input");
+            for (int o2 = o + 1; o2 < 5; ++o2)
+                if (overlap(outs[o], ob[o], outs[o2], ob[o2]))
+                    return fail(BL_ERR_UNSUPPORTED, "forward: two outputs overlap");
+            const float* aux = (flags & BL_EPI_RESIDUAL) ? epi->residual : (flags & BL_EPI_MUL) ? epi->mul_by : nullptr;
+            if (aux && !(o == 0 && outs[o] == aux) && overlap(outs[o], ob[o], aux, yb))
+                return fail(BL_ERR_UNSUPPORTED, "forward: an output overlaps residual / mul_by (only Y == it is allowed)");
+        }
+    }
     const bool need_rowsum = (x_rowsum == nullptr);
     const bool need_y = subln && (Y == nullptr);
     if (int r = check_workspace(ws, ws_bytes, M == 0 ? 0 : forward_ws(M, N, need_rowsum, need_y)))
@@ -273,6 +352,15 @@ int check_quant_forward(const char* who, const float* X, int64_t M, int64_t K, u
         return fail(BL_ERR_SHAPE, "%s: sizes exceed 2^31 elements", who);
     if (!aligned(X, 16) || !aligned(Y, 16) || !aligned(norm_gain, 16))
         return fail(BL_ERR_ALIGN, "%s: X, Y, gain need 16-byte alignment", who);
+    // Every workgroup of the few-token launch reads all of X while others
+    // write Y, so Y may not overlap X (or the gain); it may equal residual or
+    // mul_by, and overlap them in no other way.
+    const size_t yb = (size_t)(M * N) * 4;
+    if (overlap(X, (size_t)(M * K) * 4, Y, yb) || overlap(norm_gain, (size_t)K * 4, Y, yb))
+        return fail(BL_ERR_UNSUPPORTED, "%s: Y overlaps X or the norm gain", who);
+    const float* aux = (flags & BL_EPI_RESIDUAL) ? epi->residual : (flags & BL_EPI_MUL) ? epi->mul_by : nullptr;
+    if (aux && aux != Y && overlap(aux, yb, Y, yb))
+        return fail(BL_ERR_UNSUPPORTED, "%s: Y overlaps residual / mul_by (only Y == it is allowed)", who);
     return BL_OK;
 }
 
@@ -393,6 +481,8 @@ int bitnet_ffn_forward(const bitnet_ffn_layer* layers, int32_t n_layers, float* 
     }
     if (int r = check_workspace(ws, ws_bytes, M == 0 || n_layers == 0 ? 0 : ffn_ws(M, H, F))) return r;
     if (M == 0 || n_layers == 0) return ok();
+    if (overlap(hidden, (size_t)(M * H) * 4, ws, ffn_ws(M, H, F)))
+        return fail(BL_ERR_UNSUPPORTED, "ffn: hidden overlaps the workspace");
 
     Carver c(ws);
     int8_t* xq1 = c.take<int8_t>((size_t)(M * H));

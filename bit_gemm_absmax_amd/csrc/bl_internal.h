@@ -29,6 +29,11 @@ int pack_partial_blocks(int64_t count);
 hipError_t launch_pack(const void* W, bool bf16, int64_t N, int64_t K, uint8_t* packed, float* w_scale,
                        double* partial, hipStream_t s);
 
+// Between the plain row-major 2-bit form and the tile layout (to_tile: plain
+// -> tile), and the tile layout -> int8 q [N][K].  K % 64 == 0.
+hipError_t launch_relayout(const uint8_t* in, int64_t N, int64_t K, bool to_tile, uint8_t* out, hipStream_t s);
+hipError_t launch_unpack(const uint8_t* packed, int64_t N, int64_t K, int8_t* q, hipStream_t s);
+
 // Per-row absmax quantisation with optional RMSNorm (gain may be null).
 hipError_t launch_quant(const float* X, int64_t M, int64_t K, bool rmsnorm,
                         const float* gain, float eps, int8_t* Xq, float* scale,

@@ -41,9 +41,7 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 // depth for K, at most QMAX by the plan below).  GATED: a second matrix Wg
 // (the gate) of the same shape is streamed by the same lanes against the
 // same quantised rows, and the output is ReLU^2(gate) * up (Wp is up).
-// CT > 1 (very tall matrices): the workgroup owns CT adjacent 16-row tiles,
-// so one quantisation of the rows serves 16 CT outputs.
-template <int NWV, int QMAX, bool GATED, int NV, int CT = 1>
+template <int NWV, int QMAX, bool GATED, int NV>
 __global__ __launch_bounds__(NWV* kWave) void k_decode(const float* __restrict__ X, int M, int K, int rmsnorm,
                                                         const float* __restrict__ gain, float eps,
                                                         const uint8_t* __restrict__ Wp,
@@ -51,7 +49,7 @@ __global__ __launch_bounds__(NWV* kWave) void k_decode(const float* __restrict__
                                                         uint32_t epi_flags, const float* aux, float* Y,
                                                         const uint8_t* __restrict__ Wg,
                                                         const float* __restrict__ g_scale) {
-    static_assert(!GATED || CT == 1, "a gated launch streams one tile of each matrix");
+    constexpr int CT = 1;  // one 16-row output tile per workgroup
     static_assert(4 * 16 * CT <= NWV * kWave, "one epilogue thread per output");
     constexpr int NT = NWV * kWave;
     constexpr int COLS = 16 * CT;
@@ -713,21 +711,20 @@ bool plan(int64_t K, Plan& p) {
     return true;
 }
 
-template <int NWV, int Q, bool G, int NV, int CT = 1>
+template <int NWV, int Q, bool G, int NV>
 hipError_t go_decode(const float* X, int64_t M, int64_t K, bool rms, const float* gain, float eps,
                      const uint8_t* packed, const float* ws, int64_t N, uint32_t epi, const float* aux, float* Y,
                      const uint8_t* gate, const float* gate_scale, hipStream_t s) {
-    const unsigned blocks = (unsigned)((N + 16 * CT - 1) / (16 * CT));
-    const size_t red = (size_t)NWV * 16 * 16 * sizeof(int) * (G ? 2 : CT);
+    const unsigned blocks = (unsigned)((N + 15) / 16);
+    const size_t red = (size_t)NWV * 16 * 16 * sizeof(int) * (G ? 2 : 1);
     const size_t lds = 4 * (size_t)K + red;
-    hipLaunchKernelGGL((k_decode<NWV, Q, G, NV, CT>), dim3(blocks), dim3(NWV * kWave), lds, s, X, (int)M, (int)K,
+    hipLaunchKernelGGL((k_decode<NWV, Q, G, NV>), dim3(blocks), dim3(NWV * kWave), lds, s, X, (int)M, (int)K,
                        rms ? 1 : 0, gain, eps, packed, ws, (int)N, epi, aux, Y, gate, gate_scale);
     return hipGetLastError();
 }
 
 // Very tall matrices (at least 2048 tiles of 16 rows, eight per CU): the
-// persistent streaming launch, kStreamCT tiles per group (0: the one-shot
-// launch with four tiles per workgroup instead).
+// persistent streaming launch, kStreamCT tiles per group.
 constexpr int64_t kTallTiles = 2048;
 constexpr int kStreamCT = 1;
 
@@ -772,10 +769,7 @@ hipError_t go_decode_plan(const Plan& p, const float* X, int64_t M, int64_t K, b
 #define BL_DEC(NWV, Q, NV)                                                                                     \
     if (p.nw == NWV && p.qmax == Q && nv == NV)                                                                \
         return !tall ? go_decode<NWV, Q, G, NV>(X, M, K, rms, gain, eps, packed, ws, N, epi, aux, Y, gate, gate_scale, s) \
-               : kStreamCT > 0                                                                                 \
-                   ? go_decode_stream<NWV, NV, (kStreamCT > 0 ? kStreamCT : 1)>(X, M, K, rms, gain, eps, packed, ws, N, epi, aux, Y, s) \
-                   : go_decode<NWV, Q, G, NV, G ? 1 : 4>(X, M, K, rms, gain, eps, packed, ws, N, epi, aux, Y, gate,   \
-                                                         gate_scale, s);
+                     : go_decode_stream<NWV, NV, kStreamCT>(X, M, K, rms, gain, eps, packed, ws, N, epi, aux, Y, s);
     BL_DEC(4, 2, 1)
     BL_DEC(4, 2, 2)
     BL_DEC(4, 4, 3)

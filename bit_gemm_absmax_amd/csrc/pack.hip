@@ -111,6 +111,53 @@ __global__ __launch_bounds__(kThreads) void k_ternary_pack(const void* __restric
     }
 }
 
+// The plain row-major 2-bit form (weight k of row n in byte n K/4 + k/4 at
+// bits 2 (k % 4)) and this library's tile-grouped layout hold the same 32-bit
+// words of 16 consecutive weights, in different places and with the 2-bit
+// fields transposed: in the plain word, byte j field b is weight 4j + b; in
+// the tile word, byte b field j is.  The transpose is its own inverse, so one
+// kernel converts either way (TO_TILE picks which index is read).
+__device__ __forceinline__ uint32_t transpose_fields(uint32_t w) {
+    uint32_t t = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) t |= ((w >> (8 * j + 2 * b)) & 3u) << (8 * b + 2 * j);
+    return t;
+}
+
+// Word index of group g (16 weights) of row n in the tile layout.
+__device__ __forceinline__ int64_t tile_word(int64_t n, int64_t g, int64_t N, int64_t K) {
+    const int64_t t = n / 16;
+    const int64_t R = N - 16 * t < 16 ? N - 16 * t : 16;
+    return t * K + 4 * ((g / 4) * R + (n % 16)) + (g % 4);
+}
+
+template <bool TO_TILE>
+__global__ __launch_bounds__(kThreads) void k_relayout(const uint32_t* __restrict__ in, int64_t nwords, int64_t N,
+                                                       int64_t K, uint32_t* __restrict__ out) {
+    const int64_t stride = (int64_t)gridDim.x * kThreads;
+    const int64_t gpr = K / 16;
+    for (int64_t w = (int64_t)blockIdx.x * kThreads + threadIdx.x; w < nwords; w += stride) {
+        const int64_t tw = tile_word(w / gpr, w % gpr, N, K);
+        if (TO_TILE) out[tw] = transpose_fields(in[w]);
+        else out[w] = transpose_fields(in[tw]);
+    }
+}
+
+// Tile layout -> int8 q [N][K]: the tile word of group g of row n gives the
+// 16 weights 16g .. 16g + 15 of the row, four consecutive ones per field
+// shift (signed4), stored as one 16-byte write.
+__global__ __launch_bounds__(kThreads) void k_unpack(const uint32_t* __restrict__ packed, int64_t nwords, int64_t N,
+                                                     int64_t K, int4* __restrict__ q) {
+    const int64_t stride = (int64_t)gridDim.x * kThreads;
+    const int64_t gpr = K / 16;
+    for (int64_t w = (int64_t)blockIdx.x * kThreads + threadIdx.x; w < nwords; w += stride) {
+        const uint32_t v = packed[tile_word(w / gpr, w % gpr, N, K)];
+        q[w] = make_int4(signed4(v, 0), signed4(v, 1), signed4(v, 2), signed4(v, 3));
+    }
+}
+
 }  // namespace
 
 int pack_partial_blocks(int64_t count) {
@@ -141,6 +188,31 @@ hipError_t launch_pack(const void* W, bool bf16, int64_t N, int64_t K, uint8_t* 
                        double* partial, hipStream_t s) {
     return bf16 ? go_pack<InBF16>(W, N, K, packed, w_scale, partial, s)
                 : go_pack<InF32>(W, N, K, packed, w_scale, partial, s);
+}
+
+namespace {
+unsigned word_blocks(int64_t nwords) {
+    int64_t blocks = (nwords + kThreads - 1) / kThreads;
+    return (unsigned)(blocks > 8192 ? 8192 : blocks < 1 ? 1 : blocks);
+}
+}  // namespace
+
+hipError_t launch_relayout(const uint8_t* in, int64_t N, int64_t K, bool to_tile, uint8_t* out, hipStream_t s) {
+    const int64_t nwords = N * K / 16;
+    const uint32_t* i = reinterpret_cast<const uint32_t*>(in);
+    uint32_t* o = reinterpret_cast<uint32_t*>(out);
+    if (to_tile)
+        hipLaunchKernelGGL(k_relayout<true>, dim3(word_blocks(nwords)), dim3(kThreads), 0, s, i, nwords, N, K, o);
+    else
+        hipLaunchKernelGGL(k_relayout<false>, dim3(word_blocks(nwords)), dim3(kThreads), 0, s, i, nwords, N, K, o);
+    return hipGetLastError();
+}
+
+hipError_t launch_unpack(const uint8_t* packed, int64_t N, int64_t K, int8_t* q, hipStream_t s) {
+    const int64_t nwords = N * K / 16;
+    hipLaunchKernelGGL(k_unpack, dim3(word_blocks(nwords)), dim3(kThreads), 0, s,
+                       reinterpret_cast<const uint32_t*>(packed), nwords, N, K, reinterpret_cast<int4*>(q));
+    return hipGetLastError();
 }
 
 }  // namespace bl

@@ -90,7 +90,7 @@ const char* bitlinear_last_error(void);
 
 /* ABI version of this header, (major << 16) | minor. */
 int bitlinear_abi_version(void);
-#define BITLINEAR_ABI_VERSION ((1 << 16) | 2)
+#define BITLINEAR_ABI_VERSION ((1 << 16) | 3)
 
 /* ------------------------------------------------------------------------
  * Weight packing ("Model details" / Quantization: absmean ternary weights).
@@ -112,6 +112,33 @@ int bitlinear_pack_weights(const float* W, int64_t N, int64_t K,
                            void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * Packed-layout conversion ("Model variants": packed 1.58-bit weights for
+ * deployment; the page gives no byte layout).
+ *
+ * The plain ("canonical") 2-bit form is row-major [N][K/4] bytes with the
+ * code q + 1 of weight k of row n in byte n*(K/4) + k/4 at bits 2*(k%4),
+ * four consecutive weights per byte, lowest bits first.  It holds the same
+ * numbers as the tile layout above, which is what every other call reads.
+ *
+ * bitlinear_import_canonical: canonical u8 [N][K/4] (4-byte aligned) ->
+ *                             packed u8 [N][K/4] in the tile layout.
+ * bitlinear_export_canonical: the inverse (packed 16-byte aligned, canonical
+ *                             4-byte aligned).
+ * bitlinear_unpack_weights:   packed -> q int8 [N][K] in {-1, 0, 1}
+ *                             (16-byte aligned).
+ * Both directions are exact and lossless.  Inputs must hold codes 0..2 only;
+ * a code 3 is outside the contract (it is carried through, and unpacks to 2).
+ * K must be a positive multiple of 64; input and output must not overlap.
+ * The weight scale gamma_w is unaffected: keep it beside either form.
+ * ---------------------------------------------------------------------- */
+int bitlinear_import_canonical(const uint8_t* canonical, int64_t N, int64_t K,
+                               uint8_t* packed, hipStream_t stream);
+int bitlinear_export_canonical(const uint8_t* packed, int64_t N, int64_t K,
+                               uint8_t* canonical, hipStream_t stream);
+int bitlinear_unpack_weights(const uint8_t* packed, int64_t N, int64_t K,
+                             int8_t* q, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * Activation quantisation ("Model details" / Quantization: per-token absmax
  * 8-bit activations), optionally preceded by RMSNorm with a gain and no bias
  * ("Model details" / Architecture; eps from "BitNetConfig").
@@ -129,6 +156,7 @@ int bitlinear_pack_weights(const float* W, int64_t N, int64_t K,
  * Xq        out  int8 [M][K]
  * x_scale   out  fp32 [M], gamma_x
  * x_rowsum  out  int32 [M], may be NULL
+ * No output may overlap X, the gain or another output (BL_ERR_UNSUPPORTED).
  * ---------------------------------------------------------------------- */
 #define BL_QUANT_RMSNORM 0x1u
 int bitlinear_quant_act(const float* X, int64_t M, int64_t K, uint32_t flags,
@@ -161,8 +189,8 @@ int bitlinear_quant_act(const float* X, int64_t M, int64_t K, uint32_t flags,
  * epi        in  host pointer to a bl_epilogue, or NULL for plain dequant
  * Y          out fp32 [M][N]; may be NULL only with BL_EPI_SUBLN_QUANT.
  *                With BL_EPI_RESIDUAL (BL_EPI_MUL), Y may equal residual
- *                (mul_by), in place; any other overlap between outputs and
- *                inputs is not allowed.
+ *                (mul_by), in place; any other overlap between an output and
+ *                an input or another output is rejected (BL_ERR_UNSUPPORTED).
  * acc_out    out int32 [M][N], the exact accumulators, or NULL
  * ws         scratch of bitlinear_forward_workspace_bytes(M, K, N, flags)
  * ---------------------------------------------------------------------- */
@@ -204,7 +232,10 @@ int bitlinear_forward(const int8_t* Xq, const float* x_scale,
  * epi         in  host pointer or NULL; BL_EPI_RELU2, BL_EPI_RESIDUAL and
  *                 BL_EPI_MUL are accepted here (BL_ERR_UNSUPPORTED otherwise)
  * Y           out fp32 [M][N]; may equal epi->residual or epi->mul_by
- *                 (in place)
+ *                 (in place).  Y must not overlap X or norm_gain, nor
+ *                 residual / mul_by other than by being equal to it
+ *                 (BL_ERR_UNSUPPORTED): for a few tokens every workgroup
+ *                 reads all of X while others write Y.
  * ws          scratch of bitlinear_quant_forward_workspace_bytes(M, K, N)
  * ---------------------------------------------------------------------- */
 size_t bitlinear_quant_forward_workspace_bytes(int64_t M, int64_t K, int64_t N);
@@ -233,7 +264,7 @@ int bitlinear_quant_forward(const float* X, int64_t M, int64_t K, uint32_t quant
  *                 (BL_DTYPE_BF16, widened exactly to fp32); 16-byte aligned
  * epi         in  host pointer or NULL; BL_EPI_RELU2, BL_EPI_RESIDUAL and
  *                 BL_EPI_MUL as in bitlinear_quant_forward
- * Y           out fp32 [M][N]
+ * Y           out fp32 [M][N] (overlap rules of bitlinear_quant_forward)
  * w_scale     out fp32 [1], gamma_w, or NULL (kept in the workspace)
  * ws          scratch of bitlinear_latent_forward_workspace_bytes(M, K, N):
  *             the packed weights (N*K/4 bytes) and the quantised rows
@@ -267,7 +298,8 @@ int bitlinear_latent_forward(const float* X, int64_t M, int64_t K, uint32_t quan
  * hidden     in/out fp32 [M][H]
  * norm_eps   eps of both RMSNorms (1e-5)
  * ws         scratch of bitnet_ffn_workspace_bytes(M, H, F); calls that
- *            share one workspace must not overlap in time.
+ *            share one workspace must not overlap in time, and hidden must
+ *            not lie in the workspace (BL_ERR_UNSUPPORTED).
  * A gate matrix needs its scale (gate_scale) and has the up matrix's shape.
  * ---------------------------------------------------------------------- */
 #define BL_FFN_PRE_NORM 0x1u

@@ -46,7 +46,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.bitlinear_abi_version() == (1 << 16) | 2
+    assert lib.bitlinear_abi_version() == (1 << 16) | 3
     for s in range(-6, 1):
         assert lib.bitlinear_status_string(s)
     assert lib.bitlinear_status_string(-99) == b"unknown status"
@@ -70,6 +70,7 @@ B = ctypes.c_void_p(2 << 20)
 C = ctypes.c_void_p(3 << 20)
 D = ctypes.c_void_p(4 << 20)
 MIS = ctypes.c_void_p((5 << 20) + 4)
+Y = ctypes.c_void_p(6 << 20)   # an output far from every input above
 
 
 def test_pack_validation(lib):
@@ -102,31 +103,31 @@ def test_forward_validation(lib):
     f = lib.bitlinear_forward
     E = bl.Epilogue
     nul = ctypes.POINTER(E)()
-    assert f(None, B, None, 1, 64, C, D, 8, nul, A, None, None, 0, None) == bl.BL_ERR_NULL
+    assert f(None, B, None, 1, 64, C, D, 8, nul, Y, None, None, 0, None) == bl.BL_ERR_NULL
     assert f(A, B, None, 1, 64, C, D, 8, nul, None, None, None, 0, None) == bl.BL_ERR_NULL
-    assert f(A, B, None, 1, 63, C, D, 8, nul, A, None, None, 0, None) == bl.BL_ERR_SHAPE
-    assert f(A, B, None, 1, 64, C, D, 0, nul, A, None, None, 0, None) == bl.BL_ERR_SHAPE
-    assert f(A, B, None, -2, 64, C, D, 8, nul, A, None, None, 0, None) == bl.BL_ERR_SHAPE
+    assert f(A, B, None, 1, 63, C, D, 8, nul, Y, None, None, 0, None) == bl.BL_ERR_SHAPE
+    assert f(A, B, None, 1, 64, C, D, 0, nul, Y, None, None, 0, None) == bl.BL_ERR_SHAPE
+    assert f(A, B, None, -2, 64, C, D, 8, nul, Y, None, None, 0, None) == bl.BL_ERR_SHAPE
     assert f(A, B, None, 1, 64, C, D, 8, nul, MIS, None, None, 0, None) == bl.BL_ERR_ALIGN
     # missing workspace when the row sums must be computed
-    assert f(A, B, None, 1, 64, C, D, 8, nul, A, None, None, 0, None) == bl.BL_ERR_WORKSPACE
+    assert f(A, B, None, 1, 64, C, D, 8, nul, Y, None, None, 0, None) == bl.BL_ERR_WORKSPACE
     e = E(flags=bl.BL_EPI_RESIDUAL)
-    assert f(A, B, D, 1, 64, C, D, 8, ctypes.byref(e), A, None, None, 0, None) == bl.BL_ERR_NULL
+    assert f(A, B, D, 1, 64, C, D, 8, ctypes.byref(e), Y, None, None, 0, None) == bl.BL_ERR_NULL
     e = E(flags=bl.BL_EPI_SUBLN_QUANT)
-    assert f(A, B, D, 1, 64, C, D, 64, ctypes.byref(e), A, None, None, 0, None) == bl.BL_ERR_NULL
+    assert f(A, B, D, 1, 64, C, D, 64, ctypes.byref(e), Y, None, None, 0, None) == bl.BL_ERR_NULL
     e = E(flags=bl.BL_EPI_SUBLN_QUANT, out_q=A.value, out_q_scale=B.value)
-    assert f(A, B, D, 1, 64, C, D, 72, ctypes.byref(e), A, None, None, 0, None) == bl.BL_ERR_SHAPE
+    assert f(A, B, D, 1, 64, C, D, 72, ctypes.byref(e), Y, None, None, 0, None) == bl.BL_ERR_SHAPE
     e = E(flags=0x40)
-    assert f(A, B, D, 1, 64, C, D, 8, ctypes.byref(e), A, None, None, 0, None) == bl.BL_ERR_UNSUPPORTED
+    assert f(A, B, D, 1, 64, C, D, 8, ctypes.byref(e), Y, None, None, 0, None) == bl.BL_ERR_UNSUPPORTED
     # gating product: needs mul_by, 16-byte aligned, and not with the residual add
     e = E(flags=bl.BL_EPI_MUL)
-    assert f(A, B, D, 1, 64, C, D, 8, ctypes.byref(e), A, None, None, 0, None) == bl.BL_ERR_NULL
+    assert f(A, B, D, 1, 64, C, D, 8, ctypes.byref(e), Y, None, None, 0, None) == bl.BL_ERR_NULL
     e = E(flags=bl.BL_EPI_MUL, mul_by=MIS.value)
-    assert f(A, B, D, 1, 64, C, D, 8, ctypes.byref(e), A, None, None, 0, None) == bl.BL_ERR_ALIGN
+    assert f(A, B, D, 1, 64, C, D, 8, ctypes.byref(e), Y, None, None, 0, None) == bl.BL_ERR_ALIGN
     e = E(flags=bl.BL_EPI_MUL | bl.BL_EPI_RESIDUAL, mul_by=A.value, residual=B.value)
-    assert f(A, B, D, 1, 64, C, D, 8, ctypes.byref(e), A, None, None, 0, None) == bl.BL_ERR_UNSUPPORTED
+    assert f(A, B, D, 1, 64, C, D, 8, ctypes.byref(e), Y, None, None, 0, None) == bl.BL_ERR_UNSUPPORTED
     # empty batch with everything else valid
-    assert f(A, B, D, 0, 64, C, D, 8, nul, A, None, None, 0, None) == bl.BL_OK
+    assert f(A, B, D, 0, 64, C, D, 8, nul, Y, None, None, 0, None) == bl.BL_OK
 
 
 def test_ffn_validation(lib):
@@ -159,25 +160,134 @@ def test_binding_raises_on_bad_tensor():
         bl.pack_weights(torch.zeros(4, 64))  # CPU tensor: rejected before any C call
 
 
+def test_binding_checks_shapes_before_any_call():
+    """Every tensor argument's dtype and exact shape is checked against M, K
+    and N before the library is called (the C layer trusts the sizes); CPU
+    tensors of the right shapes are then refused as not on the GPU."""
+    import torch
+    M, K, N = 3, 128, 40
+    xq = torch.zeros(M, K, dtype=torch.int8)
+    xs, rs = torch.zeros(M), torch.zeros(M, dtype=torch.int32)
+    packed, ws = torch.zeros(N, K // 4, dtype=torch.uint8), torch.zeros(1)
+    good = dict(x_rowsum=rs)
+    cases = [
+        (dict(x_scale=torch.zeros(M + 1)), "x_scale"),
+        (dict(x_rowsum=torch.zeros(M, dtype=torch.int64)), "x_rowsum"),
+        (dict(w_scale=torch.zeros(2)), "w_scale"),
+        (dict(residual=torch.zeros(M, N + 1)), "residual"),
+        (dict(mul_by=torch.zeros(M + 1, N)), "mul_by"),
+        (dict(y_out=torch.zeros(M, N - 1)), "y_out"),
+        (dict(subln=True, norm_gain=torch.zeros(K)), "norm_gain"),
+    ]
+    for kw, name in cases:
+        args = dict(xq=xq, x_scale=xs, packed=packed, w_scale=ws, **good)
+        args.update(kw)
+        with pytest.raises((ValueError, TypeError), match=name):
+            bl.forward(**args)
+    with pytest.raises(ValueError, match="GPU"):
+        bl.forward(xq, xs, packed, ws, x_rowsum=rs)
+    with pytest.raises(ValueError, match="bytes per row"):
+        bl.forward(xq, xs, torch.zeros(N, K // 4 + 16, dtype=torch.uint8), ws)
+    X = torch.zeros(M, K)
+    with pytest.raises(ValueError, match="norm_gain"):
+        bl.quant_act(X, rmsnorm=True, norm_gain=torch.zeros(K + 4))
+    with pytest.raises(ValueError, match="Xq"):
+        bl.quant_act(X, out=(torch.zeros(M, K - 64, dtype=torch.int8), xs, rs))
+    with pytest.raises(ValueError, match="GPU"):
+        bl.quant_act(X)
+    with pytest.raises(ValueError, match="columns"):
+        bl.latent_forward(X, torch.zeros(N, K + 64))
+    with pytest.raises(ValueError, match="w_scale_out"):
+        bl.latent_forward(X, torch.zeros(N, K), w_scale_out=torch.zeros(2))
+    with pytest.raises(ValueError, match="GPU"):
+        bl.unpack_weights(packed)
+    with pytest.raises(TypeError):
+        bl.import_canonical(torch.zeros(N, K // 4))
+    # the FFN stack: every layer tensor against H and F, and hidden against H
+    H, F = 64, 128
+    L = {"up": torch.zeros(F, H // 4, dtype=torch.uint8), "up_scale": torch.zeros(1),
+         "down": torch.zeros(H, F // 4, dtype=torch.uint8), "down_scale": torch.zeros(1)}
+    for key, bad in (("up", torch.zeros(F, H // 4 + 1, dtype=torch.uint8)), ("down_scale", torch.zeros(3)),
+                     ("sub_norm_gain", torch.zeros(H)), ("gate", torch.zeros(H, F // 4, dtype=torch.uint8))):
+        with pytest.raises(ValueError, match=key):
+            bl.make_layers([dict(L, **{key: bad})], H, F)
+    with pytest.raises(ValueError, match="GPU"):
+        bl.make_layers([L], H, F)
+
+
+def test_layout_validation(lib):
+    for f, in_al, out_al in ((lib.bitlinear_import_canonical, 4, 16), (lib.bitlinear_export_canonical, 16, 4),
+                             (lib.bitlinear_unpack_weights, 16, 16)):
+        assert f(None, 4, 64, B, None) == bl.BL_ERR_NULL
+        assert f(A, 4, 64, None, None) == bl.BL_ERR_NULL
+        assert f(A, 0, 64, B, None) == bl.BL_ERR_SHAPE
+        assert f(A, 4, 96, B, None) == bl.BL_ERR_SHAPE
+        assert f(A, 4, 0, B, None) == bl.BL_ERR_SHAPE
+        assert f(ctypes.c_void_p(A.value + in_al // 2), 4, 64, B, None) == bl.BL_ERR_ALIGN
+        assert f(A, 4, 64, ctypes.c_void_p(B.value + out_al // 2), None) == bl.BL_ERR_ALIGN
+        # input and output ranges overlap (4 x 64 weights: 64 packed bytes)
+        assert f(A, 4, 64, ctypes.c_void_p(A.value + 32), None) == bl.BL_ERR_UNSUPPORTED
+        assert b"overlap" in lib.bitlinear_last_error()
+
+
+def test_overlap_rules(lib):
+    """Outputs may not overlap inputs (or other outputs); the one allowed
+    alias is Y equal to residual / mul_by.  Rejected before any launch."""
+    E = bl.Epilogue
+    nul = ctypes.POINTER(E)()
+    M, K, N = 2, 64, 16
+    # quant_forward: Y over X (in-place hidden = hidden + W.norm(hidden) with K == N)
+    qf = lib.bitlinear_quant_forward
+    assert qf(A, M, K, 0, None, 1e-5, B, C, K, nul, A, None, 0, None) == bl.BL_ERR_UNSUPPORTED
+    assert b"overlaps X" in lib.bitlinear_last_error()
+    assert qf(A, M, K, 0, None, 1e-5, B, C, N, nul, ctypes.c_void_p(A.value + 256), None, 0, None) == \
+        bl.BL_ERR_UNSUPPORTED
+    e = E(flags=bl.BL_EPI_RESIDUAL, residual=Y.value + 64)   # partly over Y
+    assert qf(A, M, K, 0, None, 1e-5, B, C, N, ctypes.byref(e), Y, None, 0, None) == bl.BL_ERR_UNSUPPORTED
+    e = E(flags=bl.BL_EPI_RESIDUAL, residual=Y.value)        # exactly Y: in place, allowed
+    assert qf(A, 0, K, 0, None, 1e-5, B, C, N, ctypes.byref(e), Y, None, 0, None) == bl.BL_OK
+    g = ctypes.c_void_p(Y.value + 32)                        # the gain inside Y
+    assert qf(A, M, K, 1, g, 1e-5, B, C, N, nul, Y, None, 0, None) == bl.BL_ERR_UNSUPPORTED
+    lf = lib.bitlinear_latent_forward
+    assert lf(A, M, K, 0, None, 1e-5, B, bl.BL_DTYPE_F32, K, nul, A, None, None, 0, None) == bl.BL_ERR_UNSUPPORTED
+    # forward: Y over Xq, acc over Y, out_q over the weights
+    fw = lib.bitlinear_forward
+    assert fw(A, B, C, M, K, D, B, N, nul, A, None, None, 0, None) == bl.BL_ERR_UNSUPPORTED
+    assert fw(A, B, C, M, K, D, ctypes.c_void_p(B.value + 64), N, nul, Y, Y, None, 0, None) == \
+        bl.BL_ERR_UNSUPPORTED
+    e = E(flags=bl.BL_EPI_SUBLN_QUANT, out_q=D.value, out_q_scale=Y.value + 4096)
+    assert fw(A, B, C, M, K, D, ctypes.c_void_p(B.value + 64), 64, ctypes.byref(e), Y, None, None, 0, None) == \
+        bl.BL_ERR_UNSUPPORTED
+    # quant_act: Xq over X
+    qa = lib.bitlinear_quant_act
+    assert qa(A, M, K, 0, None, 1e-5, ctypes.c_void_p(A.value + 128), B, C, None) == bl.BL_ERR_UNSUPPORTED
+    assert qa(A, M, K, 0, None, 1e-5, B, C, C, None) == bl.BL_ERR_UNSUPPORTED   # scale over rowsum
+    # ffn: hidden inside the workspace
+    f = lib.bitnet_ffn_forward
+    L = (bl.FFNLayer * 1)()
+    L[0].up, L[0].up_scale, L[0].down, L[0].down_scale = A.value, B.value, C.value, D.value
+    assert f(L, 1, ctypes.c_void_p(Y.value + 512), 1, 64, 64, 3, 1e-5, Y, 1 << 20, None) == bl.BL_ERR_UNSUPPORTED
+
+
 def test_quant_forward_validation(lib):
     f = lib.bitlinear_quant_forward
     E = bl.Epilogue
     nul = ctypes.POINTER(E)()
-    assert f(None, 1, 64, 0, None, 1e-5, B, C, 8, nul, D, None, 0, None) == bl.BL_ERR_NULL
+    assert f(None, 1, 64, 0, None, 1e-5, B, C, 8, nul, Y, None, 0, None) == bl.BL_ERR_NULL
     assert f(A, 1, 64, 0, None, 1e-5, B, C, 8, nul, None, None, 0, None) == bl.BL_ERR_NULL
-    assert f(A, 1, 64, 0x4, None, 1e-5, B, C, 8, nul, D, None, 0, None) == bl.BL_ERR_UNSUPPORTED
+    assert f(A, 1, 64, 0x4, None, 1e-5, B, C, 8, nul, Y, None, 0, None) == bl.BL_ERR_UNSUPPORTED
     e = E(flags=bl.BL_EPI_SUBLN_QUANT)
-    assert f(A, 1, 64, 0, None, 1e-5, B, C, 8, ctypes.byref(e), D, None, 0, None) == bl.BL_ERR_UNSUPPORTED
+    assert f(A, 1, 64, 0, None, 1e-5, B, C, 8, ctypes.byref(e), Y, None, 0, None) == bl.BL_ERR_UNSUPPORTED
     e = E(flags=bl.BL_EPI_RESIDUAL)
-    assert f(A, 1, 64, 0, None, 1e-5, B, C, 8, ctypes.byref(e), D, None, 0, None) == bl.BL_ERR_NULL
+    assert f(A, 1, 64, 0, None, 1e-5, B, C, 8, ctypes.byref(e), Y, None, 0, None) == bl.BL_ERR_NULL
     e = E(flags=bl.BL_EPI_MUL)
-    assert f(A, 1, 64, 0, None, 1e-5, B, C, 8, ctypes.byref(e), D, None, 0, None) == bl.BL_ERR_NULL
+    assert f(A, 1, 64, 0, None, 1e-5, B, C, 8, ctypes.byref(e), Y, None, 0, None) == bl.BL_ERR_NULL
     e = E(flags=bl.BL_EPI_MUL | bl.BL_EPI_RESIDUAL, mul_by=A.value, residual=B.value)
-    assert f(A, 1, 64, 0, None, 1e-5, B, C, 8, ctypes.byref(e), D, None, 0, None) == bl.BL_ERR_UNSUPPORTED
-    assert f(A, 1, 96, 0, None, 1e-5, B, C, 8, nul, D, None, 0, None) == bl.BL_ERR_SHAPE
-    assert f(A, 1, 64, 0, None, 1e-5, B, C, 0, nul, D, None, 0, None) == bl.BL_ERR_SHAPE
+    assert f(A, 1, 64, 0, None, 1e-5, B, C, 8, ctypes.byref(e), Y, None, 0, None) == bl.BL_ERR_UNSUPPORTED
+    assert f(A, 1, 96, 0, None, 1e-5, B, C, 8, nul, Y, None, 0, None) == bl.BL_ERR_SHAPE
+    assert f(A, 1, 64, 0, None, 1e-5, B, C, 0, nul, Y, None, 0, None) == bl.BL_ERR_SHAPE
     assert f(A, 1, 64, 0, None, 1e-5, B, C, 8, nul, MIS, None, 0, None) == bl.BL_ERR_ALIGN
-    assert f(A, 0, 64, 0, None, 1e-5, B, C, 8, nul, D, None, 0, None) == bl.BL_OK
+    assert f(A, 0, 64, 0, None, 1e-5, B, C, 8, nul, Y, None, 0, None) == bl.BL_OK
     assert lib.bitlinear_quant_forward_workspace_bytes(64, 2560, 6912) >= 64 * 2560
 
 
@@ -233,8 +343,11 @@ def test_no_device_gives_hip_status(lib):
     calls = {
         "pack": lambda: lib.bitlinear_pack_weights(A, 4, 64, B, D, WS, WSN, None),
         "quant": lambda: lib.bitlinear_quant_act(A, 2, 64, 0, None, 1e-5, B, D, None, None),
-        "forward": lambda: lib.bitlinear_forward(A, B, None, 2, 64, D, B, 8, nul, A, None, WS, WSN, None),
-        "quant_forward": lambda: lib.bitlinear_quant_forward(A, 2, 64, 0, None, 1e-5, B, D, 8, nul, A, WS, WSN, None),
+        "forward": lambda: lib.bitlinear_forward(A, B, None, 2, 64, D, B, 8, nul, Y, None, WS, WSN, None),
+        "quant_forward": lambda: lib.bitlinear_quant_forward(A, 2, 64, 0, None, 1e-5, B, D, 8, nul, Y, WS, WSN, None),
+        "import": lambda: lib.bitlinear_import_canonical(A, 4, 64, B, None),
+        "export": lambda: lib.bitlinear_export_canonical(A, 4, 64, B, None),
+        "unpack": lambda: lib.bitlinear_unpack_weights(A, 4, 64, B, None),
         "latent_forward": lambda: lib.bitlinear_latent_forward(A, 2, 64, 0, None, 1e-5, B, bl.BL_DTYPE_F32, 8, nul,
                                                                D, None, WS, WSN, None),
     }
