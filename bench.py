@@ -11,6 +11,11 @@ rotate over enough packed copies that every step reads them from HBM, not
 from the 256 MB Infinity Cache.  A second figure times the same chain at
 M=4096 (prefill, seed 3) and reports int8 TOPS of the two GEMMs.
 
+Cold cache: the timed steps rotate over 64 packed copies of the step's
+weights (566 MB, over twice the 256 MB Infinity Cache), and right before
+the timed replay a 1 GiB buffer is read, so every weight byte the timed
+steps read comes from HBM whatever the step count.
+
 Steps are launched from HIP graphs (one graph holds the K timed steps), so
 the host does not limit the measured rate.  Weight packing is an offline step
 (packed weights are the deployment format) and is timed separately.
@@ -30,6 +35,8 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, GB/s
 INT8_PEAK_TOPS = 5000.0         # MI355X dense int8 MFMA, TOPS
 MALL_BYTES = 256 * 1024 * 1024  # Infinity Cache
+FLUSH_BYTES = 1 << 30           # read between the warm-up and a timed replay
+ROOFLINE_COPIES = 128           # up-matrix copies the roofline loop rotates (566 MB)
 H, F = 2560, 6912
 PACKED_BYTES_MATRIX = H * F // 4              # 4,423,680
 PACKED_BYTES_STEP = 2 * PACKED_BYTES_MATRIX  # 8,847,360
@@ -46,6 +53,68 @@ def src_hash(*names):
         with open(os.path.join(ROOT, "bit_gemm_absmax_amd", "csrc", n), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
+
+
+# Kernels whose rocprofv3 kernel-trace durations bench.py reports beside its
+# own event timings: key -> (kernel name prefix, workgroups, sources)
+DURATION_KERNELS = {
+    "decode_up_m1": ("k_decode<4, 4, false, 3>", 432, ("gemv.hip", "bl_device.h")),
+    "decode_down_m1": ("k_decode<8, 4, false, 4>", 160, ("gemv.hip", "bl_device.h")),
+    "gemm_up_m4096": ("k_gemm_pipe<256, 256, 2, 4, 4, 1>", 432, ("gemm.hip", "bl_device.h")),
+    "gemm_down_m4096": ("k_gemm_pipe<256, 160, 4, 2, 4, 1>", 256, ("gemm.hip", "bl_device.h")),
+}
+
+
+def durations_from(trace_dir):
+    """profiles/kernel_durations.json and a markdown table from a rocprofv3
+    --kernel-trace run of bench.py: per kernel of DURATION_KERNELS, the
+    average and median of its dispatch durations (GPU timestamps)."""
+    import csv
+    import glob
+    import statistics
+    f = glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True)
+    if not f:
+        raise SystemExit(f"no kernel_trace.csv under {trace_dir}")
+    table = {}
+    for r in csv.DictReader(open(f[0])):
+        name = r["Kernel_Name"].replace("bl::(anonymous namespace)::", "")
+        if name.startswith("void "):
+            name = name[5:]
+        wgs = int(r["Grid_Size_X"] if "Grid_Size_X" in r else r["Grid_Size"]) // \
+            int(r["Workgroup_Size_X"] if "Workgroup_Size_X" in r else r["Workgroup_Size"])
+        dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        table.setdefault((name, wgs), []).append(dur)
+    rec = {"command": f"rocprofv3 --kernel-trace --stats -d {trace_dir} -o bench -- python3 bench.py"}
+    rows = []
+    for key, (prefix, wgs, srcs) in DURATION_KERNELS.items():
+        vals = [x for (n, w), v in table.items() if n.startswith(prefix) and w == wgs for x in v]
+        if not vals:
+            raise SystemExit(f"kernel {prefix} ({wgs} WGs) not in the trace")
+        rec[key] = {"kernel": prefix, "workgroups": wgs, "calls": len(vals),
+                    "avg_us": round(statistics.mean(vals), 3), "median_us": round(statistics.median(vals), 3),
+                    "min_us": round(min(vals), 3), "source_hash": src_hash(*srcs)}
+        rows.append(f"| {key} | `{prefix}` | {wgs} | {len(vals)} | {statistics.mean(vals):.3f} | "
+                    f"{statistics.median(vals):.3f} | {min(vals):.3f} |")
+    with open(os.path.join(ROOT, "profiles", "kernel_durations.json"), "w") as fo:
+        json.dump(rec, fo, indent=1)
+    print("| key | kernel | WGs | calls | avg us | median us | min us |")
+    print("|---|---|---|---|---|---|---|")
+    print("\n".join(rows))
+
+
+def rocprof_figures(key, units_per_launch, peak):
+    """The dominant kernel's rate from the committed rocprofv3 trace
+    (profiles/kernel_durations.json), while its sources are unchanged."""
+    try:
+        with open(os.path.join(ROOT, "profiles", "kernel_durations.json")) as f:
+            rec = json.load(f).get(key)
+    except (OSError, ValueError):
+        rec = None
+    if not rec or rec.get("source_hash") != src_hash(*DURATION_KERNELS[key][2]):
+        return {"rocprof_us_per_launch": None, "frac_rocprof": None}
+    rate = units_per_launch / (rec["avg_us"] * 1e-6)
+    return {"rocprof_us_per_launch": rec["avg_us"], "rocprof_median_us": rec["median_us"],
+            "frac_rocprof": round(rate / peak, 4)}
 
 
 def traffic_from_profile(kernel_key, sources):
@@ -65,7 +134,7 @@ def traffic_from_profile(kernel_key, sources):
 # Kernels whose HBM traffic is taken from rocprofv3 counters: key -> (kernel
 # name prefix in the trace, workgroups, sources whose hash the figures belong to)
 TRAFFIC_KERNELS = {
-    "decode_up_m1": ("k_decode<4, 4, false, 3, 1>", 432, ("gemv.hip", "bl_device.h")),
+    "decode_up_m1": ("k_decode<4, 4, false, 3>", 432, ("gemv.hip", "bl_device.h")),
     "gemm_up_m4096": ("k_gemm_pipe<256, 256, 2, 4, 4, 1>", 432, ("gemm.hip", "bl_device.h")),
     "gemm_down_m4096": ("k_gemm_pipe<256, 160, 4, 2, 4, 1>", 256, ("gemm.hip", "bl_device.h")),
     "batch_gate_m64": ("k_batch<4, 2, 2, 3, false>", 216, ("gemv.hip", "bl_device.h")),
@@ -84,7 +153,8 @@ PMC_CMDS = [
 
 def pmc_drive():
     """The launches the traffic counters are read from: the decode up kernel
-    over 16 weight copies (more than the per-XCD L2 holds), a plain
+    over 128 weight copies (566 MB, over twice the Infinity Cache, so its
+    weight bytes come from HBM), a plain
     elementwise pass over 256 MiB (x -> -x: reads and writes 256 MiB, the
     counters' calibration), the two prefill GEMMs, and the batched decode
     gate and down BitLinears at M=64 over 8 weight copies each."""
@@ -97,7 +167,7 @@ def pmc_drive():
     dev = torch.device("cuda:0")
     d = synth.decode_gemv()
     pu, su = bl.pack_weights(torch.from_numpy(d["W_up"]).to(dev))
-    ups = [bl.QuantForward(pu.clone(), su, 1, relu2=True) for _ in range(16)]
+    ups = [bl.QuantForward(pu.clone(), su, 1, relu2=True) for _ in range(ROOFLINE_COPIES)]
     x = torch.from_numpy(d["X_up"]).to(dev)
     y = torch.empty((1, F), dtype=torch.float32, device=dev)
     for _ in range(3):
@@ -213,6 +283,16 @@ def traffic_from(fetch_dir, write_dir):
           "(torch.neg over 256 MiB fp32 reads and writes 268,435,456 B).")
 
 
+def flush_reader(torch, dev):
+    """A callable that reads FLUSH_BYTES (torch's sum: plain loads, which
+    allocate in the Infinity Cache) so that no weight copy stays there."""
+    buf = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+
+    def flush():
+        buf.sum()
+    return flush
+
+
 def time_graph(torch, fn, reps=1):
     """Capture fn() into a HIP graph, replay once to warm, then time `reps`
     replays with events on the launch stream.  Returns seconds per replay."""
@@ -238,9 +318,23 @@ def time_graph(torch, fn, reps=1):
     return e0.elapsed_time(e1) / 1e3 / reps, g
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(budget_s=10.0):
-    """The scalar oracle on this host's cores: the same decode step, repeated
-    until `budget_s` seconds of CPU work have run."""
+    """The scalar oracle on this host: the decode step (M=1, seed 1) repeated
+    for about budget_s seconds on one core (liboracle.so) and then on every
+    core this process may use (liboracle_mt.so, the same per-element code with
+    the outer loops split over threads, identical results); and a bounded
+    sample of the prefill chain (64 of the 4096 rows, seed 3) on every core."""
     import numpy as np
 
     import oracle
@@ -249,19 +343,42 @@ def cpu_baseline(budget_s=10.0):
     qu, gu = oracle.quantize_weights(d["W_up"])
     qd, gd = oracle.quantize_weights(d["W_down"])
     x = d["X_up"]
-    n = 0
-    t0 = time.perf_counter()
-    while True:
-        oracle.ffn_layer(x, qu, gu, qd, gd, pre_gain=None, residual=False)
-        n += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s:
-            break
-    per = el / n
-    return {"value": round(PACKED_BYTES_STEP / per / 1e9, 4), "unit": "GB/s", "cores": 1,
-            "kind": "oracle", "ms_per_step": round(per * 1e3, 3),
-            "sample": f"{n} decode steps (M=1, up 2560->6912 + ReLU^2 + subln requant + down "
-                      f"6912->2560, seed 1) by the single-threaded scalar C oracle, {el:.1f} s"}
+
+    def steps(budget):
+        n = 0
+        t0 = time.perf_counter()
+        while True:
+            oracle.ffn_layer(x, qu, gu, qd, gd, pre_gain=None, residual=False)
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= budget:
+                return n, el
+
+    with oracle.parallel(1):
+        n1, el1 = steps(budget_s * 0.6)
+    nthreads = oracle.default_threads()
+    with oracle.parallel(nthreads) as used:
+        nm, elm = steps(budget_s * 0.4)
+        p = synth.prefill()
+        qpu, gpu_ = oracle.quantize_weights(p["W_up"])
+        qpd, gpd = oracle.quantize_weights(p["W_down"])
+        rows = p["X"][:64]
+        t0 = time.perf_counter()
+        oracle.ffn_layer(rows, qpu, gpu_, qpd, gpd, pre_gain=None, residual=False)
+        elp = time.perf_counter() - t0
+    per1, perm = el1 / n1, elm / nm
+    ops_p = 2.0 * 2 * 64 * H * F
+    return {"value": round(PACKED_BYTES_STEP / perm / 1e9, 4), "unit": "GB/s", "cores": used,
+            "kind": "oracle", "cpu_model": cpu_model(), "ms_per_step": round(perm * 1e3, 3),
+            "sample": f"{nm} decode steps (M=1, up 2560->6912 + ReLU^2 + subln requant + down 6912->2560, "
+                      f"seed 1) by the scalar C oracle's OpenMP build on {used} threads, {elm:.1f} s",
+            "one_core": {"value": round(PACKED_BYTES_STEP / per1 / 1e9, 4), "unit": "GB/s", "cores": 1,
+                         "ms_per_step": round(per1 * 1e3, 3),
+                         "sample": f"{n1} decode steps by the one-core build, {el1:.1f} s"},
+            "prefill_rows": {"value": round(ops_p / elp / 1e12, 5), "unit": "TOPS", "cores": used,
+                             "s": round(elp, 3),
+                             "sample": "64 of the 4096 prefill rows (seed 3) through quant, up + ReLU^2, subln "
+                                       "requant, down, on the OpenMP build"}}
 
 
 def bench_batched(torch, bl, synth, dev, log):
@@ -531,9 +648,14 @@ def main():
                     help="only run the launches the HBM traffic counters are read from")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/traffic.json from two rocprofv3 --pmc runs of --pmc-drive")
+    ap.add_argument("--durations-from", metavar="TRACE_DIR",
+                    help="write profiles/kernel_durations.json from a rocprofv3 --kernel-trace run of bench.py")
     args = ap.parse_args()
     if args.traffic_from:
         traffic_from(*args.traffic_from)
+        return
+    if args.durations_from:
+        durations_from(args.durations_from)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the BitLinear path here has no multi-GPU "
@@ -566,7 +688,8 @@ def main():
     del Wu, Wd
 
     R = max(1, args.copies)
-    if R * PACKED_BYTES_STEP < 2 * MALL_BYTES:
+    cold = R * PACKED_BYTES_STEP >= 2 * MALL_BYTES
+    if not cold:
         log(f"warning: {R} copies ({R * PACKED_BYTES_STEP / 1e6:.0f} MB) fit the Infinity Cache; numbers are warm")
     layers = [{"up": pu.clone(), "up_scale": su, "down": pd.clone(), "down_scale": sd} for _ in range(R)]
     stacks = [bl.FFNStack([L], H, F, 1, dev, pre_norm=False, residual=False) for L in layers]
@@ -585,6 +708,10 @@ def main():
         steps(args.steps)
     g.replay()  # graph warm-up replay
     torch.cuda.synchronize()
+    # the warm-up replay just read the copies the timed replay reads: read
+    # 1 GiB of other data so that none of them is left in the Infinity Cache
+    flush = flush_reader(torch, dev)
+    flush()
     stream = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -593,6 +720,7 @@ def main():
     e1.record(stream)
     torch.cuda.synchronize()
     step_s = e0.elapsed_time(e1) / 1e3 / args.steps
+    del flush
     value = PACKED_BYTES_STEP / step_s / 1e9
     log(f"decode step (graph): {step_s * 1e6:.2f} us -> {value:.1f} GB/s")
 
@@ -624,21 +752,29 @@ def main():
     log(f"gated decode step (graph): {gated_s * 1e6:.2f} us -> {1.5 * PACKED_BYTES_STEP / gated_s / 1e9:.1f} GB/s")
 
     # dominant kernel: the step's up kernel (fused absmax quant + up BitLinear
-    # + ReLU^2 at M=1), back to back over the weight copies; then the down one
-    L_launch = 4 * R
-    ups = [bl.QuantForward(layers[i]["up"], su, 1, relu2=True) for i in range(R)]
-    dns = [bl.QuantForward(layers[i]["down"], sd, 1, rmsnorm=True) for i in range(R)]
+    # + ReLU^2 at M=1), back to back over ROOFLINE_COPIES weight copies (566 MB,
+    # so each launch reads its weights from HBM); then the down one
+    del layers, stacks, gstacks
+    torch.cuda.empty_cache()
+    RC = ROOFLINE_COPIES
+    L_launch = 2 * RC
+    pool_u = torch.empty((RC, PACKED_BYTES_MATRIX), dtype=torch.uint8, device=dev)
+    pool_u.copy_(pu.reshape(1, -1).expand(RC, -1))
+    pool_d = torch.empty((RC, PACKED_BYTES_MATRIX), dtype=torch.uint8, device=dev)
+    pool_d.copy_(pd.reshape(1, -1).expand(RC, -1))
+    ups = [bl.QuantForward(pool_u[i].view(F, H // 4), su, 1, relu2=True) for i in range(RC)]
+    dns = [bl.QuantForward(pool_d[i].view(H, F // 4), sd, 1, rmsnorm=True) for i in range(RC)]
     y = torch.empty((1, F), dtype=torch.float32, device=dev)
     y2 = torch.empty((1, H), dtype=torch.float32, device=dev)
     xd = torch.from_numpy(d["X_down"]).to(dev)
 
     def up_run():
         for i in range(L_launch):
-            ups[i % R](x0, y_out=y)
+            ups[i % RC](x0, y_out=y)
 
     def dn_run():
         for i in range(L_launch):
-            dns[i % R](xd, y_out=y2)
+            dns[i % RC](xd, y_out=y2)
 
     gemv_s, gg = time_graph(torch, up_run, reps=3)
     gemv_s /= L_launch
@@ -652,10 +788,13 @@ def main():
     traffic = traffic_from_profile("decode_up_m1", ["gemv.hip", "bl_device.h"])
     roofline = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": "k_decode<4,4,false,3,1> (absmax quant + up BitLinear + ReLU^2, M=1, K=2560, N=6912)",
+                "kernel": "k_decode<4,4,false,3> (absmax quant + up BitLinear + ReLU^2, M=1, K=2560, N=6912)",
                 "bytes_per_launch": PACKED_BYTES_MATRIX, "us_per_launch": round(gemv_s * 1e6, 3),
+                "timing": f"HIP events around a graph of {L_launch} back-to-back launches over {RC} weight "
+                          f"copies ({RC * PACKED_BYTES_MATRIX / 1e6:.0f} MB)",
                 "down_us_per_launch": round(gemv_dn_s * 1e6, 3)}
-    del layers, stacks, ups, dns, gstacks
+    roofline.update(rocprof_figures("decode_up_m1", PACKED_BYTES_MATRIX / 1e9, HBM_PEAK_GBS))
+    del ups, dns, pool_u, pool_d
     torch.cuda.empty_cache()
 
     # ---------------------------------------------------------------- decode, M=1, per BitLinear shape
@@ -727,14 +866,17 @@ def main():
         prefill = {"metric": "int8 TOPS of the two FFN GEMMs at M=4096", "value": round(tops, 2),
                    "unit": "TOPS", "ms_per_chain": round(chain_s * 1e3, 4),
                    "config": {"workload": "prefill chain M=4096: quant, up 2560->6912 +ReLU^2, subln "
-                                          "requant, down 6912->2560 (seed 3)"},
+                                          "requant, down 6912->2560 (seed 3)",
+                              "cache": "warm: the replays reuse one copy of each matrix (the GEMMs are bound "
+                                       "by the matrix cores; their operands are re-read from L2 by many tiles)"},
                    "roofline": {"bound": "mfma", "achieved": round(tops_up, 2), "peak": INT8_PEAK_TOPS,
                                 "unit": "TOPS", "frac": round(tops_up / INT8_PEAK_TOPS, 4),
                                 "traffic": traffic_from_profile("gemm_up_m4096", ["gemm.hip", "bl_device.h"]),
                                 "kernel": "k_gemm_pipe<256,256,2,4,4,1> (M=4096, K=2560, N=6912, +ReLU^2)",
                                 "ops_per_launch": int(ops), "us_per_launch": round(up_s * 1e6, 2),
                                 "down_us_per_launch": round(dn_s * 1e6, 2),
-                                "down_tops": round(tops_dn, 2)}}
+                                "down_tops": round(tops_dn, 2),
+                                **rocprof_figures("gemm_up_m4096", ops / 1e12, INT8_PEAK_TOPS)}}
 
     batched = None if args.no_batched else bench_batched(torch, bl, synth, dev, log)
     torch.cuda.empty_cache()
@@ -756,8 +898,13 @@ def main():
            "config": {"workload": "decode FFN chain at model width, M=1: quant, up 2560->6912 +ReLU^2, "
                                   "subln requant, down 6912->2560 (seed 1)",
                       "M": 1, "hidden": H, "ffn": F, "packed_bytes_per_step": PACKED_BYTES_STEP,
-                      "weight_copies": R, "cache": "cold: rotating packed-weight copies exceed 2x the "
-                                                   "256 MB Infinity Cache",
+                      "weight_copies": R,
+                      "cache": ("cold: 1 GiB of other data is read between the warm-up and the timed replay, and "
+                                "a copy is read again only after the other copies (reuse distance above)"
+                                if cold else "warm: the rotated copies fit twice the Infinity Cache"),
+                      "cold_bytes_touched": FLUSH_BYTES,
+                      "timed_weight_bytes_distinct": min(args.steps, R) * PACKED_BYTES_STEP,
+                      "reuse_distance_bytes": R * PACKED_BYTES_STEP,
                       "launch": "HIP graph of the K steps", "eager_us_per_step": round(eager_s * 1e6, 2),
                       "pack_ms_up_plus_down": round(pack_t * 1e3, 4),
                       "gated_step_us": round(gated_s * 1e6, 3),
