@@ -452,9 +452,12 @@ size_t bitnet_ffn_workspace_bytes(int64_t M, int64_t H, int64_t F) {
     return ffn_ws(M, H, F);
 }
 
-int bitnet_ffn_forward(const bitnet_ffn_layer* layers, int32_t n_layers, float* hidden, int64_t M,
-                       int64_t H, int64_t F, uint32_t flags, float norm_eps, void* ws,
-                       size_t ws_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+// Everything bitnet_ffn_forward checks before its workspace.
+int ffn_check(const bitnet_ffn_layer* layers, int32_t n_layers, float* hidden, int64_t M, int64_t H, int64_t F,
+              uint32_t flags) {
     if (!hidden) return fail(BL_ERR_NULL, "ffn: hidden is required");
     if (n_layers < 0) return fail(BL_ERR_SHAPE, "ffn: n_layers = %d must be >= 0", n_layers);
     if (n_layers > 0 && !layers) return fail(BL_ERR_NULL, "ffn: layers is required");
@@ -479,11 +482,12 @@ int bitnet_ffn_forward(const bitnet_ffn_layer* layers, int32_t n_layers, float* 
             !aligned(L.gate, 16) || !aligned(L.gate_scale, 4))
             return fail(BL_ERR_ALIGN, "ffn: layer %d: misaligned pointer", l);
     }
-    if (int r = check_workspace(ws, ws_bytes, M == 0 || n_layers == 0 ? 0 : ffn_ws(M, H, F))) return r;
-    if (M == 0 || n_layers == 0) return ok();
-    if (overlap(hidden, (size_t)(M * H) * 4, ws, ffn_ws(M, H, F)))
-        return fail(BL_ERR_UNSUPPORTED, "ffn: hidden overlaps the workspace");
+    return BL_OK;
+}
 
+// The layer launches, with scratch `ws` of ffn_ws(M, H, F) bytes (M >= 1).
+int ffn_launch(const bitnet_ffn_layer* layers, int32_t n_layers, float* hidden, int64_t M, int64_t H, int64_t F,
+               uint32_t flags, float norm_eps, void* ws, hipStream_t stream) {
     Carver c(ws);
     int8_t* xq1 = c.take<int8_t>((size_t)(M * H));
     float* s1 = c.take<float>((size_t)M);
@@ -540,6 +544,21 @@ int bitnet_ffn_forward(const bitnet_ffn_layer* layers, int32_t n_layers, float* 
         if (e != hipSuccess) return hip_status(e, "ffn: down");
     }
     return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int bitnet_ffn_forward(const bitnet_ffn_layer* layers, int32_t n_layers, float* hidden, int64_t M,
+                       int64_t H, int64_t F, uint32_t flags, float norm_eps, void* ws,
+                       size_t ws_bytes, hipStream_t stream) {
+    if (int r = ffn_check(layers, n_layers, hidden, M, H, F, flags)) return r;
+    if (int r = check_workspace(ws, ws_bytes, M == 0 || n_layers == 0 ? 0 : ffn_ws(M, H, F))) return r;
+    if (M == 0 || n_layers == 0) return ok();
+    if (overlap(hidden, (size_t)(M * H) * 4, ws, ffn_ws(M, H, F)))
+        return fail(BL_ERR_UNSUPPORTED, "ffn: hidden overlaps the workspace");
+    return ffn_launch(layers, n_layers, hidden, M, H, F, flags, norm_eps, ws, stream);
 }
 
 }  // extern "C"
