@@ -11,10 +11,12 @@ rotate over enough packed copies that every step reads them from HBM, not
 from the 256 MB Infinity Cache.  A second figure times the same chain at
 M=4096 (prefill, seed 3) and reports int8 TOPS of the two GEMMs.
 
-Cold cache: the timed steps rotate over 64 packed copies of the step's
-weights (566 MB, over twice the 256 MB Infinity Cache), and right before
-the timed replay a 1 GiB buffer is read, so every weight byte the timed
-steps read comes from HBM whatever the step count.
+Cold cache: the steps rotate over 64 packed copies of the step's weights
+(566 MB), and right before the timed replay one pass over all copies is run
+in the order the replay reads them, so every copy the timed steps read was
+last read 63 copies (557 MB, over twice the 256 MB Infinity Cache) earlier,
+whatever the step count: its weight bytes come from HBM, as in steady-state
+decode where the other layers' weights are read in between.
 
 Steps are launched from HIP graphs (one graph holds the K timed steps), so
 the host does not limit the measured rate.  Weight packing is an offline step
@@ -65,6 +67,10 @@ DURATION_KERNELS = {
 }
 
 
+PROFILE_CMD = ("rocprofv3 --kernel-trace --stats -d {dir} -o bench -- python3 bench.py --steps 300 --warmup 20 "
+               "--no-cpu --no-shapes")
+
+
 def durations_from(trace_dir):
     """profiles/kernel_durations.json and a markdown table from a rocprofv3
     --kernel-trace run of bench.py: per kernel of DURATION_KERNELS, the
@@ -72,19 +78,27 @@ def durations_from(trace_dir):
     import csv
     import glob
     import statistics
-    f = glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True)
-    if not f:
-        raise SystemExit(f"no kernel_trace.csv under {trace_dir}")
+    def clean(name):
+        name = name.replace("bl::(anonymous namespace)::", "")
+        return name[5:] if name.startswith("void ") else name
+
     table = {}
-    for r in csv.DictReader(open(f[0])):
-        name = r["Kernel_Name"].replace("bl::(anonymous namespace)::", "")
-        if name.startswith("void "):
-            name = name[5:]
-        wgs = int(r["Grid_Size_X"] if "Grid_Size_X" in r else r["Grid_Size"]) // \
-            int(r["Workgroup_Size_X"] if "Workgroup_Size_X" in r else r["Workgroup_Size"])
-        dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
-        table.setdefault((name, wgs), []).append(dur)
-    rec = {"command": f"rocprofv3 --kernel-trace --stats -d {trace_dir} -o bench -- python3 bench.py"}
+    f = glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True)
+    db = glob.glob(os.path.join(trace_dir, "**", "*results.db"), recursive=True)
+    if f:
+        for r in csv.DictReader(open(f[0])):
+            wgs = int(r["Grid_Size_X"] if "Grid_Size_X" in r else r["Grid_Size"]) // \
+                int(r["Workgroup_Size_X"] if "Workgroup_Size_X" in r else r["Workgroup_Size"])
+            dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+            table.setdefault((clean(r["Kernel_Name"]), wgs), []).append(dur)
+    elif db:  # rocprofv3's default SQLite (rocpd) output
+        import sqlite3
+        con = sqlite3.connect(db[0])
+        for name, gx, wx, t0, t1 in con.execute("select name, grid_x, workgroup_x, start, end from kernels"):
+            table.setdefault((clean(name), gx // wx), []).append((t1 - t0) / 1e3)
+    else:
+        raise SystemExit(f"no kernel_trace.csv or results.db under {trace_dir}")
+    rec = {"command": PROFILE_CMD.format(dir=trace_dir)}
     rows = []
     for key, (prefix, wgs, srcs) in DURATION_KERNELS.items():
         vals = [x for (n, w), v in table.items() if n.startswith(prefix) and w == wgs for x in v]
@@ -688,7 +702,8 @@ def main():
     del Wu, Wd
 
     R = max(1, args.copies)
-    cold = R * PACKED_BYTES_STEP >= 2 * MALL_BYTES
+    reuse = (R - 1) * PACKED_BYTES_STEP  # other weight bytes read between two reads of one copy
+    cold = reuse >= 2 * MALL_BYTES
     if not cold:
         log(f"warning: {R} copies ({R * PACKED_BYTES_STEP / 1e6:.0f} MB) fit the Infinity Cache; numbers are warm")
     layers = [{"up": pu.clone(), "up_scale": su, "down": pd.clone(), "down_scale": sd} for _ in range(R)]
@@ -708,20 +723,29 @@ def main():
         steps(args.steps)
     g.replay()  # graph warm-up replay
     torch.cuda.synchronize()
-    # the warm-up replay just read the copies the timed replay reads: read
-    # 1 GiB of other data so that none of them is left in the Infinity Cache
-    flush = flush_reader(torch, dev)
-    flush()
     stream = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    g.replay()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    step_s = e0.elapsed_time(e1) / 1e3 / args.steps
-    del flush
+
+    def timed_replay():
+        torch.cuda.synchronize()
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / 1e3 / args.steps
+
+    # the warm-up replay just read the copies the timed replay reads: one pass
+    # over all copies in replay order, so each timed copy was last read R - 1
+    # copies earlier
+    steps(R)
+    step_s = timed_replay()
     value = PACKED_BYTES_STEP / step_s / 1e9
+    # context: the same replay after 1 GiB of unrelated reads (Infinity Cache
+    # and address-translation caches cold)
+    flush = flush_reader(torch, dev)
+    flush()
+    flushed_s = timed_replay()
+    del flush
     log(f"decode step (graph): {step_s * 1e6:.2f} us -> {value:.1f} GB/s")
 
     # eager rate for context
@@ -899,12 +923,12 @@ def main():
                                   "subln requant, down 6912->2560 (seed 1)",
                       "M": 1, "hidden": H, "ffn": F, "packed_bytes_per_step": PACKED_BYTES_STEP,
                       "weight_copies": R,
-                      "cache": ("cold: 1 GiB of other data is read between the warm-up and the timed replay, and "
-                                "a copy is read again only after the other copies (reuse distance above)"
+                      "cache": ("cold: every weight copy a timed step reads was last read cold_bytes_touched "
+                                "bytes of other weight copies earlier (over twice the 256 MB Infinity Cache)"
                                 if cold else "warm: the rotated copies fit twice the Infinity Cache"),
-                      "cold_bytes_touched": FLUSH_BYTES,
+                      "cold_bytes_touched": reuse,
                       "timed_weight_bytes_distinct": min(args.steps, R) * PACKED_BYTES_STEP,
-                      "reuse_distance_bytes": R * PACKED_BYTES_STEP,
+                      "after_1GiB_flush_us_per_step": round(flushed_s * 1e6, 3),
                       "launch": "HIP graph of the K steps", "eager_us_per_step": round(eager_s * 1e6, 2),
                       "pack_ms_up_plus_down": round(pack_t * 1e3, 4),
                       "gated_step_us": round(gated_s * 1e6, 3),

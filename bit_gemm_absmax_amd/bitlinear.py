@@ -14,7 +14,9 @@ from typing import Optional, Sequence
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libbitlinear.so")
+# BITLINEAR_LIB selects another build of the same library (the host-sanitizer
+# build of build.py); the default is the in-tree one.
+LIB_PATH = os.environ.get("BITLINEAR_LIB") or os.path.join(_HERE, "libbitlinear.so")
 
 BL_OK = 0
 BL_ERR_NULL = -1

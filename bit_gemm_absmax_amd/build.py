@@ -3,7 +3,10 @@ libblbench.so, the benchmark's streaming-read reference kernel (csrc/bench;
 measurement support, not part of the BitLinear path).
 
 Usage: ``python -m bit_gemm_absmax_amd.build`` or :func:`build` from Python.
-Every call recompiles all sources.
+Every call recompiles all sources.  ``build_sanitized()`` (``--sanitize``)
+builds a separate copy whose host code carries AddressSanitizer and
+UndefinedBehaviorSanitizer (device code unchanged) under _build/sanitize/,
+for host-side checks on a machine without a GPU.
 """
 from __future__ import annotations
 
@@ -42,9 +45,16 @@ def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.basename(src)[:-4] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
+# Host-only sanitizers: each -fsanitize= applies to the host pass alone.
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-g"]
+SAN_DIR = os.path.join(BUILD_DIR, "sanitize")
+SAN_LIB = os.path.join(SAN_DIR, "libbitlinear.so")
+
+
+def _compile(src: str, extra=(), out_dir: str = BUILD_DIR) -> str:
+    obj = os.path.join(out_dir, os.path.basename(src)[:-4] + ".o")
+    cmd = [HIPCC, *FLAGS, *extra, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
@@ -80,6 +90,27 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+def build_sanitized(verbose: bool = False) -> str:
+    """libbitlinear with host-side ASan + UBSan in _build/sanitize/ (load it
+    with the clang ASan runtime preloaded)."""
+    os.makedirs(SAN_DIR, exist_ok=True)
+    srcs = sources()
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        objs = list(ex.map(lambda f: _compile(f, SAN_FLAGS, SAN_DIR), srcs))
+    tmp = SAN_LIB + ".tmp"
+    r = subprocess.run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stderr}")
+    os.replace(tmp, SAN_LIB)
+    if verbose:
+        print(f"built {SAN_LIB}")
+    return SAN_LIB
+
+
 if __name__ == "__main__":
-    build(verbose=True)
+    if "--sanitize" in sys.argv[1:]:
+        build_sanitized(verbose=True)
+    else:
+        build(verbose=True)
     sys.exit(0)

@@ -34,6 +34,16 @@ CFLAGS = ["-O2", "-fno-tree-vectorize", "-ffp-contract=off", "-fno-fast-math",
           "-std=c11", "-fPIC", "-shared", "-Wall", "-Wextra"]
 # (extra flags, output) of the two builds of oracle.c
 _BUILDS = {"serial": (["-Wno-unknown-pragmas"], _LIB), "mt": (["-fopenmp"], _LIB_MT)}
+_CC = "gcc"
+# ORACLE_SANITIZE=1: both builds with AddressSanitizer and UndefinedBehaviorSanitizer
+# (clang, so one sanitizer runtime serves this and the HIP library's host code),
+# under separate names; the arithmetic flags are the same.
+if os.environ.get("ORACLE_SANITIZE") == "1":
+    _CC = "/opt/rocm/llvm/bin/clang"
+    _SAN = ["-fsanitize=address,undefined", "-fno-omit-frame-pointer", "-g"]
+    _LIB = os.path.join(_HERE, "liboracle_san.so")
+    _LIB_MT = os.path.join(_HERE, "liboracle_mt_san.so")
+    _BUILDS = {"serial": (["-Wno-unknown-pragmas", *_SAN], _LIB), "mt": (["-fopenmp", *_SAN], _LIB_MT)}
 
 _libs = {}
 _threads = 1
@@ -42,7 +52,7 @@ _threads = 1
 def _compile(which: str) -> str:
     extra, out = _BUILDS[which]
     tmp = out + ".tmp"
-    subprocess.run(["gcc", *CFLAGS, *extra, "-o", tmp, _SRC, "-lm"], check=True)
+    subprocess.run([_CC, *CFLAGS, *extra, "-o", tmp, _SRC, "-lm"], check=True)
     os.replace(tmp, out)
     return out
 
