@@ -46,8 +46,9 @@ SYMBOLS = (
     "bitlinear_forward_workspace_bytes", "bitlinear_forward",
     "bitlinear_quant_forward_workspace_bytes", "bitlinear_quant_forward",
     "bitlinear_latent_forward_workspace_bytes", "bitlinear_latent_forward",
-    "bitnet_ffn_workspace_bytes", "bitnet_ffn_forward",
+    "bitnet_ffn_workspace_bytes", "bitnet_ffn_forward", "bitnet_ffn_forward_noalloc",
 )
+NOALLOC_MAX_BYTES = 64 << 20  # BITNET_FFN_NOALLOC_MAX_BYTES
 
 
 class BitLinearError(RuntimeError):
@@ -119,6 +120,9 @@ def load(path: str = LIB_PATH):
     lib.bitnet_ffn_forward.argtypes = [ctypes.POINTER(FFNLayer), ctypes.c_int32, P, I64, I64, I64,
                                        U32, F, P, SZ, P]
     lib.bitnet_ffn_forward.restype = I
+    lib.bitnet_ffn_forward_noalloc.argtypes = [ctypes.POINTER(FFNLayer), ctypes.c_int32, P, I64, I64, I64,
+                                               U32, F, P]
+    lib.bitnet_ffn_forward_noalloc.restype = I
     _lib = lib
     return lib
 
@@ -446,6 +450,23 @@ class FFNStack:
                                            self.eps, _p(self.ws), 0 if self.ws is None else self.ws.numel(),
                                            _stream(hidden.device)))
         return hidden
+
+
+def ffn_forward_noalloc(layers: Sequence[dict], hidden: torch.Tensor, pre_norm: bool = True,
+                        residual: bool = True, eps: float = RMS_EPS) -> torch.Tensor:
+    """The FFN stack in place on hidden [M][H] with the library's fixed
+    scratch (bitnet_ffn_forward_noalloc: no workspace, nothing allocated
+    beyond the layer descriptors' host array)."""
+    lib = load()
+    _need(hidden, torch.float32, 2, "hidden")
+    M, H = hidden.shape
+    F = layers[0]["up"].shape[0] if layers else 64
+    arr = make_layers(layers, H, F)
+    _on_gpu(hidden)
+    flags = (BL_FFN_PRE_NORM if pre_norm else 0) | (BL_FFN_RESIDUAL if residual else 0)
+    _check(lib.bitnet_ffn_forward_noalloc(arr, len(layers), _p(hidden), M, H, F, flags, float(eps),
+                                          _stream(hidden.device)))
+    return hidden
 
 
 def ffn_forward(layers: Sequence[dict], hidden: torch.Tensor, pre_norm: bool = True,

@@ -4,6 +4,8 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
+
 #include "bitlinear.h"
 #include "bl_internal.h"
 
@@ -558,6 +560,59 @@ int bitnet_ffn_forward(const bitnet_ffn_layer* layers, int32_t n_layers, float* 
     if (M == 0 || n_layers == 0) return ok();
     if (overlap(hidden, (size_t)(M * H) * 4, ws, ffn_ws(M, H, F)))
         return fail(BL_ERR_UNSUPPORTED, "ffn: hidden overlaps the workspace");
+    return ffn_launch(layers, n_layers, hidden, M, H, F, flags, norm_eps, ws, stream);
+}
+
+// ---------------------------------------------------------------- FFN stack without allocation
+
+}  // extern "C"
+
+namespace {
+// Scratch of bitnet_ffn_forward_noalloc: a fixed array in device memory, one
+// copy per GPU the library runs on, held until the process ends.  In host
+// code `scratch` names a host-side stand-in, not the device array: its device
+// address comes from hipGetSymbolAddress, once per device (with that device
+// current), and only that address is handed to kernels.
+constexpr size_t kScratchBytes = BITNET_FFN_NOALLOC_MAX_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+int scratch_address(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e, "ffn_noalloc: hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(BL_ERR_UNSUPPORTED, "ffn_noalloc: device %d beyond the %d this build tracks", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_status(e, "ffn_noalloc: hipGetSymbolAddress");
+        if (p == nullptr) return fail(BL_ERR_HIP, "ffn_noalloc: hipGetSymbolAddress returned NULL");
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return BL_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int bitnet_ffn_forward_noalloc(const bitnet_ffn_layer* layers, int32_t n_layers, float* hidden, int64_t M,
+                               int64_t H, int64_t F, uint32_t flags, float norm_eps, hipStream_t stream) {
+    if (int r = ffn_check(layers, n_layers, hidden, M, H, F, flags)) return r;
+    if (M == 0 || n_layers == 0) return ok();
+    const size_t need = ffn_ws(M, H, F);
+    if (need > kScratchBytes)
+        return fail(BL_ERR_WORKSPACE,
+                    "ffn_noalloc: M = %lld, H = %lld, F = %lld need %zu bytes of scratch, above the library's "
+                    "fixed %zu (use bitnet_ffn_forward with a workspace)",
+                    (long long)M, (long long)H, (long long)F, need, kScratchBytes);
+    void* ws = nullptr;
+    if (int r = scratch_address(&ws)) return r;
     return ffn_launch(layers, n_layers, hidden, M, H, F, flags, norm_eps, ws, stream);
 }
 

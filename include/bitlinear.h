@@ -322,6 +322,25 @@ int bitnet_ffn_forward(const bitnet_ffn_layer* layers, int32_t n_layers,
                        uint32_t flags, float norm_eps,
                        void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* ------------------------------------------------------------------------
+ * bitnet_ffn_forward without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Same arguments, results and errors as
+ * bitnet_ffn_forward, but its scratch is a fixed array inside the library,
+ * BITNET_FFN_NOALLOC_MAX_BYTES (64 MiB) on every GPU it runs on (held until
+ * the process ends); calls whose bitnet_ffn_workspace_bytes(M, H, F) exceeds
+ * it return BL_ERR_WORKSPACE (at H = 2560, F = 6912: M up to 1807 tokens).
+ * Allocates nothing: the first call on a device looks the array up
+ * (hipGetSymbolAddress), so make one call on each device before capturing a
+ * graph.  Every call on one GPU shares that GPU's array: calls that overlap
+ * in time on one GPU (other streams, other threads) race and give wrong
+ * results; calls in order on one stream are safe.
+ * ---------------------------------------------------------------------- */
+#define BITNET_FFN_NOALLOC_MAX_BYTES ((size_t)64 << 20)
+int bitnet_ffn_forward_noalloc(const bitnet_ffn_layer* layers, int32_t n_layers,
+                               float* hidden, int64_t M, int64_t H, int64_t F,
+                               uint32_t flags, float norm_eps, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -154,6 +154,25 @@ def test_ffn_validation(lib):
     assert f(L, 1, A, 0, 64, 64, 3, 1e-5, None, 0, None) == bl.BL_OK
 
 
+def test_ffn_noalloc_validation(lib):
+    """The no-allocation FFN entry point checks its arguments as the
+    workspace one does, and refuses shapes whose scratch exceeds its fixed
+    array (64 MiB: 1807 tokens at hidden 2560 / intermediate 6912) before any
+    device call."""
+    f = lib.bitnet_ffn_forward_noalloc
+    L = (bl.FFNLayer * 1)()
+    L[0].up, L[0].up_scale, L[0].down, L[0].down_scale = A.value, B.value, C.value, D.value
+    assert f(L, 1, None, 1, 64, 64, 3, 1e-5, None) == bl.BL_ERR_NULL
+    assert f(L, 1, A, 1, 64, 96, 3, 1e-5, None) == bl.BL_ERR_SHAPE
+    assert f(L, 1, A, 1, 64, 64, 0x10, 1e-5, None) == bl.BL_ERR_UNSUPPORTED
+    assert f(L, 1, MIS, 1, 64, 64, 3, 1e-5, None) == bl.BL_ERR_ALIGN
+    assert f(L, 0, A, 1, 64, 64, 3, 1e-5, None) == bl.BL_OK
+    assert f(L, 1, A, 0, 64, 64, 3, 1e-5, None) == bl.BL_OK
+    assert lib.bitnet_ffn_workspace_bytes(1807, 2560, 6912) <= bl.NOALLOC_MAX_BYTES
+    assert f(L, 1, A, 1808, 2560, 6912, 3, 1e-5, None) == bl.BL_ERR_WORKSPACE
+    assert b"scratch" in lib.bitlinear_last_error()
+
+
 def test_binding_raises_on_bad_tensor():
     import torch
     with pytest.raises((ValueError, TypeError)):
@@ -357,3 +376,6 @@ def test_no_device_gives_hip_status(lib):
     layer = bl.FFNLayer(up=A.value, up_scale=B.value, down=D.value, down_scale=B.value)
     arr = (bl.FFNLayer * 1)(layer)
     assert lib.bitnet_ffn_forward(arr, 1, A, 2, 64, 64, 0, 1e-5, WS, WSN, None) == bl.BL_ERR_HIP
+    # the no-allocation entry: its scratch lookup needs a device
+    assert lib.bitnet_ffn_forward_noalloc(arr, 1, A, 2, 64, 64, 0, 1e-5, None) == bl.BL_ERR_HIP
+    assert lib.bitlinear_last_error()
