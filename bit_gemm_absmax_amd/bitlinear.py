@@ -43,7 +43,7 @@ SYMBOLS = (
     "bitlinear_pack_workspace_bytes", "bitlinear_pack_weights",
     "bitlinear_import_canonical", "bitlinear_export_canonical", "bitlinear_unpack_weights",
     "bitlinear_quant_act",
-    "bitlinear_forward_workspace_bytes", "bitlinear_forward",
+    "bitlinear_forward_workspace_bytes", "bitlinear_forward", "bitlinear_forward_grouped",
     "bitlinear_quant_forward_workspace_bytes", "bitlinear_quant_forward",
     "bitlinear_latent_forward_workspace_bytes", "bitlinear_latent_forward",
     "bitnet_ffn_workspace_bytes", "bitnet_ffn_forward", "bitnet_ffn_forward_noalloc",
@@ -62,6 +62,14 @@ class Epilogue(ctypes.Structure):
                 ("norm_gain", ctypes.c_void_p), ("norm_eps", ctypes.c_float),
                 ("out_q", ctypes.c_void_p), ("out_q_scale", ctypes.c_void_p),
                 ("out_q_rowsum", ctypes.c_void_p), ("mul_by", ctypes.c_void_p)]
+
+
+BL_MAX_GROUPS = 4
+
+
+class Group(ctypes.Structure):
+    _fields_ = [("packed", ctypes.c_void_p), ("w_scale", ctypes.c_void_p), ("N", ctypes.c_int64),
+                ("epi", Epilogue), ("Y", ctypes.c_void_p), ("acc_out", ctypes.c_void_p)]
 
 
 class FFNLayer(ctypes.Structure):
@@ -105,6 +113,8 @@ def load(path: str = LIB_PATH):
     lib.bitlinear_forward.argtypes = [P, P, P, I64, I64, P, P, I64, ctypes.POINTER(Epilogue),
                                       P, P, P, SZ, P]
     lib.bitlinear_forward.restype = I
+    lib.bitlinear_forward_grouped.argtypes = [P, P, P, I64, I64, ctypes.POINTER(Group), ctypes.c_int32, P]
+    lib.bitlinear_forward_grouped.restype = I
     lib.bitlinear_quant_forward_workspace_bytes.argtypes = [I64, I64, I64]
     lib.bitlinear_quant_forward_workspace_bytes.restype = SZ
     lib.bitlinear_quant_forward.argtypes = [P, I64, I64, U32, P, F, P, P, I64, ctypes.POINTER(Epilogue),
@@ -310,6 +320,69 @@ def forward(xq: torch.Tensor, x_scale: torch.Tensor, packed: torch.Tensor, w_sca
                                  N, ctypes.byref(epi), _p(y), _p(acc), _p(ws),
                                  0 if ws is None else ws.numel(), _stream(dev)))
     return res
+
+
+def forward_grouped(xq: torch.Tensor, x_scale: torch.Tensor, x_rowsum: torch.Tensor, mats: Sequence[dict]):
+    """Several BitLinears of the same K on the same int8 rows in one call
+    (bitlinear_forward_grouped).  Each dict of ``mats`` holds ``packed``,
+    ``w_scale`` and optionally ``relu2``, ``residual``, ``mul_by``, ``subln``,
+    ``norm_gain``, ``eps``, ``want_acc``, ``y_out``; returns one result dict
+    per matrix, as :func:`forward` does."""
+    lib = load()
+    _need(xq, torch.int8, 2, "xq")
+    M, K = xq.shape
+    _shape(x_scale, torch.float32, (M,), "x_scale")
+    _shape(x_rowsum, torch.int32, (M,), "x_rowsum")
+    if not 1 <= len(mats) <= BL_MAX_GROUPS:
+        raise ValueError(f"1 to {BL_MAX_GROUPS} matrices per call, got {len(mats)}")
+    for i, d in enumerate(mats):
+        _need(d["packed"], torch.uint8, 2, f"matrix {i} packed")
+        N = d["packed"].shape[0]
+        if d["packed"].shape[1] * 4 != K:
+            raise ValueError(f"matrix {i}: packed has {d['packed'].shape[1]} bytes per row, expected K/4 = {K // 4}")
+        _shape(d["w_scale"], torch.float32, (1,), f"matrix {i} w_scale")
+        for key in ("residual", "mul_by", "y_out"):
+            _shape(d.get(key), torch.float32, (M, N), f"matrix {i} {key}")
+        if d.get("subln"):
+            _shape(d.get("norm_gain"), torch.float32, (N,), f"matrix {i} norm_gain")
+        _on_gpu(d["packed"], d["w_scale"], d.get("residual"), d.get("mul_by"), d.get("y_out"), d.get("norm_gain"))
+    _on_gpu(xq, x_scale, x_rowsum)
+    dev = xq.device
+    arr = (Group * len(mats))()
+    results = []
+    for i, d in enumerate(mats):
+        N = d["packed"].shape[0]
+        res = {}
+        g = arr[i]
+        g.packed, g.w_scale, g.N = d["packed"].data_ptr(), d["w_scale"].data_ptr(), N
+        flags = BL_EPI_RELU2 if d.get("relu2") else 0
+        if d.get("residual") is not None:
+            flags |= BL_EPI_RESIDUAL
+            g.epi.residual = d["residual"].data_ptr()
+        if d.get("mul_by") is not None:
+            flags |= BL_EPI_MUL
+            g.epi.mul_by = d["mul_by"].data_ptr()
+        if d.get("subln"):
+            flags |= BL_EPI_SUBLN_QUANT
+            res["q"] = torch.empty((M, N), dtype=torch.int8, device=dev)
+            res["q_scale"] = torch.empty(M, dtype=torch.float32, device=dev)
+            res["q_rowsum"] = torch.empty(M, dtype=torch.int32, device=dev)
+            g.epi.out_q, g.epi.out_q_scale = res["q"].data_ptr(), res["q_scale"].data_ptr()
+            g.epi.out_q_rowsum = res["q_rowsum"].data_ptr()
+            g.epi.norm_gain = None if d.get("norm_gain") is None else d["norm_gain"].data_ptr()
+            g.epi.norm_eps = float(d.get("eps", RMS_EPS))
+        g.epi.flags = flags
+        y = d.get("y_out")
+        if y is None:
+            y = torch.empty((M, N), dtype=torch.float32, device=dev)
+        res["y"] = y
+        g.Y = y.data_ptr()
+        if d.get("want_acc"):
+            res["acc"] = torch.empty((M, N), dtype=torch.int32, device=dev)
+            g.acc_out = res["acc"].data_ptr()
+        results.append(res)
+    _check(lib.bitlinear_forward_grouped(_p(xq), _p(x_scale), _p(x_rowsum), M, K, arr, len(mats), _stream(dev)))
+    return results
 
 
 class QuantForward:

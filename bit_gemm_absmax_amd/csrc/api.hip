@@ -246,56 +246,78 @@ size_t bitlinear_forward_workspace_bytes(int64_t M, int64_t K, int64_t N, uint32
     return forward_ws(M, N, true, (epi_flags & BL_EPI_SUBLN_QUANT) != 0);
 }
 
-int bitlinear_forward(const int8_t* Xq, const float* x_scale, const int32_t* x_rowsum, int64_t M,
-                      int64_t K, const uint8_t* packed, const float* w_scale, int64_t N,
-                      const bl_epilogue* epi, float* Y, int32_t* acc_out, void* ws, size_t ws_bytes,
-                      hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+// Every check of bitlinear_forward but the workspace: null pointers, flags,
+// shapes, alignment, and no output overlapping an input or another output
+// (Y may equal residual / mul_by).
+int check_forward(const char* who, const int8_t* Xq, const float* x_scale, const int32_t* x_rowsum, int64_t M,
+                  int64_t K, const uint8_t* packed, const float* w_scale, int64_t N, const bl_epilogue* epi,
+                  float* Y, int32_t* acc_out) {
     const uint32_t flags = epi ? epi->flags : 0u;
     const bool subln = (flags & BL_EPI_SUBLN_QUANT) != 0;
     if (!Xq || !x_scale || !packed || !w_scale)
-        return fail(BL_ERR_NULL, "forward: Xq, x_scale, packed and w_scale are required");
+        return fail(BL_ERR_NULL, "%s: Xq, x_scale, packed and w_scale are required", who);
     if (flags & ~(BL_EPI_RELU2 | BL_EPI_RESIDUAL | BL_EPI_SUBLN_QUANT | BL_EPI_MUL))
-        return fail(BL_ERR_UNSUPPORTED, "forward: unknown epilogue flags 0x%x", flags);
-    if (!Y && !subln) return fail(BL_ERR_NULL, "forward: Y is required without BL_EPI_SUBLN_QUANT");
-    if (int r = epi ? check_aux(epi, flags, "forward") : BL_OK) return r;
+        return fail(BL_ERR_UNSUPPORTED, "%s: unknown epilogue flags 0x%x", who, flags);
+    if (!Y && !subln) return fail(BL_ERR_NULL, "%s: Y is required without BL_EPI_SUBLN_QUANT", who);
+    if (int r = epi ? check_aux(epi, flags, who) : BL_OK) return r;
     if (subln && (!epi->out_q || !epi->out_q_scale))
-        return fail(BL_ERR_NULL, "forward: BL_EPI_SUBLN_QUANT needs out_q and out_q_scale");
-    if (M < 0) return fail(BL_ERR_SHAPE, "forward: M = %lld must be >= 0", (long long)M);
-    if (N < 1) return fail(BL_ERR_SHAPE, "forward: N = %lld must be >= 1", (long long)N);
-    if (int r = check_k(K, "forward: K")) return r;
+        return fail(BL_ERR_NULL, "%s: BL_EPI_SUBLN_QUANT needs out_q and out_q_scale", who);
+    if (M < 0) return fail(BL_ERR_SHAPE, "%s: M = %lld must be >= 0", who, (long long)M);
+    if (N < 1) return fail(BL_ERR_SHAPE, "%s: N = %lld must be >= 1", who, (long long)N);
+    if (K < 64 || K % 64 != 0)
+        return fail(BL_ERR_SHAPE, "%s: K = %lld must be a positive multiple of 64", who, (long long)K);
     if (subln) {
-        if (int r = check_k(N, "forward: N (BL_EPI_SUBLN_QUANT)")) return r;
+        if (N < 64 || N % 64 != 0)
+            return fail(BL_ERR_SHAPE, "%s: N = %lld must be a positive multiple of 64 with subln", who,
+                        (long long)N);
         if (!bl::quant_supported(N))
-            return fail(BL_ERR_UNSUPPORTED, "forward: N = %lld above 32768 with subln", (long long)N);
+            return fail(BL_ERR_UNSUPPORTED, "%s: N = %lld above 32768 with subln", who, (long long)N);
     }
     if (M * K >= kLimit || M * N >= kLimit || N * K >= kLimit * 4)
-        return fail(BL_ERR_SHAPE, "forward: sizes exceed 2^31 elements");
+        return fail(BL_ERR_SHAPE, "%s: sizes exceed 2^31 elements", who);
     if (!aligned(Xq, 16) || !aligned(packed, 16) || !aligned(Y, 16) || !aligned(acc_out, 16) ||
         !aligned(x_scale, 4) || !aligned(x_rowsum, 4) || !aligned(w_scale, 4))
-        return fail(BL_ERR_ALIGN, "forward: Xq, packed, Y, acc_out need 16-byte alignment, scales 4-byte");
+        return fail(BL_ERR_ALIGN, "%s: Xq, packed, Y, acc_out need 16-byte alignment, scales 4-byte", who);
     if (subln && (!aligned(epi->out_q, 16) || !aligned(epi->out_q_scale, 4) ||
                   !aligned(epi->out_q_rowsum, 4) || !aligned(epi->norm_gain, 16)))
-        return fail(BL_ERR_ALIGN, "forward: subln outputs/gain misaligned");
+        return fail(BL_ERR_ALIGN, "%s: subln outputs/gain misaligned", who);
     {
-        // outputs must not overlap the inputs, except Y == residual / mul_by
         const size_t xb = (size_t)(M * K), yb = (size_t)(M * N) * 4, wb = (size_t)(N * K / 4);
         const void* outs[5] = {Y, acc_out, subln ? epi->out_q : nullptr, subln ? epi->out_q_scale : nullptr,
                                subln ? epi->out_q_rowsum : nullptr};
         const size_t ob[5] = {yb, yb, (size_t)(M * N), (size_t)M * 4, (size_t)M * 4};
         const void* ins[5] = {Xq, x_scale, x_rowsum, packed, w_scale};
         const size_t ib[5] = {xb, (size_t)M * 4, (size_t)M * 4, wb, 4};
+        const float* aux = (flags & BL_EPI_RESIDUAL) ? epi->residual : (flags & BL_EPI_MUL) ? epi->mul_by : nullptr;
         for (int o = 0; o < 5; ++o) {
             for (int i = 0; i < 5; ++i)
                 if (overlap(outs[o], ob[o], ins[i], ib[i]))
-                    return fail(BL_ERR_UNSUPPORTED, "forward: an output overlaps an input");
+                    return fail(BL_ERR_UNSUPPORTED, "%s: an output overlaps an input", who);
             for (int o2 = o + 1; o2 < 5; ++o2)
                 if (overlap(outs[o], ob[o], outs[o2], ob[o2]))
-                    return fail(BL_ERR_UNSUPPORTED, "forward: two outputs overlap");
-            const float* aux = (flags & BL_EPI_RESIDUAL) ? epi->residual : (flags & BL_EPI_MUL) ? epi->mul_by : nullptr;
+                    return fail(BL_ERR_UNSUPPORTED, "%s: two outputs overlap", who);
             if (aux && !(o == 0 && outs[o] == aux) && overlap(outs[o], ob[o], aux, yb))
-                return fail(BL_ERR_UNSUPPORTED, "forward: an output overlaps residual / mul_by (only Y == it is allowed)");
+                return fail(BL_ERR_UNSUPPORTED, "%s: an output overlaps residual / mul_by (only Y == it is allowed)",
+                            who);
         }
     }
+    return BL_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int bitlinear_forward(const int8_t* Xq, const float* x_scale, const int32_t* x_rowsum, int64_t M,
+                      int64_t K, const uint8_t* packed, const float* w_scale, int64_t N,
+                      const bl_epilogue* epi, float* Y, int32_t* acc_out, void* ws, size_t ws_bytes,
+                      hipStream_t stream) {
+    if (int r = check_forward("forward", Xq, x_scale, x_rowsum, M, K, packed, w_scale, N, epi, Y, acc_out))
+        return r;
+    const uint32_t flags = epi ? epi->flags : 0u;
+    const bool subln = (flags & BL_EPI_SUBLN_QUANT) != 0;
     const bool need_rowsum = (x_rowsum == nullptr);
     const bool need_y = subln && (Y == nullptr);
     if (int r = check_workspace(ws, ws_bytes, M == 0 ? 0 : forward_ws(M, N, need_rowsum, need_y)))
@@ -316,6 +338,78 @@ int bitlinear_forward(const int8_t* Xq, const float* x_scale, const int32_t* x_r
         e = bl::launch_quant(y, M, N, true, epi->norm_gain, epi->norm_eps, epi->out_q,
                              epi->out_q_scale, epi->out_q_rowsum, stream);
         if (e != hipSuccess) return hip_status(e, "forward: subln requant");
+    }
+    return ok();
+}
+
+// ---------------------------------------------------------------- grouped forward
+
+int bitlinear_forward_grouped(const int8_t* Xq, const float* x_scale, const int32_t* x_rowsum, int64_t M,
+                              int64_t K, const bl_group* groups, int32_t n_groups, hipStream_t stream) {
+    const char* who = "forward_grouped";
+    if (n_groups < 1 || n_groups > BL_MAX_GROUPS)
+        return fail(BL_ERR_UNSUPPORTED, "%s: n_groups = %d outside 1..%d", who, n_groups, BL_MAX_GROUPS);
+    if (!groups) return fail(BL_ERR_NULL, "%s: groups is required", who);
+    if (!x_rowsum) return fail(BL_ERR_NULL, "%s: x_rowsum is required", who);
+    char what[64];
+    for (int32_t g = 0; g < n_groups; ++g) {
+        const bl_group& G = groups[g];
+        snprintf(what, sizeof(what), "%s: matrix %d", who, g);
+        if (!G.Y) return fail(BL_ERR_NULL, "%s: Y is required", what);
+        if (int r = check_forward(what, Xq, x_scale, x_rowsum, M, K, G.packed, G.w_scale, G.N, &G.epi, G.Y,
+                                  G.acc_out))
+            return r;
+    }
+    // across matrices: no output of one may overlap another's inputs or outputs
+    for (int32_t a = 0; a < n_groups; ++a)
+        for (int32_t b = 0; b < n_groups; ++b) {
+            if (a == b) continue;
+            const bl_group& A = groups[a];
+            const bl_group& B = groups[b];
+            const bool sa = (A.epi.flags & BL_EPI_SUBLN_QUANT) != 0;
+            const size_t ya = (size_t)(M * A.N) * 4, yb = (size_t)(M * B.N) * 4;
+            const void* outs[5] = {A.Y, A.acc_out, sa ? A.epi.out_q : nullptr, sa ? A.epi.out_q_scale : nullptr,
+                                   sa ? A.epi.out_q_rowsum : nullptr};
+            const size_t ob[5] = {ya, ya, (size_t)(M * A.N), (size_t)M * 4, (size_t)M * 4};
+            const bool sb = (B.epi.flags & BL_EPI_SUBLN_QUANT) != 0;
+            const float* bx = (B.epi.flags & BL_EPI_RESIDUAL) ? B.epi.residual
+                              : (B.epi.flags & BL_EPI_MUL) ? B.epi.mul_by : nullptr;
+            const void* other[8] = {B.packed, B.w_scale, bx, B.Y, B.acc_out, sb ? B.epi.out_q : nullptr,
+                                    sb ? B.epi.out_q_scale : nullptr, sb ? B.epi.out_q_rowsum : nullptr};
+            const size_t otb[8] = {(size_t)(B.N * K / 4), 4, yb, yb, yb, (size_t)(M * B.N), (size_t)M * 4,
+                                   (size_t)M * 4};
+            for (int o = 0; o < 5; ++o)
+                for (int i = 0; i < 8; ++i)
+                    if (overlap(outs[o], ob[o], other[i], otb[i]))
+                        return fail(BL_ERR_UNSUPPORTED, "%s: an output of matrix %d overlaps matrix %d's data", who,
+                                    a, b);
+        }
+    if (M == 0) return ok();
+
+    bl::GroupMat mats[BL_MAX_GROUPS];
+    bool one_launch = n_groups <= bl::gemv_max_groups();
+    for (int32_t g = 0; g < n_groups; ++g) {
+        const bl_group& G = groups[g];
+        mats[g] = bl::GroupMat{G.packed, G.w_scale, G.N, kernel_epi(&G.epi), G.Y, G.acc_out};
+        one_launch = one_launch && bl::gemv_supported(M, K, G.N);
+    }
+    hipError_t e = hipSuccess;
+    if (one_launch) {
+        e = bl::launch_gemv_grouped(Xq, x_scale, x_rowsum, M, K, mats, n_groups, stream);
+        if (e != hipSuccess) return hip_status(e, "forward_grouped: contraction");
+    } else {
+        for (int32_t g = 0; g < n_groups; ++g) {
+            e = bl::launch_contract(Xq, x_scale, x_rowsum, M, K, mats[g].packed, mats[g].w_scale, mats[g].N,
+                                    mats[g].epi, mats[g].Y, mats[g].acc_out, stream);
+            if (e != hipSuccess) return hip_status(e, "forward_grouped: contraction");
+        }
+    }
+    for (int32_t g = 0; g < n_groups; ++g) {
+        const bl_group& G = groups[g];
+        if (!(G.epi.flags & BL_EPI_SUBLN_QUANT)) continue;
+        e = bl::launch_quant(G.Y, M, G.N, true, G.epi.norm_gain, G.epi.norm_eps, G.epi.out_q, G.epi.out_q_scale,
+                             G.epi.out_q_rowsum, stream);
+        if (e != hipSuccess) return hip_status(e, "forward_grouped: subln requant");
     }
     return ok();
 }

@@ -56,6 +56,20 @@ hipError_t launch_gemv(const int8_t* Xq, const float* xs, const int32_t* rs, int
                        int64_t K, const uint8_t* packed, const float* ws, int64_t N, Epi epi,
                        float* Y, int32_t* acc_out, hipStream_t s);
 
+// Several matrices of the same K on the same int8 rows in one skinny launch
+// (at most gemv_max_groups()), each with its own scale, epilogue and outputs.
+struct GroupMat {
+    const uint8_t* packed;
+    const float* w_scale;
+    int64_t N;
+    Epi epi;
+    float* Y;
+    int32_t* acc_out;
+};
+int gemv_max_groups();
+hipError_t launch_gemv_grouped(const int8_t* Xq, const float* xs, const int32_t* rs, int64_t M, int64_t K,
+                               const GroupMat* groups, int count, hipStream_t s);
+
 // The gated pair ReLU^2(BitLinear(x; gate)) * BitLinear(x; up) in one
 // skinny launch (same shapes as launch_gemv).
 hipError_t launch_gemv_gated(const int8_t* Xq, const float* xs, const int32_t* rs, int64_t M, int64_t K,

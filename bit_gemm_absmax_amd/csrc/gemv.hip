@@ -391,6 +391,7 @@ __global__ __launch_bounds__(NWV* kWave) void k_decode_stream(const float* __res
 // outputs are dropped, or its weights are zero.
 constexpr int kBatchWaves = 4;
 constexpr int kTileBytes = 16 * 256;  // one token tile x one chunk quad
+constexpr int kMaxGroups = 4;         // matrices per grouped launch
 
 // s_waitcnt vmcnt(n) for a count that is a constant once the caller's loop
 // is unrolled (the chain of ifs folds to one instruction); n <= 63.
@@ -494,17 +495,33 @@ __device__ __forceinline__ void batch_body(Rsrc ra, const uint32_t (&voff)[MT][2
 #undef BL_WT
 }
 
-// GATED (CT = 2): the two column tiles are the same 16 output rows of the up
-// matrix Wp (tile 0) and of the gate matrix Wg (tile 1), sharing every
-// activation fragment, and the output is ReLU^2(gate) * up.
+// A launch may stream several weight matrices of the same K against the
+// same int8 rows (a grouped launch: e.g. q, k and v, each with its own
+// per-tensor scale): matrix i takes the workgroups from wg0 on, each with its
+// own scale, output, epilogue and accumulator output.
+struct BatchMat {
+    const uint8_t* W;
+    const float* w_scale;
+    const float* aux;
+    float* Y;
+    int32_t* acc_out;
+    int N;
+    uint32_t epi_flags;
+    int wg0;
+};
+struct BatchMats {
+    BatchMat m[kMaxGroups];
+    int count;
+};
+
+// GATED (CT = 2, one matrix): the two column tiles are the same 16 output
+// rows of the up matrix (tile 0) and of the gate matrix Wg (tile 1), sharing
+// every activation fragment, and the output is ReLU^2(gate) * up.
 template <int MT, int CT, int NS, int QMAX, bool GATED = false>
 __global__ __launch_bounds__(kBatchWaves* kWave) void k_batch(const int8_t* __restrict__ Xq,
                                                                const float* __restrict__ x_scale,
                                                                const int32_t* __restrict__ x_rowsum, int M, int K,
-                                                               const uint8_t* __restrict__ Wp,
-                                                               const float* __restrict__ w_scale, int N,
-                                                               uint32_t epi_flags, const float* aux, float* Y,
-                                                               int32_t* __restrict__ acc_out,
+                                                               const BatchMats mats,
                                                                const uint8_t* __restrict__ Wg,
                                                                const float* __restrict__ g_scale) {
     static_assert(!GATED || CT == 2, "a gated tile pairs one up and one gate tile");
@@ -521,11 +538,38 @@ __global__ __launch_bounds__(kBatchWaves* kWave) void k_batch(const int8_t* __re
     __shared__ float sdqg[GATED ? 16 * MT : 1];  // the same with the gate's scale
     __shared__ int srs[16 * MT];
 
+    // this workgroup's matrix: the last whose first workgroup is at or before
+    // it (uniform: every field is picked by a scalar select, no indexing)
+    int gi = 0;
+#pragma unroll
+    for (int i = 1; i < kMaxGroups; ++i)
+        if (i < mats.count && (int)blockIdx.x >= mats.m[i].wg0) gi = i;
+    const uint8_t* Wp = mats.m[0].W;
+    const float* w_scale = mats.m[0].w_scale;
+    const float* aux = mats.m[0].aux;
+    float* Y = mats.m[0].Y;
+    int32_t* acc_out = mats.m[0].acc_out;
+    int N = mats.m[0].N;
+    uint32_t epi_flags = mats.m[0].epi_flags;
+    int wg0 = mats.m[0].wg0;
+#pragma unroll
+    for (int i = 1; i < kMaxGroups; ++i)
+        if (gi == i) {
+            Wp = mats.m[i].W;
+            w_scale = mats.m[i].w_scale;
+            aux = mats.m[i].aux;
+            Y = mats.m[i].Y;
+            acc_out = mats.m[i].acc_out;
+            N = mats.m[i].N;
+            epi_flags = mats.m[i].epi_flags;
+            wg0 = mats.m[i].wg0;
+        }
+
     const int lane = threadIdx.x % kWave;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int fr = lane & 15;  // activation row of the A operand / output column of the tile
     const int fg = lane >> 4;  // k group
-    const int n0 = blockIdx.x * OCOLS;
+    const int n0 = ((int)blockIdx.x - wg0) * OCOLS;
     const int C = K / 64;
     const int nq = (C + 3) / 4;
     const float ws = *w_scale;
@@ -691,6 +735,236 @@ __global__ __launch_bounds__(kBatchWaves* kWave) void k_batch(const int8_t* __re
     }
 }
 
+// Activation-stationary batched BitLinear (M <= 32 tokens, K <= 2560): every
+// workgroup copies all M rows of int8 activations into LDS once (MT * 16 * K
+// bytes, at most the whole 160 KB), then each wave contracts whole 16-row
+// weight tiles over the full K by itself, one tile after another, with no
+// cross-wave reduction and no barrier after the copy.  For launches of many
+// tiles (a grouped launch of several matrices: q, k and v, or o, gate and
+// up) this replaces the per-workgroup activation stream of k_batch, whose
+// cost is M * K bytes through the CU for every 16 or 32 output rows, by one
+// copy per CU.
+//   LDS layout: row r of the activations at r * K, its 16-byte chunk j at
+//   slot j ^ (r % 16) inside each whole group of 16 chunks (j ^ (r % 8) in a
+//   last group of 8), so the 16 rows an operand read takes at one k fall on
+//   distinct banks.  The copy is direct
+//   buffer->LDS: instruction i fills LDS bytes [1024 i, 1024 i + 1024), each
+//   lane fetching the global chunk that its slot holds.
+//   A wave's tile: lane (fr, fg) loads chunk 4s + fg of weight row fr for
+//   every quad s (all loads first); the A operand of MFMA (s, d) for token
+//   tile t is row 16 t + fr, bytes 64 (4 s + fg) + 16 d.
+constexpr int kStatLds = 160 * 1024;
+constexpr int kStatWaves = 4;
+
+// Byte offset of (row r, 16-byte chunk j) of the activation copy in LDS; nch
+// chunks per row (K / 16), swizzled only inside whole groups of 16 (or of 8
+// at the end of a row).  The map is its own inverse: a chunk and its image
+// lie in the same group.
+__device__ __forceinline__ uint32_t stat_slot(uint32_t r, uint32_t j, uint32_t K, uint32_t nch) {
+    const uint32_t sj = ((j | 15u) < nch) ? (j ^ (r & 15u)) : ((j | 7u) < nch) ? (j ^ (r & 7u)) : j;
+    return r * K + 16u * sj;
+}
+
+// One matrix of a grouped launch, as seen by the tile that works on it.
+struct StatTile {
+    const uint8_t* W;
+    const float* w_scale;
+    const float* aux;
+    float* Y;
+    int32_t* acc_out;
+    int N;
+    uint32_t epi_flags;
+    int n0;    // first output row of the tile
+    int rows;  // its rows (16, or fewer in a matrix's last tile)
+};
+
+// The matrix tile `tile` (counted over all matrices) belongs to: the last
+// whose first tile (wg0) is at or before it; every field picked by a scalar
+// select (the tile index is uniform), no indexing into the argument block.
+__device__ __forceinline__ StatTile stat_tile(const BatchMats mats, int tile) {
+    int gi = 0;
+#pragma unroll
+    for (int i = 1; i < kMaxGroups; ++i)
+        if (i < mats.count && tile >= mats.m[i].wg0) gi = i;
+    StatTile t{mats.m[0].W, mats.m[0].w_scale, mats.m[0].aux, mats.m[0].Y, mats.m[0].acc_out,
+               mats.m[0].N, mats.m[0].epi_flags, mats.m[0].wg0, 0};
+#pragma unroll
+    for (int i = 1; i < kMaxGroups; ++i)
+        if (gi == i)
+            t = StatTile{mats.m[i].W, mats.m[i].w_scale, mats.m[i].aux, mats.m[i].Y, mats.m[i].acc_out,
+                         mats.m[i].N, mats.m[i].epi_flags, mats.m[i].wg0, 0};
+    t.n0 = (tile - t.n0) * 16;
+    t.rows = __builtin_amdgcn_readfirstlane(t.N - t.n0 < 16 ? t.N - t.n0 : 16);
+    return t;
+}
+
+template <int QMAX>
+__device__ __forceinline__ void stat_load_weights(const uint8_t* W, int n0, int rows, int K, int C, int nq, int fr,
+                                                  int fg, uint4 (&w)[QMAX]) {
+    const Rsrc rw = make_rsrc(W + (int64_t)n0 * (K / 4), (uint32_t)rows * (uint32_t)(K / 4));
+#pragma unroll
+    for (int s = 0; s < QMAX; ++s) {
+        const int c = 4 * s + fg;
+        w[s] = buf_load16_nt(rw, (s < nq && c < C) ? (uint32_t)(c * rows + fr) * 16u : kOob);
+    }
+}
+
+template <int MT, int QMAX>
+__global__ __launch_bounds__(kStatWaves* kWave) void k_stat(const int8_t* __restrict__ Xq,
+                                                             const float* __restrict__ x_scale,
+                                                             const int32_t* __restrict__ x_rowsum, int M, int K,
+                                                             const BatchMats mats, int tiles, uint32_t kdiv) {
+    __shared__ __align__(1024) int8_t act[kStatLds];
+    const int lane = threadIdx.x % kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int fr = lane & 15;
+    const int fg = lane >> 4;
+    const int C = K / 64;
+    const int nq = (C + 3) / 4;
+    const uint32_t nch = (uint32_t)K / 16u;
+    const int stride = (int)gridDim.x * kStatWaves;
+    int tile = (int)blockIdx.x * kStatWaves + wave;
+
+    // ---- the first tile's weights go out first, so their latency overlaps
+    // the activation copy
+    uint4 w[QMAX];
+    StatTile T = stat_tile(mats, tile < tiles ? tile : 0);
+    stat_load_weights<QMAX>(T.W, T.n0, T.rows, K, C, nq, fr, fg, w);
+
+    // ---- the activation copy: MT * 16 rows (rows past M read zeros)
+    {
+        const Rsrc rx = make_rsrc(Xq, (uint32_t)M * (uint32_t)K);
+        const int ninst = MT * 16 * K / 1024;
+        for (int i = wave; i < ninst; i += kStatWaves) {
+            const uint32_t o = 1024u * (uint32_t)i + 16u * (uint32_t)lane;
+            // r = o / K by a multiply-high with ceil(2^32 / K), then one correction
+            uint32_t r = __umulhi(o, kdiv);
+            if (r * (uint32_t)K > o) --r;
+            if ((r + 1u) * (uint32_t)K <= o) ++r;
+            const uint32_t j = (o - r * (uint32_t)K) / 16u;
+            // the global chunk held by this LDS slot: the swizzle is its own inverse
+            dma16(rx, (lds_ptr)(act + 1024 * i), stat_slot(r, j, (uint32_t)K, nch), 0u);
+        }
+    }
+
+    // ---- the rows' scales and sums for this lane's outputs: acc[t][q] is
+    // token 16 t + 4 fg + q, output column fr of the tile
+    float xs[MT][4];
+    int rsum[MT][4];
+    {
+        const Rsrc rs = make_rsrc(x_scale, (uint32_t)M * 4u);
+        const Rsrc rr = make_rsrc(x_rowsum, (uint32_t)M * 4u);
+#pragma unroll
+        for (int t = 0; t < MT; ++t)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint32_t m = (uint32_t)(16 * t + 4 * fg + q);
+                xs[t][q] = buf_load4f(rs, m * 4u);
+                rsum[t][q] = buf_load4i(rr, m * 4u);
+            }
+    }
+    // operand addresses: row 16 t + fr, chunk 16 s + 4 fg + d of a whole group
+    // of 16 sits at slot 16 s + ((4 fg + d) ^ fr), i.e. at ap[t][d] + 256 s
+    const int8_t* ap[MT][4];
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int d = 0; d < 4; ++d) ap[t][d] = act + (16 * t + fr) * K + 16 * ((4 * fg + d) ^ fr);
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's copy (and first weights) have landed
+    __syncthreads();                // and every other wave's copy
+
+    for (bool first = true; tile < tiles; tile += stride, first = false) {
+        if (!first) {
+            T = stat_tile(mats, tile);
+            stat_load_weights<QMAX>(T.W, T.n0, T.rows, K, C, nq, fr, fg, w);
+        }
+        const float ws = *T.w_scale;
+        const int n = T.n0 + fr;
+        const int N = T.N;
+        float e_aux[MT][4];
+        {
+            const Rsrc ra =
+                make_rsrc(T.aux, (T.epi_flags & (kEpiResidual | kEpiMul)) ? 0x7FFFFFFFu : 0u);
+#pragma unroll
+            for (int t = 0; t < MT; ++t)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int m = 16 * t + 4 * fg + q;
+                    e_aux[t][q] = buf_load4f(ra, (m < M && n < N) ? (uint32_t)((int64_t)m * N + n) * 4u : kOob);
+                }
+        }
+
+        v4i acc[MT];
+#pragma unroll
+        for (int t = 0; t < MT; ++t) acc[t] = v4i{0, 0, 0, 0};
+        // QMAX is the row's quad count (the launcher picks it so), and only the
+        // last quad can be partial: earlier quads are whole groups of 16
+        // chunks, read at the precomputed offsets plus 256 s; the last one
+        // goes through the general map (a chunk past the row end has zero
+        // weights, so its operand offset is clamped to chunk 0).  The operand
+        // fragments of quad s + 1 are read from LDS while quad s's MFMAs run
+        // (two register sets, pinned by scheduling barriers).
+        auto read_quad = [&](int s, v4i (&a)[4][MT]) {
+            const int c = 4 * s + fg;
+            const uint32_t j0 = (uint32_t)(c < C ? 4 * c : 0);
+#pragma unroll
+            for (int d = 0; d < 4; ++d)
+#pragma unroll
+                for (int t = 0; t < MT; ++t) {
+                    const int8_t* p = s + 1 < QMAX
+                                          ? ap[t][d] + 256 * s
+                                          : act + stat_slot((uint32_t)(16 * t + fr), j0 + d, (uint32_t)K, nch);
+                    a[d][t] = *reinterpret_cast<const v4i*>(p);
+                }
+        };
+        auto mma_quad = [&](int s, const v4i (&a)[4][MT]) {
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                const uint32_t wd = d == 0 ? w[s].x : d == 1 ? w[s].y : d == 2 ? w[s].z : w[s].w;
+                const v4i b = v4i{codes4(wd, 0), codes4(wd, 1), codes4(wd, 2), codes4(wd, 3)};
+#pragma unroll
+                for (int t = 0; t < MT; ++t) acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[d][t], b, acc[t], 0, 0, 0);
+            }
+        };
+        v4i a0[4][MT], a1[4][MT];
+        read_quad(0, a0);
+#pragma unroll
+        for (int s = 0; s < QMAX; ++s) {
+            if (s + 1 < QMAX) {
+                if (s % 2 == 0) read_quad(s + 1, a1);
+                else read_quad(s + 1, a0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            if (s % 2 == 0) mma_quad(s, a0);
+            else mma_quad(s, a1);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+
+        // ---- epilogue straight from the accumulators
+        if (n < N) {
+#pragma unroll
+            for (int t = 0; t < MT; ++t)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int m = 16 * t + 4 * fg + q;
+                    if (m < M) {
+                        const int a = acc[t][q] - rsum[t][q];
+                        float y = (float)a * ((xs[t][q] * ws) / 127.0f);
+                        if (T.epi_flags & kEpiRelu2) {
+                            const float tt = y > 0.0f ? y : 0.0f;
+                            y = tt * tt;
+                        }
+                        if (T.epi_flags & kEpiMul) y = y * e_aux[t][q];
+                        else if (T.epi_flags & kEpiResidual) y = y + e_aux[t][q];
+                        const int64_t o = (int64_t)m * N + n;
+                        if (T.Y != nullptr) T.Y[o] = y;
+                        if (T.acc_out != nullptr) T.acc_out[o] = a;
+                    }
+                }
+        }
+    }
+}
+
 struct Plan {
     int nw, qmax;
 };
@@ -805,27 +1079,102 @@ bool gemv_supported(int64_t M, int64_t K, int64_t N) {
     return M * N < (1LL << 29) && batch_shape(M, K, N, q, mt, ct);
 }
 
+// mats.m[i].wg0 is filled in here from each matrix's N and the launch's
+// column tiles per workgroup.
 template <int MT, int CT, int Q, bool G = false>
 static hipError_t go_batch(const int8_t* Xq, const float* xs, const int32_t* rs, int64_t M, int64_t K,
-                           const uint8_t* packed, const float* ws, int64_t N, Epi epi, float* Y, int32_t* acc_out,
-                           hipStream_t s, const uint8_t* gate = nullptr, const float* gate_scale = nullptr) {
+                           BatchMats mats, hipStream_t s, const uint8_t* gate = nullptr,
+                           const float* gate_scale = nullptr) {
     constexpr int NS = MT == 1 ? 4 : MT == 2 ? 3 : 2;
     const int64_t cols = G ? 16 : 16 * CT;
-    const unsigned blocks = (unsigned)((N + cols - 1) / cols);
-    hipLaunchKernelGGL((k_batch<MT, CT, NS, Q, G>), dim3(blocks), dim3(kBatchWaves * kWave), 0, s, Xq, xs, rs, (int)M,
-                       (int)K, packed, ws, (int)N, epi.flags, epi.aux, Y, acc_out, gate, gate_scale);
+    int64_t blocks = 0;
+    for (int i = 0; i < mats.count; ++i) {
+        mats.m[i].wg0 = (int)blocks;
+        blocks += (mats.m[i].N + cols - 1) / cols;
+    }
+    hipLaunchKernelGGL((k_batch<MT, CT, NS, Q, G>), dim3((unsigned)blocks), dim3(kBatchWaves * kWave), 0, s, Xq, xs,
+                       rs, (int)M, (int)K, mats, gate, gate_scale);
     return hipGetLastError();
 }
 
 template <int MT, int CT, bool G = false>
 static hipError_t go_batch_q(int q, const int8_t* Xq, const float* xs, const int32_t* rs, int64_t M, int64_t K,
-                             const uint8_t* packed, const float* ws, int64_t N, Epi epi, float* Y, int32_t* acc_out,
-                             hipStream_t s, const uint8_t* gate = nullptr, const float* gate_scale = nullptr) {
+                             const BatchMats& mats, hipStream_t s, const uint8_t* gate = nullptr,
+                             const float* gate_scale = nullptr) {
     switch (q) {
 #define BL_BQ(Q) \
-    case Q: return go_batch<MT, CT, Q, G>(Xq, xs, rs, M, K, packed, ws, N, epi, Y, acc_out, s, gate, gate_scale);
+    case Q: return go_batch<MT, CT, Q, G>(Xq, xs, rs, M, K, mats, s, gate, gate_scale);
         BL_BQ(1) BL_BQ(2) BL_BQ(3) BL_BQ(4) BL_BQ(5) BL_BQ(6) BL_BQ(7) BL_BQ(8)
 #undef BL_BQ
+        default: return hipErrorInvalidValue;
+    }
+}
+
+static BatchMat batch_mat(const uint8_t* packed, const float* ws, int64_t N, Epi epi, float* Y, int32_t* acc_out) {
+    return BatchMat{packed, ws, epi.aux, Y, acc_out, (int)N, epi.flags, 0};
+}
+
+// The activation-stationary launch: up to 32 tokens, K <= 2560 (at most 10
+// weight chunk quads per lane), and enough 16-row tiles for every CU (a
+// launch of fewer tiles keeps k_batch, whose workgroups split K four ways).
+// Measured on the grouped o + gate + up launch (1024 tiles, K = 2560): at
+// 8 / 32 tokens 9.1 / 11.3 us against 10.3 / 12.6 us with k_batch, but at 64
+// tokens 17.0 against 15.7 us (each wave then reads 160 KB of operands from
+// LDS per tile, one wave per SIMD), so 33..64 tokens keep k_batch.
+constexpr int64_t kStatMinTiles = 512;
+constexpr int64_t kStatMaxM = 32;
+
+static int stat_mt(int64_t M) { return M <= 16 ? 1 : 2; }
+
+static bool stat_shape(int64_t M, int64_t K, int64_t tiles) {
+    return M >= 1 && M <= kStatMaxM && K >= 64 && K <= 2560 && (int64_t)stat_mt(M) * 16 * K <= kStatLds &&
+           tiles >= kStatMinTiles;
+}
+
+template <int MT, int Q>
+static hipError_t go_stat(const int8_t* Xq, const float* xs, const int32_t* rs, int64_t M, int64_t K, BatchMats mats,
+                          hipStream_t s) {
+    int64_t tiles = 0;
+    for (int i = 0; i < mats.count; ++i) {
+        mats.m[i].wg0 = (int)tiles;
+        tiles += (mats.m[i].N + 15) / 16;
+    }
+    const int64_t want = (tiles + kStatWaves - 1) / kStatWaves;
+    const int64_t cus = cu_count();
+    const unsigned blocks = (unsigned)(want < cus ? want : cus);
+    const uint32_t kdiv = (uint32_t)((((uint64_t)1 << 32) + (uint64_t)K - 1) / (uint64_t)K);
+    hipLaunchKernelGGL((k_stat<MT, Q>), dim3(blocks), dim3(kStatWaves * kWave), 0, s, Xq, xs, rs, (int)M, (int)K,
+                       mats, (int)tiles, kdiv);
+    return hipGetLastError();
+}
+
+static hipError_t go_stat_mt(const int8_t* Xq, const float* xs, const int32_t* rs, int64_t M, int64_t K,
+                             const BatchMats& mats, hipStream_t s) {
+    const int q = (int)((K / 64 + 3) / 4);
+#define BL_SQ(MT, Q) \
+    if (stat_mt(M) == MT && q == Q) return go_stat<MT, Q>(Xq, xs, rs, M, K, mats, s);
+#define BL_SQ_MT(MT) BL_SQ(MT, 1) BL_SQ(MT, 2) BL_SQ(MT, 3) BL_SQ(MT, 4) BL_SQ(MT, 5) \
+    BL_SQ(MT, 6) BL_SQ(MT, 7) BL_SQ(MT, 8) BL_SQ(MT, 9) BL_SQ(MT, 10)
+    BL_SQ_MT(1) BL_SQ_MT(2)
+#undef BL_SQ_MT
+#undef BL_SQ
+    return hipErrorInvalidValue;
+}
+
+// Column tiles per workgroup for a launch covering `rows` output rows in all.
+static hipError_t go_batch_mats(const int8_t* Xq, const float* xs, const int32_t* rs, int64_t M, int64_t K,
+                                int64_t rows, const BatchMats& mats, hipStream_t s) {
+    int64_t tiles = 0;
+    for (int i = 0; i < mats.count; ++i) tiles += (mats.m[i].N + 15) / 16;
+    if (stat_shape(M, K, tiles)) return go_stat_mt(Xq, xs, rs, M, K, mats, s);
+    int q, mt, ct;
+    if (!batch_shape(M, K, rows, q, mt, ct)) return hipErrorInvalidValue;
+    switch (mt * 2 + ct - 1) {
+        case 2: return go_batch_q<1, 1>(q, Xq, xs, rs, M, K, mats, s);
+        case 4: return go_batch_q<2, 1>(q, Xq, xs, rs, M, K, mats, s);
+        case 5: return go_batch_q<2, 2>(q, Xq, xs, rs, M, K, mats, s);
+        case 8: return go_batch_q<4, 1>(q, Xq, xs, rs, M, K, mats, s);
+        case 9: return go_batch_q<4, 2>(q, Xq, xs, rs, M, K, mats, s);
         default: return hipErrorInvalidValue;
     }
 }
@@ -833,16 +1182,25 @@ static hipError_t go_batch_q(int q, const int8_t* Xq, const float* xs, const int
 hipError_t launch_gemv(const int8_t* Xq, const float* xs, const int32_t* rs, int64_t M, int64_t K,
                        const uint8_t* packed, const float* ws, int64_t N, Epi epi, float* Y, int32_t* acc_out,
                        hipStream_t s) {
-    int q, mt, ct;
-    if (!batch_shape(M, K, N, q, mt, ct)) return hipErrorInvalidValue;
-    switch (mt * 2 + ct - 1) {
-        case 2: return go_batch_q<1, 1>(q, Xq, xs, rs, M, K, packed, ws, N, epi, Y, acc_out, s);
-        case 4: return go_batch_q<2, 1>(q, Xq, xs, rs, M, K, packed, ws, N, epi, Y, acc_out, s);
-        case 5: return go_batch_q<2, 2>(q, Xq, xs, rs, M, K, packed, ws, N, epi, Y, acc_out, s);
-        case 8: return go_batch_q<4, 1>(q, Xq, xs, rs, M, K, packed, ws, N, epi, Y, acc_out, s);
-        case 9: return go_batch_q<4, 2>(q, Xq, xs, rs, M, K, packed, ws, N, epi, Y, acc_out, s);
-        default: return hipErrorInvalidValue;
+    BatchMats mats{};
+    mats.m[0] = batch_mat(packed, ws, N, epi, Y, acc_out);
+    mats.count = 1;
+    return go_batch_mats(Xq, xs, rs, M, K, N, mats, s);
+}
+
+int gemv_max_groups() { return kMaxGroups; }
+
+hipError_t launch_gemv_grouped(const int8_t* Xq, const float* xs, const int32_t* rs, int64_t M, int64_t K,
+                               const GroupMat* g, int count, hipStream_t s) {
+    if (count < 1 || count > kMaxGroups) return hipErrorInvalidValue;
+    BatchMats mats{};
+    int64_t rows = 0;
+    for (int i = 0; i < count; ++i) {
+        mats.m[i] = batch_mat(g[i].packed, g[i].w_scale, g[i].N, g[i].epi, g[i].Y, g[i].acc_out);
+        rows += g[i].N;
     }
+    mats.count = count;
+    return go_batch_mats(Xq, xs, rs, M, K, rows, mats, s);
 }
 
 // The gated pair in one launch: one workgroup per 16 output rows, streaming
@@ -852,11 +1210,13 @@ hipError_t launch_gemv_gated(const int8_t* Xq, const float* xs, const int32_t* r
                              int64_t N, float* Y, hipStream_t s) {
     int q, mt, ct;
     if (!batch_shape(M, K, N, q, mt, ct)) return hipErrorInvalidValue;
-    const Epi none{0u, nullptr};
+    BatchMats mats{};
+    mats.m[0] = batch_mat(up, up_scale, N, Epi{0u, nullptr}, Y, nullptr);
+    mats.count = 1;
     switch (mt) {
-        case 1: return go_batch_q<1, 2, true>(q, Xq, xs, rs, M, K, up, up_scale, N, none, Y, nullptr, s, gate, gate_scale);
-        case 2: return go_batch_q<2, 2, true>(q, Xq, xs, rs, M, K, up, up_scale, N, none, Y, nullptr, s, gate, gate_scale);
-        case 4: return go_batch_q<4, 2, true>(q, Xq, xs, rs, M, K, up, up_scale, N, none, Y, nullptr, s, gate, gate_scale);
+        case 1: return go_batch_q<1, 2, true>(q, Xq, xs, rs, M, K, mats, s, gate, gate_scale);
+        case 2: return go_batch_q<2, 2, true>(q, Xq, xs, rs, M, K, mats, s, gate, gate_scale);
+        case 4: return go_batch_q<4, 2, true>(q, Xq, xs, rs, M, K, mats, s, gate, gate_scale);
         default: return hipErrorInvalidValue;
     }
 }

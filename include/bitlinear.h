@@ -219,6 +219,43 @@ int bitlinear_forward(const int8_t* Xq, const float* x_scale,
                       void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * Grouped BitLinear: up to BL_MAX_GROUPS weight matrices of the same K on the
+ * same quantised rows, each with its own weight scale, epilogue and outputs
+ * ("Model details" / Architecture: the BitLinear layers of a block that read
+ * one input, e.g. the attention block's q, k and v projections, whose
+ * absmean scales are per tensor; "BitNetConfig": 20 heads, 5 key/value
+ * heads).  Results are identical to one bitlinear_forward per matrix; for
+ * M <= 64 and K <= 8192 the contractions of all matrices stream in one launch.
+ *
+ * Xq, x_scale, M, K   as in bitlinear_forward
+ * x_rowsum   in  int32 [M], required here
+ * groups     in  host array of n_groups (1..BL_MAX_GROUPS) bl_group:
+ *   packed, w_scale, N   one matrix, as in bitlinear_forward
+ *   epi                  its epilogue, as bitlinear_forward's (with
+ *                        BL_EPI_SUBLN_QUANT the requantisation of its Y runs
+ *                        after the contraction)
+ *   Y                    out fp32 [M][N], required
+ *   acc_out              out int32 [M][N] or NULL
+ * Overlap rules of bitlinear_forward for each matrix, and no output of one
+ * matrix may overlap another matrix's inputs or outputs.  No workspace.
+ * ---------------------------------------------------------------------- */
+#define BL_MAX_GROUPS 4
+
+typedef struct bl_group {
+    const uint8_t* packed;   /* [N][K/4] */
+    const float* w_scale;    /* [1] */
+    int64_t N;
+    bl_epilogue epi;         /* flags 0 for plain dequantisation */
+    float* Y;                /* [M][N] */
+    int32_t* acc_out;        /* [M][N] or NULL */
+} bl_group;
+
+int bitlinear_forward_grouped(const int8_t* Xq, const float* x_scale,
+                              const int32_t* x_rowsum, int64_t M, int64_t K,
+                              const bl_group* groups, int32_t n_groups,
+                              hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * Fused quantise + BitLinear: bitlinear_quant_act followed by
  * bitlinear_forward, from fp32 activation rows, with the same results as the
  * two calls.  For a few tokens (M <= 4) it is one launch in which every

@@ -367,6 +367,8 @@ def test_no_device_gives_hip_status(lib):
         "import": lambda: lib.bitlinear_import_canonical(A, 4, 64, B, None),
         "export": lambda: lib.bitlinear_export_canonical(A, 4, 64, B, None),
         "unpack": lambda: lib.bitlinear_unpack_weights(A, 4, 64, B, None),
+        "grouped": lambda: lib.bitlinear_forward_grouped(A, B, D, 2, 64, (bl.Group * 1)(bl.Group(
+            packed=C.value, w_scale=B.value, N=8, Y=Y.value)), 1, None),
         "latent_forward": lambda: lib.bitlinear_latent_forward(A, 2, 64, 0, None, 1e-5, B, bl.BL_DTYPE_F32, 8, nul,
                                                                D, None, WS, WSN, None),
     }
@@ -379,3 +381,35 @@ def test_no_device_gives_hip_status(lib):
     # the no-allocation entry: its scratch lookup needs a device
     assert lib.bitnet_ffn_forward_noalloc(arr, 1, A, 2, 64, 64, 0, 1e-5, None) == bl.BL_ERR_HIP
     assert lib.bitlinear_last_error()
+
+
+def test_forward_grouped_validation(lib):
+    """The grouped forward: group count, required row sums and outputs, each
+    matrix's own checks, and no output of one matrix over another's data;
+    all before any launch."""
+    f = lib.bitlinear_forward_grouped
+    G = (bl.Group * 5)()
+    for i in range(5):
+        G[i].packed, G[i].w_scale, G[i].N = C.value + i * 4096, D.value + 16 * i, 16
+        G[i].Y = Y.value + i * 4096
+    assert f(A, B, D, 2, 64, G, 0, None) == bl.BL_ERR_UNSUPPORTED
+    assert f(A, B, D, 2, 64, G, 5, None) == bl.BL_ERR_UNSUPPORTED
+    assert f(A, B, D, 2, 64, None, 2, None) == bl.BL_ERR_NULL
+    assert f(A, B, None, 2, 64, G, 2, None) == bl.BL_ERR_NULL            # row sums required
+    H = (bl.Group * 2)()
+    ctypes.memmove(H, G, ctypes.sizeof(H))
+    H[1].Y = None
+    assert f(A, B, D, 2, 64, H, 2, None) == bl.BL_ERR_NULL               # Y required
+    assert b"matrix 1" in lib.bitlinear_last_error()
+    H[1].Y, H[1].N = Y.value + 4096, 0
+    assert f(A, B, D, 2, 64, H, 2, None) == bl.BL_ERR_SHAPE
+    H[1].N = 16
+    H[1].Y = Y.value + 64                                                 # over matrix 0's Y
+    assert f(A, B, D, 2, 64, H, 2, None) == bl.BL_ERR_UNSUPPORTED
+    H[1].Y = C.value                                                      # over matrix 0's weights
+    assert f(A, B, D, 2, 64, H, 2, None) == bl.BL_ERR_UNSUPPORTED
+    H[1].Y = Y.value + 4096
+    H[0].epi.flags, H[0].epi.residual = bl.BL_EPI_RESIDUAL, H[1].Y          # residual = matrix 1's output
+    assert f(A, B, D, 2, 64, H, 2, None) == bl.BL_ERR_UNSUPPORTED
+    H[0].epi.residual = H[0].Y                                            # its own Y: in place, allowed
+    assert f(A, B, D, 0, 64, H, 2, None) == bl.BL_OK

@@ -337,6 +337,109 @@ def test_quant_forward(M, K, N, rms, gain, relu2, res):
         assert_exact(host(h), host(y), "quant_forward in place")
 
 
+@pytest.mark.parametrize("M", [1, 4, 8, 17, 33, 64, 80])
+def test_forward_grouped(M):
+    """Grouped BitLinears on one set of int8 rows: q, k, v shapes (2560 ->
+    2560, 640, 640, each with its own absmean scale) plus a ragged matrix,
+    with ReLU^2, residual, gating product and subln requantisation spread over
+    the matrices: every output bit-identical to one bitlinear_forward per
+    matrix (one launch for M <= 64, one per matrix beyond), and against the
+    oracle."""
+    log(f"[grouped] M={M}")
+    rng = np.random.default_rng(3300 + M)
+    K = 2560
+    X = synth.activations(rng, M, K, outliers=True)
+    shapes = [(2560, {"relu2": True, "subln": True}), (640, {"residual": True}), (640, {"mul": True}),
+              (200, {})]
+    packs, mats, refs = [], [], []
+    xq, xs, rs = bl.quant_act(dev(X))
+    rq = oracle.quant_act(X)
+    assert_exact(host(xq), rq[0], "xq")
+    for i, (N, kw) in enumerate(shapes):
+        W = synth.weights(rng, N, K)
+        p, s, q, g = check_pack(W, f"grouped {i}")
+        A = synth.activations(rng, M, N)
+        d = {"packed": p, "w_scale": s, "want_acc": True, "relu2": kw.get("relu2", False),
+             "subln": kw.get("subln", False)}
+        if kw.get("residual"):
+            d["residual"] = dev(A)
+        if kw.get("mul"):
+            d["mul_by"] = dev(A)
+        mats.append(d)
+        packs.append((p, s, q, g, A, kw))
+    out = bl.forward_grouped(xq, xs, rs, mats)
+    for i, (p, s, q, g, A, kw) in enumerate(packs):
+        one = bl.forward(xq, xs, p, s, x_rowsum=rs, relu2=kw.get("relu2", False), subln=kw.get("subln", False),
+                         residual=dev(A) if kw.get("residual") else None,
+                         mul_by=dev(A) if kw.get("mul") else None, want_acc=True)
+        for key in one:
+            assert_exact(host(out[i][key]), host(one[key]), f"matrix {i} {key}: grouped vs single")
+        acc = oracle.int_matmul(rq[0], q)
+        assert_exact(host(out[i]["acc"]), acc, f"matrix {i} acc")
+        want = oracle.dequant(acc, rq[1], g)
+        if kw.get("relu2"):
+            want = oracle.relu2(want)
+        if kw.get("residual"):
+            want = oracle.add(A, want)
+        if kw.get("mul"):
+            want = oracle.mul(want, A)
+        assert_y_close(host(out[i]["y"]), want, f"matrix {i} y")
+        if kw.get("subln"):
+            check_requant(oracle.rmsnorm(host(out[i]["y"])), host(out[i]["q"]), host(out[i]["q_scale"]),
+                          host(out[i]["q_rowsum"]), f"matrix {i} subln")
+
+
+def _stationary_cases():
+    # (M, K, row counts of the matrices): at least 512 tiles of 16 rows, so the
+    # launch copies all activations into LDS once per workgroup; ragged N, K
+    # with a partial last chunk quad and K % 128 == 64 (unswizzled tail)
+    # (up to 32 tokens); beyond 32 tokens the same calls run k_batch
+    return [(1, 2560, (2560, 6912, 6912)), (5, 576, (3000, 3001, 2999)), (16, 64, (8200,)),
+            (17, 1088, (4100, 4099)), (31, 1344, (600, 7700, 5)), (32, 2560, (2560, 6912, 6912)),
+            (33, 2560, (2560, 6912, 6912)), (48, 192, (9000,)), (64, 2560, (2560, 6912, 6912))]
+
+
+@pytest.mark.parametrize("M,K,Ns", _stationary_cases())
+def test_forward_stationary(M, K, Ns):
+    """The activation-stationary launch (many 16-row tiles, K <= 2560): int32
+    accumulators bit-exact and outputs within 1e-5 of the oracle for every
+    matrix, with ReLU^2, residual and gating product epilogues; the same
+    values as the matrices run one by one through the grouped call's
+    per-matrix path is implied by the oracle match."""
+    log(f"[stationary] M={M} K={K} N={Ns}")
+    rng = np.random.default_rng(3400 + M + K)
+    X = synth.activations(rng, M, K, outliers=True)
+    xq, xs, rs = bl.quant_act(dev(X))
+    rq = oracle.quant_act(X)
+    epis = [{"relu2": True}, {"residual": True}, {"mul": True}, {}]
+    mats, refs = [], []
+    for i, N in enumerate(Ns):
+        W = synth.weights(rng, N, K)
+        p, s, q, g = check_pack(W, f"stationary {i}")
+        A = synth.activations(rng, M, N)
+        kw = epis[i % len(epis)]
+        d = {"packed": p, "w_scale": s, "want_acc": True, "relu2": kw.get("relu2", False)}
+        if kw.get("residual"):
+            d["residual"] = dev(A)
+        if kw.get("mul"):
+            d["mul_by"] = dev(A)
+        mats.append(d)
+        refs.append((q, g, A, kw))
+    out = bl.forward_grouped(xq, xs, rs, mats) if len(Ns) > 1 else [bl.forward(
+        xq, xs, mats[0]["packed"], mats[0]["w_scale"], x_rowsum=rs, want_acc=True, relu2=mats[0]["relu2"])]
+    for i, (q, g, A, kw) in enumerate(refs):
+        acc = oracle.int_matmul(rq[0], q)
+        assert_exact(host(out[i]["acc"]), acc, f"matrix {i} acc")
+        want = oracle.dequant(acc, rq[1], g)
+        if kw.get("relu2"):
+            want = oracle.relu2(want)
+        if kw.get("residual"):
+            want = oracle.add(A, want)
+        if kw.get("mul"):
+            want = oracle.mul(want, A)
+        assert_y_close(host(out[i]["y"]), want, f"matrix {i} y")
+
+
 def test_gemv_row_equals_gemm_row():
     """Token independence across kernels: M=1 (batched kernel, one token tile) equals
     row 0 of M=80 (tiled GEMM)."""
