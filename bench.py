@@ -556,6 +556,21 @@ def bench_stack(torch, bl, synth, dev, log, passes=8):
         out.append(rec)
         log(f"stack M={M}: {t * 1e6:.1f} us per 30-layer pass -> {nbytes / t / 1e9:.0f} GB/s")
         del stacks
+        if M == 1:
+            # the same pass as one persistent launch (BL_FFN_PERSISTENT)
+            pst = [bl.FFNStack(ls, H, F, 1, dev, persistent=True) for ls in sets]
+
+            def run_p():
+                for i in range(passes):
+                    pst[i % R](h)
+
+            tp, gg = time_graph(torch, run_p, reps=2)
+            del gg, pst
+            tp /= passes
+            rec["persistent_us_per_pass"] = round(tp * 1e6, 2)
+            rec["persistent_us_per_layer"] = round(tp * 1e6 / len(layers), 3)
+            rec["persistent_GB_per_s"] = round(nbytes / tp / 1e9, 1)
+            log(f"stack M=1 persistent: {tp * 1e6:.1f} us per 30-layer pass -> {nbytes / tp / 1e9:.0f} GB/s")
     return {"workload": "30-layer FFN stack (RMSNorm, quant, up 2560->6912, ReLU^2, subln requant, down "
                         "6912->2560, residual add), seed 4",
             "layers": len(layers), "packed_bytes_per_pass": int(nbytes), "weight_copies": R,

@@ -33,6 +33,7 @@ BL_EPI_SUBLN_QUANT = 0x4
 BL_EPI_MUL = 0x8
 BL_FFN_PRE_NORM = 0x1
 BL_FFN_RESIDUAL = 0x2
+BL_FFN_PERSISTENT = 0x4
 BL_DTYPE_F32 = 0
 BL_DTYPE_BF16 = 1
 
@@ -503,13 +504,14 @@ class FFNStack:
     and a workspace sized for up to ``max_m`` tokens."""
 
     def __init__(self, layers: Sequence[dict], H: int, F: int, max_m: int, device,
-                 pre_norm: bool = True, residual: bool = True, eps: float = RMS_EPS):
+                 pre_norm: bool = True, residual: bool = True, eps: float = RMS_EPS, persistent: bool = False):
         self.lib = load()
         self._keep = list(layers)
         self.arr = make_layers(layers, H, F)
         self.n = len(layers)
         self.H, self.F = H, F
-        self.flags = (BL_FFN_PRE_NORM if pre_norm else 0) | (BL_FFN_RESIDUAL if residual else 0)
+        self.flags = ((BL_FFN_PRE_NORM if pre_norm else 0) | (BL_FFN_RESIDUAL if residual else 0)
+                      | (BL_FFN_PERSISTENT if persistent else 0))
         self.eps = float(eps)
         self.ws = _workspace(self.lib.bitnet_ffn_workspace_bytes(max_m, H, F), device)
 

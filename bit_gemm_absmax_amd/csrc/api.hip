@@ -89,6 +89,7 @@ size_t ffn_ws(int64_t M, int64_t H, int64_t F) {
     c.take<int8_t>((size_t)(M * F));
     c.take<float>((size_t)M);
     c.take<int32_t>((size_t)M);
+    c.take<uint8_t>(bl::stack_ws_bytes());  // the persistent launch's layer descriptors and counter
     return c.off;
 }
 
@@ -557,7 +558,7 @@ int ffn_check(const bitnet_ffn_layer* layers, int32_t n_layers, float* hidden, i
     if (!hidden) return fail(BL_ERR_NULL, "ffn: hidden is required");
     if (n_layers < 0) return fail(BL_ERR_SHAPE, "ffn: n_layers = %d must be >= 0", n_layers);
     if (n_layers > 0 && !layers) return fail(BL_ERR_NULL, "ffn: layers is required");
-    if (flags & ~(BL_FFN_PRE_NORM | BL_FFN_RESIDUAL))
+    if (flags & ~(BL_FFN_PRE_NORM | BL_FFN_RESIDUAL | BL_FFN_PERSISTENT))
         return fail(BL_ERR_UNSUPPORTED, "ffn: unknown flags 0x%x", flags);
     if (M < 0) return fail(BL_ERR_SHAPE, "ffn: M = %lld must be >= 0", (long long)M);
     if (int r = check_k(H, "ffn: H")) return r;
@@ -577,6 +578,14 @@ int ffn_check(const bitnet_ffn_layer* layers, int32_t n_layers, float* hidden, i
             !aligned(L.down_scale, 4) || !aligned(L.pre_norm_gain, 16) || !aligned(L.sub_norm_gain, 16) ||
             !aligned(L.gate, 16) || !aligned(L.gate_scale, 4))
             return fail(BL_ERR_ALIGN, "ffn: layer %d: misaligned pointer", l);
+        if ((flags & BL_FFN_PERSISTENT) && L.gate)
+            return fail(BL_ERR_UNSUPPORTED, "ffn: BL_FFN_PERSISTENT: layer %d is gated", l);
+    }
+    if (flags & BL_FFN_PERSISTENT) {
+        if (M > 1) return fail(BL_ERR_UNSUPPORTED, "ffn: BL_FFN_PERSISTENT runs one token, M = %lld", (long long)M);
+        if (!bl::stack_supported(H, F))
+            return fail(BL_ERR_UNSUPPORTED, "ffn: BL_FFN_PERSISTENT: no persistent launch for H = %lld, F = %lld",
+                        (long long)H, (long long)F);
     }
     return BL_OK;
 }
@@ -594,6 +603,18 @@ int ffn_launch(const bitnet_ffn_layer* layers, int32_t n_layers, float* hidden, 
     int32_t* rs2 = c.take<int32_t>((size_t)M);
     const bool pre = (flags & BL_FFN_PRE_NORM) != 0;
     const bool res = (flags & BL_FFN_RESIDUAL) != 0;
+    void* stack_ws = c.take<uint8_t>(bl::stack_ws_bytes());
+
+    // One token, persistent: every layer in one launch (chunks of
+    // stack_max_layers() layers).
+    if (flags & BL_FFN_PERSISTENT) {
+        for (int32_t l0 = 0; l0 < n_layers; l0 += bl::stack_max_layers()) {
+            const int32_t n = n_layers - l0 < bl::stack_max_layers() ? n_layers - l0 : bl::stack_max_layers();
+            hipError_t e = bl::launch_stack(layers + l0, n, hidden, H, F, pre, res, norm_eps, y1, stack_ws, stream);
+            if (e != hipSuccess) return hip_status(e, "ffn: persistent stack");
+        }
+        return ok();
+    }
 
     // Few tokens: two launches per layer, each quantising its own input rows
     // (a gated layer streams gate and up in the first one).

@@ -207,25 +207,36 @@ __device__ __forceinline__ int signed4(uint32_t w, int j) {
 // quant_row_load issues the row's loads, and the gain's (zeros when there is
 // none), so a caller can put them ahead of other traffic; quant_row_finish
 // does the arithmetic, writes xq (global memory or LDS) and returns gamma to
-// all threads.  With rs_slot, lane 0 of each wave also writes the wave's
+// all threads.
+//
+// VT < NT: a workgroup of NT threads reproduces the VT-thread quantiser
+// exactly: threads t < VT own float4 t + VT*i as a VT-thread workgroup's
+// would, threads from VT on load and store nothing and reduce zeros, and the
+// block reductions then add those waves' +0.0 (or take their max with 0)
+// after the real ones, which changes no bit.  AUX is the load's cache policy
+// (0: default).  With rs_slot, lane 0 of each wave also writes the wave's
 // share of the int8 row sum to rs_slot[wave]: the caller adds the NT/64
 // entries after its next barrier.  Slot arrays follow block_sum's rule.
-template <int NT, int NV>
+template <int NT, int NV, int VT = NT, int AUX = 0>
 __device__ __forceinline__ void quant_row_load_x(const float* x, int K, float4 (&v)[NV]) {
     const Rsrc rx = make_rsrc(x, (uint32_t)K * 4u);
 #pragma unroll
-    for (int i = 0; i < NV; ++i) v[i] = buf_load16f(rx, (uint32_t)(threadIdx.x + i * NT) * 16u);
+    for (int i = 0; i < NV; ++i) {
+        const uint32_t off = (VT == NT || (int)threadIdx.x < VT) ? (uint32_t)(threadIdx.x + i * VT) * 16u : kOob;
+        v[i] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, AUX));
+    }
 }
-template <int NT, int NV>
+template <int NT, int NV, int VT = NT>
 __device__ __forceinline__ void quant_row_load(const float* x, const float* gain, int K, float4 (&v)[NV],
                                                float4 (&gv)[NV]) {
-    quant_row_load_x<NT, NV>(x, K, v);
+    quant_row_load_x<NT, NV, VT>(x, K, v);
     const Rsrc rg = make_rsrc(gain, gain != nullptr ? (uint32_t)K * 4u : 0u);
 #pragma unroll
-    for (int i = 0; i < NV; ++i) gv[i] = buf_load16f(rg, (uint32_t)(threadIdx.x + i * NT) * 16u);
+    for (int i = 0; i < NV; ++i)
+        gv[i] = buf_load16f(rg, (VT == NT || (int)threadIdx.x < VT) ? (uint32_t)(threadIdx.x + i * VT) * 16u : kOob);
 }
 
-template <int NT, int NV>
+template <int NT, int NV, int VT = NT>
 __device__ __forceinline__ float quant_row_finish(float4 (&v)[NV], const float4 (&gv)[NV], int K, bool rmsnorm,
                                                   bool has_gain, float eps, int8_t* xq, double* dslot,
                                                   float* fslot, float* fslot2, int* rs_slot) {
@@ -290,7 +301,7 @@ __device__ __forceinline__ float quant_row_finish(float4 (&v)[NV], const float4 
     int* q4 = reinterpret_cast<int*>(xq);
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-        const int idx = threadIdx.x + i * NT;
+        const int idx = (VT == NT || (int)threadIdx.x < VT) ? threadIdx.x + i * VT : n4;  // n4: stores nothing
         const float e[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
         uint32_t packed = 0;
 #pragma unroll

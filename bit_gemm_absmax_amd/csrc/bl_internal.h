@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "bitlinear.h"
+
 namespace bl {
 
 // Fused epilogue description handed to the contraction kernels by value.
@@ -102,5 +104,15 @@ hipError_t launch_decode_bitlinear(const float* X, int64_t M, int64_t K, bool rm
 hipError_t launch_decode_gated(const float* X, int64_t M, int64_t K, bool rmsnorm, const float* gain, float eps,
                                const uint8_t* up, const float* up_scale, const uint8_t* gate,
                                const float* gate_scale, int64_t N, float* Y, hipStream_t s);
+
+// The FFN stack for one token in one persistent launch (all layers), for
+// hidden H and intermediate F it supports (stack_supported) and up to
+// stack_max_layers() layers per launch; ws: stack_ws_bytes() of scratch (layer
+// descriptors, arrival counter), y1: F floats.  The layers must be ungated.
+bool stack_supported(int64_t H, int64_t F);
+size_t stack_ws_bytes();
+int stack_max_layers();
+hipError_t launch_stack(const bitnet_ffn_layer* layers, int n_layers, float* hidden, int64_t H, int64_t F,
+                        bool pre, bool residual, float eps, float* y1, void* ws, hipStream_t s);
 
 }  // namespace bl

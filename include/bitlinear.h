@@ -341,6 +341,18 @@ int bitlinear_latent_forward(const float* X, int64_t M, int64_t K, uint32_t quan
  * ---------------------------------------------------------------------- */
 #define BL_FFN_PRE_NORM 0x1u
 #define BL_FFN_RESIDUAL 0x2u
+/* BL_FFN_PERSISTENT: one token (M == 1), ungated layers: all layers run in
+ * one persistent launch (one workgroup per CU; the phases of a layer hand
+ * their rows to each other through device memory, each value carrying its
+ * own ready flag, instead of through kernel boundaries, and each phase's
+ * weight loads are issued while the previous row is still in flight).
+ * Results are bit-identical to the call without the flag.
+ * BL_ERR_UNSUPPORTED for M > 1, a gated layer, or a shape without a
+ * persistent plan (hidden 2560 / intermediate 6912 has one).  The launch
+ * needs every one of its workgroups resident at once: do not run it beside
+ * work that holds CUs for as long as it waits (each wait gives up after about
+ * a second; the outputs are then not valid). */
+#define BL_FFN_PERSISTENT 0x4u
 
 typedef struct bitnet_ffn_layer {
     const float* pre_norm_gain;  /* [H] or NULL (ones) */
@@ -366,7 +378,7 @@ int bitnet_ffn_forward(const bitnet_ffn_layer* layers, int32_t n_layers,
  * bitnet_ffn_forward, but its scratch is a fixed array inside the library,
  * BITNET_FFN_NOALLOC_MAX_BYTES (64 MiB) on every GPU it runs on (held until
  * the process ends); calls whose bitnet_ffn_workspace_bytes(M, H, F) exceeds
- * it return BL_ERR_WORKSPACE (at H = 2560, F = 6912: M up to 1807 tokens).
+ * it return BL_ERR_WORKSPACE (at H = 2560, F = 6912: M up to 1806 tokens).
  * Allocates nothing: the first call on a device looks the array up
  * (hipGetSymbolAddress), so make one call on each device before capturing a
  * graph.  Every call on one GPU shares that GPU's array: calls that overlap

@@ -100,6 +100,26 @@ def test_graph_ffn_stack(M, gated, n):
     replay_matches(f"ffn stack M={M} gated={gated} layers={n}", run, [hs], other)
 
 
+def test_graph_ffn_persistent():
+    """The one-launch persistent stack at one token (its descriptor copy and
+    counter reset are a kernel of their own, no memset): graph replays equal
+    the eager call."""
+    rng = np.random.default_rng(9150)
+    stack = bl.FFNStack(ffn_layers(rng, 3, False), H, F, 1, DEV, persistent=True)
+    h0, h1 = dev(synth.activations(rng, 1, H)), dev(synth.activations(rng, 1, H))
+    hs, ho = torch.empty_like(h0), torch.empty_like(h1)
+
+    def run():
+        hs.copy_(h0)
+        stack(hs)
+
+    def other():
+        ho.copy_(h1)
+        stack(ho)
+
+    replay_matches("persistent ffn stack M=1", run, [hs], other)
+
+
 @pytest.mark.parametrize("M,N", [(1, 6912), (3, 2560), (1, 40008)])
 def test_graph_quant_forward(M, N):
     """The fused quantise + BitLinear launch, including the persistent

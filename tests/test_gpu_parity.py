@@ -1039,3 +1039,59 @@ def test_workload_ffn_stack(M):
     log(f"[workload] ffn stack M={M}: {M} rows x 30 layers teacher-forced, near-tie flips {flips}; "
         f"free running after 30 layers: max |diff| / max |h| per row: max {rel.max():.3g}, median "
         f"{np.median(rel):.3g}")
+
+
+# ------------------------------------------------------------------ persistent one-token stack
+
+@pytest.mark.parametrize("H,F,L,pre,residual", [(256, 640, 3, True, True), (512, 1536, 2, False, True),
+                                                 (256, 1024, 5, True, False), (1024, 256, 2, True, True)])
+def test_ffn_persistent_small(H, F, L, pre, residual):
+    """The one-launch persistent stack (BL_FFN_PERSISTENT) at one token gives
+    bit for bit the two-launch-per-layer path's hidden state (itself checked
+    stage by stage against the oracle), with gains, with and without the
+    pre-norm and the residual, a hidden row longer than the intermediate one,
+    on two calls in a row."""
+    log(f"[persistent] H={H} F={F} L={L} pre={pre} residual={residual}")
+    rng = np.random.default_rng(5100 + H + F + L)
+    gl, ol = to_gpu_layers(ffn_layers_np(rng, L, H, F, gains=True))
+    h0 = synth.activations(rng, 1, H, outliers=True)
+    ref = dev(h0)
+    bl.FFNStack(gl, H, F, 1, DEV, pre_norm=pre, residual=residual)(ref)
+    stack = bl.FFNStack(gl, H, F, 1, DEV, pre_norm=pre, residual=residual, persistent=True)
+    for rep in range(2):
+        h = dev(h0)
+        stack(h)
+        assert_exact(host(h), host(ref), f"persistent vs two launches per layer (call {rep})")
+    # the staged path against the oracle, layer by layer
+    hs = h0
+    for l in range(L):
+        hs, _ = layer_teacher_forced(hs, gl[l], ol[l], 1, pre=pre, residual=residual)
+    assert_exact(host(ref), hs, "two launches per layer vs staged calls")
+
+
+def test_ffn_persistent_model_stack():
+    """The 30-layer stack at hidden 2560 / intermediate 6912 (seed 4) at one
+    token through the persistent launch: bit-identical to the two-launch path
+    (which test_workload_ffn_stack checks layer by layer against the oracle),
+    and a gated layer or more than one token is refused."""
+    log("[persistent] 30-layer model stack, M=1")
+    gl = []
+    rng = None
+    for rng, l, Wu, Wd in synth.ffn_stack_weights():
+        pu, su = bl.pack_weights(dev(Wu))
+        pd, sd = bl.pack_weights(dev(Wd))
+        gl.append({"up": pu, "up_scale": su, "down": pd, "down_scale": sd})
+    h0 = synth.ffn_stack_hidden(rng)[:1].copy()
+    ref = dev(h0)
+    bl.FFNStack(gl, synth.HIDDEN, synth.FFN, 1, DEV)(ref)
+    for rep in range(2):
+        h = dev(h0)
+        bl.FFNStack(gl, synth.HIDDEN, synth.FFN, 1, DEV, persistent=True)(h)
+        assert_exact(host(h), host(ref), f"persistent 30-layer stack vs two launches per layer (call {rep})")
+    h2 = dev(synth.ffn_stack_hidden(rng)[:2].copy())
+    with pytest.raises(bl.BitLinearError) as e:
+        bl.FFNStack(gl, synth.HIDDEN, synth.FFN, 2, DEV, persistent=True)(h2)
+    assert e.value.status == bl.BL_ERR_UNSUPPORTED
+    gated = [dict(gl[0], gate=gl[1]["up"], gate_scale=gl[1]["up_scale"])]
+    with pytest.raises(bl.BitLinearError):
+        bl.FFNStack(gated, synth.HIDDEN, synth.FFN, 1, DEV, persistent=True)(dev(h0))
