@@ -46,6 +46,7 @@ SYMBOLS = (
     "bitlinear_quant_act",
     "bitlinear_forward_workspace_bytes", "bitlinear_forward", "bitlinear_forward_grouped",
     "bitlinear_quant_forward_workspace_bytes", "bitlinear_quant_forward",
+    "bitlinear_quant_forward_grouped_workspace_bytes", "bitlinear_quant_forward_grouped",
     "bitlinear_latent_forward_workspace_bytes", "bitlinear_latent_forward",
     "bitnet_ffn_workspace_bytes", "bitnet_ffn_forward", "bitnet_ffn_forward_noalloc",
 )
@@ -116,6 +117,11 @@ def load(path: str = LIB_PATH):
     lib.bitlinear_forward.restype = I
     lib.bitlinear_forward_grouped.argtypes = [P, P, P, I64, I64, ctypes.POINTER(Group), ctypes.c_int32, P]
     lib.bitlinear_forward_grouped.restype = I
+    lib.bitlinear_quant_forward_grouped_workspace_bytes.argtypes = [I64, I64]
+    lib.bitlinear_quant_forward_grouped_workspace_bytes.restype = ctypes.c_size_t
+    lib.bitlinear_quant_forward_grouped.argtypes = [P, I64, I64, ctypes.c_uint32, P, ctypes.c_float,
+                                                    ctypes.POINTER(Group), ctypes.c_int32, P, ctypes.c_size_t, P]
+    lib.bitlinear_quant_forward_grouped.restype = I
     lib.bitlinear_quant_forward_workspace_bytes.argtypes = [I64, I64, I64]
     lib.bitlinear_quant_forward_workspace_bytes.restype = SZ
     lib.bitlinear_quant_forward.argtypes = [P, I64, I64, U32, P, F, P, P, I64, ctypes.POINTER(Epilogue),
@@ -323,17 +329,8 @@ def forward(xq: torch.Tensor, x_scale: torch.Tensor, packed: torch.Tensor, w_sca
     return res
 
 
-def forward_grouped(xq: torch.Tensor, x_scale: torch.Tensor, x_rowsum: torch.Tensor, mats: Sequence[dict]):
-    """Several BitLinears of the same K on the same int8 rows in one call
-    (bitlinear_forward_grouped).  Each dict of ``mats`` holds ``packed``,
-    ``w_scale`` and optionally ``relu2``, ``residual``, ``mul_by``, ``subln``,
-    ``norm_gain``, ``eps``, ``want_acc``, ``y_out``; returns one result dict
-    per matrix, as :func:`forward` does."""
-    lib = load()
-    _need(xq, torch.int8, 2, "xq")
-    M, K = xq.shape
-    _shape(x_scale, torch.float32, (M,), "x_scale")
-    _shape(x_rowsum, torch.int32, (M,), "x_rowsum")
+def _groups(mats: Sequence[dict], M: int, K: int, dev):
+    """The bl_group array and the result dicts of a grouped call."""
     if not 1 <= len(mats) <= BL_MAX_GROUPS:
         raise ValueError(f"1 to {BL_MAX_GROUPS} matrices per call, got {len(mats)}")
     for i, d in enumerate(mats):
@@ -347,8 +344,6 @@ def forward_grouped(xq: torch.Tensor, x_scale: torch.Tensor, x_rowsum: torch.Ten
         if d.get("subln"):
             _shape(d.get("norm_gain"), torch.float32, (N,), f"matrix {i} norm_gain")
         _on_gpu(d["packed"], d["w_scale"], d.get("residual"), d.get("mul_by"), d.get("y_out"), d.get("norm_gain"))
-    _on_gpu(xq, x_scale, x_rowsum)
-    dev = xq.device
     arr = (Group * len(mats))()
     results = []
     for i, d in enumerate(mats):
@@ -382,7 +377,49 @@ def forward_grouped(xq: torch.Tensor, x_scale: torch.Tensor, x_rowsum: torch.Ten
             res["acc"] = torch.empty((M, N), dtype=torch.int32, device=dev)
             g.acc_out = res["acc"].data_ptr()
         results.append(res)
-    _check(lib.bitlinear_forward_grouped(_p(xq), _p(x_scale), _p(x_rowsum), M, K, arr, len(mats), _stream(dev)))
+    return arr, results
+
+
+def forward_grouped(xq: torch.Tensor, x_scale: torch.Tensor, x_rowsum: torch.Tensor, mats: Sequence[dict]):
+    """Several BitLinears of the same K on the same int8 rows in one call
+    (bitlinear_forward_grouped).  Each dict of ``mats`` holds ``packed``,
+    ``w_scale`` and optionally ``relu2``, ``residual``, ``mul_by``, ``subln``,
+    ``norm_gain``, ``eps``, ``want_acc``, ``y_out``; returns one result dict
+    per matrix, as :func:`forward` does."""
+    lib = load()
+    _need(xq, torch.int8, 2, "xq")
+    M, K = xq.shape
+    _shape(x_scale, torch.float32, (M,), "x_scale")
+    _shape(x_rowsum, torch.int32, (M,), "x_rowsum")
+    _on_gpu(xq, x_scale, x_rowsum)
+    arr, results = _groups(mats, M, K, xq.device)
+    _check(lib.bitlinear_forward_grouped(_p(xq), _p(x_scale), _p(x_rowsum), M, K, arr, len(mats), _stream(xq.device)))
+    return results
+
+
+def quant_forward_grouped(X: torch.Tensor, mats: Sequence[dict], rmsnorm: bool = False,
+                          norm_gain: Optional[torch.Tensor] = None, eps: float = RMS_EPS,
+                          ws: Optional[torch.Tensor] = None):
+    """bitlinear_quant_forward_grouped: quantise fp32 rows X (optional
+    RMSNorm) and apply every matrix of ``mats`` (as in
+    :func:`forward_grouped`) to them; one launch for a few tokens against
+    many tiles.  ``ws`` (uint8, at least the call's workspace size) may be
+    passed to avoid an allocation."""
+    lib = load()
+    _need(X, torch.float32, 2, "X")
+    M, K = X.shape
+    _shape(norm_gain, torch.float32, (K,), "norm_gain")
+    _on_gpu(X, norm_gain)
+    arr, results = _groups(mats, M, K, X.device)
+    nb = lib.bitlinear_quant_forward_grouped_workspace_bytes(M, K)
+    if ws is None:
+        ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=X.device)
+    _need(ws, torch.uint8, 1, "ws")
+    if ws.numel() < nb:
+        raise ValueError(f"ws holds {ws.numel()} bytes, the call needs {nb}")
+    _on_gpu(ws)
+    _check(lib.bitlinear_quant_forward_grouped(_p(X), M, K, BL_QUANT_RMSNORM if rmsnorm else 0, _p(norm_gain),
+                                               float(eps), arr, len(mats), _p(ws), ws.numel(), _stream(X.device)))
     return results
 
 

@@ -345,9 +345,13 @@ int bitlinear_forward(const int8_t* Xq, const float* x_scale, const int32_t* x_r
 
 // ---------------------------------------------------------------- grouped forward
 
-int bitlinear_forward_grouped(const int8_t* Xq, const float* x_scale, const int32_t* x_rowsum, int64_t M,
-                              int64_t K, const bl_group* groups, int32_t n_groups, hipStream_t stream) {
-    const char* who = "forward_grouped";
+}  // extern "C"
+
+namespace {
+// Every check of bitlinear_forward_grouped: each matrix as bitlinear_forward
+// would check it, and no output of one matrix overlapping another's data.
+int check_grouped(const char* who, const int8_t* Xq, const float* x_scale, const int32_t* x_rowsum, int64_t M,
+                  int64_t K, const bl_group* groups, int32_t n_groups) {
     if (n_groups < 1 || n_groups > BL_MAX_GROUPS)
         return fail(BL_ERR_UNSUPPORTED, "%s: n_groups = %d outside 1..%d", who, n_groups, BL_MAX_GROUPS);
     if (!groups) return fail(BL_ERR_NULL, "%s: groups is required", who);
@@ -385,15 +389,37 @@ int bitlinear_forward_grouped(const int8_t* Xq, const float* x_scale, const int3
                         return fail(BL_ERR_UNSUPPORTED, "%s: an output of matrix %d overlaps matrix %d's data", who,
                                     a, b);
         }
-    if (M == 0) return ok();
+    return BL_OK;
+}
 
-    bl::GroupMat mats[BL_MAX_GROUPS];
-    bool one_launch = n_groups <= bl::gemv_max_groups();
+void group_mats(const bl_group* groups, int32_t n_groups, bl::GroupMat (&mats)[BL_MAX_GROUPS]) {
     for (int32_t g = 0; g < n_groups; ++g) {
         const bl_group& G = groups[g];
         mats[g] = bl::GroupMat{G.packed, G.w_scale, G.N, kernel_epi(&G.epi), G.Y, G.acc_out};
-        one_launch = one_launch && bl::gemv_supported(M, K, G.N);
     }
+}
+
+// The subln requant of every matrix that asks for it, after its contraction.
+int grouped_requant(const char* who, int64_t M, const bl_group* groups, int32_t n_groups, hipStream_t stream) {
+    for (int32_t g = 0; g < n_groups; ++g) {
+        const bl_group& G = groups[g];
+        if (!(G.epi.flags & BL_EPI_SUBLN_QUANT)) continue;
+        hipError_t e = bl::launch_quant(G.Y, M, G.N, true, G.epi.norm_gain, G.epi.norm_eps, G.epi.out_q,
+                                        G.epi.out_q_scale, G.epi.out_q_rowsum, stream);
+        if (e != hipSuccess) return hip_status(e, who);
+    }
+    return ok();
+}
+
+// The contraction launches of a checked grouped forward from int8 rows: one
+// launch when every matrix fits the skinny kernels, else one per matrix;
+// then the subln requants.
+int run_grouped(const int8_t* Xq, const float* x_scale, const int32_t* x_rowsum, int64_t M, int64_t K,
+                const bl_group* groups, int32_t n_groups, hipStream_t stream) {
+    bl::GroupMat mats[BL_MAX_GROUPS];
+    group_mats(groups, n_groups, mats);
+    bool one_launch = n_groups <= bl::gemv_max_groups();
+    for (int32_t g = 0; g < n_groups; ++g) one_launch = one_launch && bl::gemv_supported(M, K, mats[g].N);
     hipError_t e = hipSuccess;
     if (one_launch) {
         e = bl::launch_gemv_grouped(Xq, x_scale, x_rowsum, M, K, mats, n_groups, stream);
@@ -405,14 +431,88 @@ int bitlinear_forward_grouped(const int8_t* Xq, const float* x_scale, const int3
             if (e != hipSuccess) return hip_status(e, "forward_grouped: contraction");
         }
     }
+    return grouped_requant("forward_grouped: subln requant", M, groups, n_groups, stream);
+}
+
+// A stand-in address for the workspace rows of a call with no rows.
+alignas(256) char g_no_rows[16];
+
+size_t quant_grouped_ws(int64_t M, int64_t K) {
+    Carver c(nullptr);
+    c.take<int8_t>((size_t)(M * K));
+    c.take<float>((size_t)M);
+    c.take<int32_t>((size_t)M);
+    return c.off;
+}
+}  // namespace
+
+extern "C" {
+
+int bitlinear_forward_grouped(const int8_t* Xq, const float* x_scale, const int32_t* x_rowsum, int64_t M,
+                              int64_t K, const bl_group* groups, int32_t n_groups, hipStream_t stream) {
+    if (int r = check_grouped("forward_grouped", Xq, x_scale, x_rowsum, M, K, groups, n_groups)) return r;
+    if (M == 0) return ok();
+    return run_grouped(Xq, x_scale, x_rowsum, M, K, groups, n_groups, stream);
+}
+
+size_t bitlinear_quant_forward_grouped_workspace_bytes(int64_t M, int64_t K) {
+    if (M < 1 || K < 1) return 0;
+    return quant_grouped_ws(M, K);
+}
+
+int bitlinear_quant_forward_grouped(const float* X, int64_t M, int64_t K, uint32_t quant_flags,
+                                    const float* norm_gain, float norm_eps, const bl_group* groups,
+                                    int32_t n_groups, void* ws, size_t ws_bytes, hipStream_t stream) {
+    const char* who = "quant_forward_grouped";
+    if (!X) return fail(BL_ERR_NULL, "%s: X is required", who);
+    if (quant_flags & ~BL_QUANT_RMSNORM) return fail(BL_ERR_UNSUPPORTED, "%s: unknown quant flags 0x%x", who, quant_flags);
+    if (M < 0) return fail(BL_ERR_SHAPE, "%s: M = %lld must be >= 0", who, (long long)M);
+    if (K < 64 || K % 64 != 0)
+        return fail(BL_ERR_SHAPE, "%s: K = %lld must be a positive multiple of 64", who, (long long)K);
+    if (!bl::quant_supported(K)) return fail(BL_ERR_UNSUPPORTED, "%s: K = %lld above 32768", who, (long long)K);
+    if (M * K >= kLimit) return fail(BL_ERR_SHAPE, "%s: sizes exceed 2^31 elements", who);
+    if (!aligned(X, 16) || !aligned(norm_gain, 16)) return fail(BL_ERR_ALIGN, "%s: X and gain need 16-byte alignment", who);
+    if (int r = check_workspace(ws, ws_bytes, M == 0 ? 0 : quant_grouped_ws(M, K))) return r;
+    Carver c(ws);
+    int8_t* xq = c.take<int8_t>((size_t)(M * K));
+    float* xs = c.take<float>((size_t)M);
+    int32_t* rs = c.take<int32_t>((size_t)M);
+    if (M == 0) {  // no rows: nothing is read or written, only the checks run
+        xq = reinterpret_cast<int8_t*>(g_no_rows);
+        xs = reinterpret_cast<float*>(g_no_rows);
+        rs = reinterpret_cast<int32_t*>(g_no_rows);
+    }
+    // the matrices against the quantised rows in the workspace, and X (and
+    // the gain) against every output, which other workgroups write while
+    // every workgroup still reads X
+    if (int r = check_grouped(who, xq, xs, rs, M, K, groups, n_groups)) return r;
+    const size_t xb = (size_t)(M * K) * 4;
+    if (overlap(X, xb, ws, quant_grouped_ws(M, K)) || (norm_gain && overlap(norm_gain, (size_t)K * 4, ws, quant_grouped_ws(M, K))))
+        return fail(BL_ERR_UNSUPPORTED, "%s: X or the gain overlaps the workspace", who);
     for (int32_t g = 0; g < n_groups; ++g) {
         const bl_group& G = groups[g];
-        if (!(G.epi.flags & BL_EPI_SUBLN_QUANT)) continue;
-        e = bl::launch_quant(G.Y, M, G.N, true, G.epi.norm_gain, G.epi.norm_eps, G.epi.out_q, G.epi.out_q_scale,
-                             G.epi.out_q_rowsum, stream);
-        if (e != hipSuccess) return hip_status(e, "forward_grouped: subln requant");
+        const bool sg = (G.epi.flags & BL_EPI_SUBLN_QUANT) != 0;
+        const size_t yb = (size_t)(M * G.N) * 4;
+        const void* outs[5] = {G.Y, G.acc_out, sg ? G.epi.out_q : nullptr, sg ? G.epi.out_q_scale : nullptr,
+                               sg ? G.epi.out_q_rowsum : nullptr};
+        const size_t ob[5] = {yb, yb, (size_t)(M * G.N), (size_t)M * 4, (size_t)M * 4};
+        for (int o = 0; o < 5; ++o)
+            if (overlap(outs[o], ob[o], X, xb) || (norm_gain && overlap(outs[o], ob[o], norm_gain, (size_t)K * 4)))
+                return fail(BL_ERR_UNSUPPORTED, "%s: an output of matrix %d overlaps X or the gain", who, g);
     }
-    return ok();
+    if (M == 0) return ok();
+    const bool rms = (quant_flags & BL_QUANT_RMSNORM) != 0;
+    bl::GroupMat mats[BL_MAX_GROUPS];
+    group_mats(groups, n_groups, mats);
+    if (bl::gemv_grouped_quant_supported(M, K, mats, n_groups)) {
+        hipError_t e = bl::launch_gemv_grouped_quant(X, M, K, rms, rms ? norm_gain : nullptr, norm_eps, mats,
+                                                     n_groups, stream);
+        if (e != hipSuccess) return hip_status(e, "quant_forward_grouped: contraction");
+        return grouped_requant("quant_forward_grouped: subln requant", M, groups, n_groups, stream);
+    }
+    hipError_t e = bl::launch_quant(X, M, K, rms, rms ? norm_gain : nullptr, norm_eps, xq, xs, rs, stream);
+    if (e != hipSuccess) return hip_status(e, "quant_forward_grouped: quantise");
+    return run_grouped(xq, xs, rs, M, K, groups, n_groups, stream);
 }
 
 // ---------------------------------------------------------------- fused quant + forward

@@ -192,6 +192,22 @@ __device__ __forceinline__ int signed4(uint32_t w, int j) {
     return (int)((((w >> (2 * j)) & 0x03030303u) + 0x7F7F7F7Fu) ^ 0x80808080u);
 }
 
+// Four elements quantised at scale s, q = clamp(rint(x * s), -127, 127), as
+// four int8 in one word (element b in byte b).  Each q is formed as the byte
+// of q + 128 in 1..255 (an exact float, med3 being the clamp, converted and
+// inserted in one instruction); flipping bit 7 then turns the biased byte
+// into the two's-complement int8 q.
+__device__ __forceinline__ uint32_t quant4(float4 v, float s) {
+    const float e[4] = {v.x, v.y, v.z, v.w};
+    uint32_t packed = 0;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        const float t = __builtin_amdgcn_fmed3f(rintf(e[b] * s), -127.0f, 127.0f);
+        packed = __builtin_amdgcn_cvt_pk_u8_f32(t + 128.0f, b, packed);
+    }
+    return packed ^ 0x80808080u;
+}
+
 // One token row of the activation quantiser, run by a whole workgroup of NT
 // threads: optional RMSNorm (binary64 sum of squares, r rounded once to
 // binary32, z = (x * r) * gain), then absmax int8 quantisation.  Thread t
@@ -302,18 +318,7 @@ __device__ __forceinline__ float quant_row_finish(float4 (&v)[NV], const float4 
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
         const int idx = (VT == NT || (int)threadIdx.x < VT) ? threadIdx.x + i * VT : n4;  // n4: stores nothing
-        const float e[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
-        uint32_t packed = 0;
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            // q = clamp(rint(x * s), -127, 127) (med3 is the clamp), stored as
-            // the byte of q + 128 in 1..255 (an exact float, converted and
-            // inserted in one instruction); flipping bit 7 below turns the
-            // biased byte into the two's-complement int8 q
-            const float t = __builtin_amdgcn_fmed3f(rintf(e[b] * s), -127.0f, 127.0f);
-            packed = __builtin_amdgcn_cvt_pk_u8_f32(t + 128.0f, b, packed);
-        }
-        packed ^= 0x80808080u;
+        const uint32_t packed = quant4(v[i], s);
         sum = __builtin_amdgcn_sdot4((int)packed, 0x01010101, sum, false);  // slots past the row hold 0
         if (idx < n4) q4[idx] = (int)packed;
     }

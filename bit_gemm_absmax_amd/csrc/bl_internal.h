@@ -71,6 +71,12 @@ struct GroupMat {
 int gemv_max_groups();
 hipError_t launch_gemv_grouped(const int8_t* Xq, const float* xs, const int32_t* rs, int64_t M, int64_t K,
                                const GroupMat* groups, int count, hipStream_t s);
+// The grouped contraction quantising its fp32 rows itself (bitlinear_quant_act
+// then launch_gemv_grouped, in one launch, with the same results): few
+// tokens, K whose quantiser runs 256 threads, many tiles.
+bool gemv_grouped_quant_supported(int64_t M, int64_t K, const GroupMat* g, int count);
+hipError_t launch_gemv_grouped_quant(const float* X, int64_t M, int64_t K, bool rmsnorm, const float* gain, float eps,
+                                     const GroupMat* g, int count, hipStream_t s);
 
 // The gated pair ReLU^2(BitLinear(x; gate)) * BitLinear(x; up) in one
 // skinny launch (same shapes as launch_gemv).

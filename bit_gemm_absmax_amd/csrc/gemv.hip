@@ -809,12 +809,120 @@ __device__ __forceinline__ void stat_load_weights(const uint8_t* W, int n0, int 
     }
 }
 
-template <int MT, int QMAX>
+// The rows to quantise inside the launch (fp32, the quantiser's optional
+// RMSNorm), or X == nullptr when the launch reads int8 rows.
+struct StatQuant {
+    const float* X;     // [M][K]
+    const float* gain;  // [K] or nullptr
+    float eps;
+    int rms;
+};
+
+// One row as the 256-thread quantiser holds it, in one wave: lane l plays
+// threads l + 64 u (u < 4), each with its float4 indices t + 256 i (i < NV).
+template <int NV>
+__device__ __forceinline__ void wrow_load(const float* X, int K, float4 (&v)[4][NV]) {
+    const int lane = threadIdx.x % kWave;
+    const Rsrc rx = make_rsrc(X, X != nullptr ? (uint32_t)K * 4u : 0u);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int i = 0; i < NV; ++i) v[u][i] = buf_load16f(rx, (uint32_t)(lane + 64 * u + 256 * i) * 16u);
+}
+
+// quant_row_finish for NT = 256, run by one wave for row r of the copy: the
+// same per-thread order, the same DPP tree per played wave and the four wave
+// sums added in index order, so the same bits as the standalone quantiser.
+// The int8 row goes into the copy's slots (float4 f = four bytes of chunk
+// f / 4), gamma and the int8 row sum into s_xs[r], s_rs[r].
+template <int NV>
+__device__ __forceinline__ void wrow_quant(float4 (&v)[4][NV], const float4 (&gv)[4][NV], int K, bool rms,
+                                           bool has_gain, float eps, int r, int8_t* act, uint32_t nch, float* s_xs,
+                                           int* s_rs) {
+    const int lane = threadIdx.x % kWave;
+    const int n4 = K / 4;
+    float amax = 0.0f;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int i = 0; i < NV; ++i)
+            amax = fmaxf(fmaxf(amax, fmaxf(fabsf(v[u][i].x), fabsf(v[u][i].y))),
+                         fmaxf(fabsf(v[u][i].z), fabsf(v[u][i].w)));
+    float g;
+    if (rms) {
+        double t = 0.0;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            double ss = 0.0;
+#pragma unroll
+            for (int i = 0; i < NV; ++i) {
+                ss = __builtin_fma((double)v[u][i].x, (double)v[u][i].x, ss);
+                ss = __builtin_fma((double)v[u][i].y, (double)v[u][i].y, ss);
+                ss = __builtin_fma((double)v[u][i].z, (double)v[u][i].z, ss);
+                ss = __builtin_fma((double)v[u][i].w, (double)v[u][i].w, ss);
+            }
+            t += wave_sum(ss);
+        }
+        const float rr = (float)(1.0 / sqrt(t / (double)K + (double)eps));
+        float az = 0.0f;
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int i = 0; i < NV; ++i) {
+                float4 z = v[u][i];
+                z.x = z.x * rr;
+                z.y = z.y * rr;
+                z.z = z.z * rr;
+                z.w = z.w * rr;
+                if (has_gain) {
+                    z.x = z.x * gv[u][i].x;
+                    z.y = z.y * gv[u][i].y;
+                    z.z = z.z * gv[u][i].z;
+                    z.w = z.w * gv[u][i].w;
+                    az = fmaxf(fmaxf(az, fmaxf(fabsf(z.x), fabsf(z.y))), fmaxf(fabsf(z.z), fabsf(z.w)));
+                }
+                v[u][i] = z;
+            }
+        g = has_gain ? wave_max(az) : wave_max(amax) * rr;
+    } else {
+        g = wave_max(amax);
+    }
+    if (!(g >= 1e-5f)) g = 1e-5f;
+    const float sc = 127.0f / g;
+    int sum = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int f = lane + 64 * u + 256 * i;
+            const uint32_t packed = quant4(v[u][i], sc);
+            sum = __builtin_amdgcn_sdot4((int)packed, 0x01010101, sum, false);  // slots past the row hold 0
+            if (f < n4)
+                *reinterpret_cast<uint32_t*>(act + stat_slot((uint32_t)r, (uint32_t)f / 4u, (uint32_t)K, nch) +
+                                             4 * (f % 4)) = packed;
+        }
+    sum = wave_sum(sum);
+    if (lane == 0) {
+        s_xs[r] = g;
+        s_rs[r] = sum;
+    }
+}
+
+// NVQ > 0: the launch quantises the fp32 rows of sq itself (one token tile,
+// M <= 8: wave w takes rows w and w + 4), NVQ float4 per played thread;
+// Xq, x_scale and x_rowsum are then unused.
+template <int MT, int QMAX, int NVQ>
 __global__ __launch_bounds__(kStatWaves* kWave) void k_stat(const int8_t* __restrict__ Xq,
                                                              const float* __restrict__ x_scale,
                                                              const int32_t* __restrict__ x_rowsum, int M, int K,
-                                                             const BatchMats mats, int tiles, uint32_t kdiv) {
+                                                             const BatchMats mats, int tiles, uint32_t kdiv,
+                                                             const StatQuant sq) {
+    static_assert(NVQ == 0 || MT == 1, "in-launch quantisation covers one token tile");
     __shared__ __align__(1024) int8_t act[kStatLds];
+    // quantised in the launch: gamma and row sums of the 16 rows in the last
+    // 128 bytes (the rows themselves take at most 16 * 2560 bytes)
+    float* s_xs = reinterpret_cast<float*>(act + kStatLds - 128);
+    int* s_rs = reinterpret_cast<int*>(act + kStatLds - 64);
     const int lane = threadIdx.x % kWave;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int fr = lane & 15;
@@ -825,14 +933,32 @@ __global__ __launch_bounds__(kStatWaves* kWave) void k_stat(const int8_t* __rest
     const int stride = (int)gridDim.x * kStatWaves;
     int tile = (int)blockIdx.x * kStatWaves + wave;
 
-    // ---- the first tile's weights go out first, so their latency overlaps
-    // the activation copy
     uint4 w[QMAX];
     StatTile T = stat_tile(mats, tile < tiles ? tile : 0);
-    stat_load_weights<QMAX>(T.W, T.n0, T.rows, K, C, nq, fr, fg, w);
+    float xs[MT][4];
+    int rsum[MT][4];
+    if constexpr (NVQ > 0) {
+        // ---- the rows' loads first (vector loads complete in issue order,
+        // and the quantisation waits for them only), then the first tile's
+        // weights, which land while the rows are quantised; rows past M are
+        // left as they are (their outputs are never stored)
+        const int r0 = wave, r1 = wave + kStatWaves;
+        float4 v0[4][NVQ], v1[4][NVQ], gv[4][NVQ];
+        wrow_load<NVQ>(r0 < M ? sq.X + (int64_t)r0 * K : nullptr, K, v0);
+        wrow_load<NVQ>(r1 < M ? sq.X + (int64_t)r1 * K : nullptr, K, v1);
+        const bool has_gain = sq.rms && sq.gain != nullptr;
+        wrow_load<NVQ>(has_gain ? sq.gain : nullptr, K, gv);
+        __builtin_amdgcn_sched_barrier(0);
+        stat_load_weights<QMAX>(T.W, T.n0, T.rows, K, C, nq, fr, fg, w);
+        __builtin_amdgcn_sched_barrier(0);
+        if (r0 < M) wrow_quant<NVQ>(v0, gv, K, sq.rms != 0, has_gain, sq.eps, r0, act, nch, s_xs, s_rs);
+        if (r1 < M) wrow_quant<NVQ>(v1, gv, K, sq.rms != 0, has_gain, sq.eps, r1, act, nch, s_xs, s_rs);
+    } else {
+        // ---- the first tile's weights go out first, so their latency
+        // overlaps the activation copy
+        stat_load_weights<QMAX>(T.W, T.n0, T.rows, K, C, nq, fr, fg, w);
 
-    // ---- the activation copy: MT * 16 rows (rows past M read zeros)
-    {
+        // ---- the activation copy: MT * 16 rows (rows past M read zeros)
         const Rsrc rx = make_rsrc(Xq, (uint32_t)M * (uint32_t)K);
         const int ninst = MT * 16 * K / 1024;
         for (int i = wave; i < ninst; i += kStatWaves) {
@@ -845,13 +971,9 @@ __global__ __launch_bounds__(kStatWaves* kWave) void k_stat(const int8_t* __rest
             // the global chunk held by this LDS slot: the swizzle is its own inverse
             dma16(rx, (lds_ptr)(act + 1024 * i), stat_slot(r, j, (uint32_t)K, nch), 0u);
         }
-    }
 
-    // ---- the rows' scales and sums for this lane's outputs: acc[t][q] is
-    // token 16 t + 4 fg + q, output column fr of the tile
-    float xs[MT][4];
-    int rsum[MT][4];
-    {
+        // ---- the rows' scales and sums for this lane's outputs: acc[t][q] is
+        // token 16 t + 4 fg + q, output column fr of the tile
         const Rsrc rs = make_rsrc(x_scale, (uint32_t)M * 4u);
         const Rsrc rr = make_rsrc(x_rowsum, (uint32_t)M * 4u);
 #pragma unroll
@@ -872,6 +994,14 @@ __global__ __launch_bounds__(kStatWaves* kWave) void k_stat(const int8_t* __rest
         for (int d = 0; d < 4; ++d) ap[t][d] = act + (16 * t + fr) * K + 16 * ((4 * fg + d) ^ fr);
     __builtin_amdgcn_s_waitcnt(0);  // this wave's copy (and first weights) have landed
     __syncthreads();                // and every other wave's copy
+    if constexpr (NVQ > 0) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int m = 4 * fg + q;  // rows past M: never stored
+            xs[0][q] = s_xs[m];
+            rsum[0][q] = s_rs[m];
+        }
+    }
 
     for (bool first = true; tile < tiles; tile += stride, first = false) {
         if (!first) {
@@ -1131,9 +1261,9 @@ static bool stat_shape(int64_t M, int64_t K, int64_t tiles) {
            tiles >= kStatMinTiles;
 }
 
-template <int MT, int Q>
+template <int MT, int Q, int NVQ = 0>
 static hipError_t go_stat(const int8_t* Xq, const float* xs, const int32_t* rs, int64_t M, int64_t K, BatchMats mats,
-                          hipStream_t s) {
+                          hipStream_t s, const StatQuant sq = StatQuant{nullptr, nullptr, 0.0f, 0}) {
     int64_t tiles = 0;
     for (int i = 0; i < mats.count; ++i) {
         mats.m[i].wg0 = (int)tiles;
@@ -1143,8 +1273,8 @@ static hipError_t go_stat(const int8_t* Xq, const float* xs, const int32_t* rs, 
     const int64_t cus = cu_count();
     const unsigned blocks = (unsigned)(want < cus ? want : cus);
     const uint32_t kdiv = (uint32_t)((((uint64_t)1 << 32) + (uint64_t)K - 1) / (uint64_t)K);
-    hipLaunchKernelGGL((k_stat<MT, Q>), dim3(blocks), dim3(kStatWaves * kWave), 0, s, Xq, xs, rs, (int)M, (int)K,
-                       mats, (int)tiles, kdiv);
+    hipLaunchKernelGGL((k_stat<MT, Q, NVQ>), dim3(blocks), dim3(kStatWaves * kWave), 0, s, Xq, xs, rs, (int)M,
+                       (int)K, mats, (int)tiles, kdiv, sq);
     return hipGetLastError();
 }
 
@@ -1158,6 +1288,25 @@ static hipError_t go_stat_mt(const int8_t* Xq, const float* xs, const int32_t* r
     BL_SQ_MT(1) BL_SQ_MT(2)
 #undef BL_SQ_MT
 #undef BL_SQ
+    return hipErrorInvalidValue;
+}
+
+// The stationary launch that quantises its fp32 rows itself: at most 8
+// tokens (each wave quantises two rows the way the 256-thread quantiser
+// would, while the first tile's weights are in flight).
+constexpr int64_t kStatQuantMaxM = 8;
+
+static bool stat_quant_shape(int64_t M, int64_t K, int64_t tiles) {
+    return M <= kStatQuantMaxM && quant_threads(K) == 256 && stat_shape(M, K, tiles);
+}
+
+static hipError_t go_stat_quant(const StatQuant& sq, int64_t M, int64_t K, const BatchMats& mats, hipStream_t s) {
+    const int q = (int)((K / 64 + 3) / 4);  // NVQ: float4 per played thread of 256, (K / 4) / 256 rounded up
+#define BL_SQQ(Q, NV) \
+    if (q == Q) return go_stat<1, Q, NV>(nullptr, nullptr, nullptr, M, K, mats, s, sq);
+    BL_SQQ(1, 1) BL_SQQ(2, 1) BL_SQQ(3, 1) BL_SQQ(4, 1) BL_SQQ(5, 2) BL_SQQ(6, 2) BL_SQQ(7, 2) BL_SQQ(8, 2)
+    BL_SQQ(9, 3) BL_SQQ(10, 3)
+#undef BL_SQQ
     return hipErrorInvalidValue;
 }
 
@@ -1201,6 +1350,22 @@ hipError_t launch_gemv_grouped(const int8_t* Xq, const float* xs, const int32_t*
     }
     mats.count = count;
     return go_batch_mats(Xq, xs, rs, M, K, rows, mats, s);
+}
+
+bool gemv_grouped_quant_supported(int64_t M, int64_t K, const GroupMat* g, int count) {
+    if (count < 1 || count > kMaxGroups || M < 1) return false;
+    int64_t tiles = 0;
+    for (int i = 0; i < count; ++i) tiles += (g[i].N + 15) / 16;
+    return stat_quant_shape(M, K, tiles);
+}
+
+hipError_t launch_gemv_grouped_quant(const float* X, int64_t M, int64_t K, bool rmsnorm, const float* gain, float eps,
+                                     const GroupMat* g, int count, hipStream_t s) {
+    if (!gemv_grouped_quant_supported(M, K, g, count)) return hipErrorInvalidValue;
+    BatchMats mats{};
+    for (int i = 0; i < count; ++i) mats.m[i] = batch_mat(g[i].packed, g[i].w_scale, g[i].N, g[i].epi, g[i].Y, g[i].acc_out);
+    mats.count = count;
+    return go_stat_quant(StatQuant{X, gain, eps, rmsnorm ? 1 : 0}, M, K, mats, s);
 }
 
 // The gated pair in one launch: one workgroup per 16 output rows, streaming

@@ -90,7 +90,7 @@ const char* bitlinear_last_error(void);
 
 /* ABI version of this header, (major << 16) | minor. */
 int bitlinear_abi_version(void);
-#define BITLINEAR_ABI_VERSION ((1 << 16) | 3)
+#define BITLINEAR_ABI_VERSION ((1 << 16) | 4)
 
 /* ------------------------------------------------------------------------
  * Weight packing ("Model details" / Quantization: absmean ternary weights).
@@ -281,6 +281,28 @@ int bitlinear_quant_forward(const float* X, int64_t M, int64_t K, uint32_t quant
                             const uint8_t* packed, const float* w_scale, int64_t N,
                             const bl_epilogue* epi, float* Y,
                             void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Grouped fused quantise + BitLinear: bitlinear_quant_act followed by
+ * bitlinear_forward_grouped on the quantised rows, with the same results
+ * bit for bit.  For a few tokens (M <= 8) against many 16-row tiles in all
+ * (at least 512, K <= 2560) it is one contraction launch in which every
+ * workgroup quantises the rows itself, exactly as the standalone quantiser
+ * would; otherwise the rows are quantised into the workspace first.
+ *
+ * X           in  fp32 [M][K]; quant_flags / norm_gain / norm_eps as in
+ *                 bitlinear_quant_act
+ * groups      as in bitlinear_forward_grouped; no output may overlap X, the
+ *                 gain or the workspace
+ * ws          scratch of bitlinear_quant_forward_grouped_workspace_bytes(M, K)
+ *             (the quantised rows; its contents afterwards are unspecified)
+ * Errors as bitlinear_quant_act and bitlinear_forward_grouped.
+ * ---------------------------------------------------------------------- */
+size_t bitlinear_quant_forward_grouped_workspace_bytes(int64_t M, int64_t K);
+int bitlinear_quant_forward_grouped(const float* X, int64_t M, int64_t K, uint32_t quant_flags,
+                                    const float* norm_gain, float norm_eps,
+                                    const bl_group* groups, int32_t n_groups,
+                                    void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * BitLinear from latent weights, the forward pass of quantisation-aware

@@ -46,7 +46,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.bitlinear_abi_version() == (1 << 16) | 3
+    assert lib.bitlinear_abi_version() == (1 << 16) | 4
     for s in range(-6, 1):
         assert lib.bitlinear_status_string(s)
     assert lib.bitlinear_status_string(-99) == b"unknown status"
@@ -370,6 +370,8 @@ def test_no_device_gives_hip_status(lib):
         "unpack": lambda: lib.bitlinear_unpack_weights(A, 4, 64, B, None),
         "grouped": lambda: lib.bitlinear_forward_grouped(A, B, D, 2, 64, (bl.Group * 1)(bl.Group(
             packed=C.value, w_scale=B.value, N=8, Y=Y.value)), 1, None),
+        "quant_grouped": lambda: lib.bitlinear_quant_forward_grouped(A, 2, 64, 0, None, 1e-5, (bl.Group * 1)(bl.Group(
+            packed=C.value, w_scale=B.value, N=8, Y=Y.value)), 1, WS, WSN, None),
         "latent_forward": lambda: lib.bitlinear_latent_forward(A, 2, 64, 0, None, 1e-5, B, bl.BL_DTYPE_F32, 8, nul,
                                                                D, None, WS, WSN, None),
     }
@@ -414,3 +416,39 @@ def test_forward_grouped_validation(lib):
     assert f(A, B, D, 2, 64, H, 2, None) == bl.BL_ERR_UNSUPPORTED
     H[0].epi.residual = H[0].Y                                            # its own Y: in place, allowed
     assert f(A, B, D, 0, 64, H, 2, None) == bl.BL_OK
+
+
+def test_quant_forward_grouped_validation(lib):
+    """The grouped fused quantise + forward: its own checks of X, the flags,
+    K and the workspace, every check of the grouped forward against the
+    workspace rows, and no output over X, the gain or the workspace; all
+    before any launch."""
+    f = lib.bitlinear_quant_forward_grouped
+    nb = lib.bitlinear_quant_forward_grouped_workspace_bytes(2, 64)
+    assert nb >= 2 * 64 + 8
+    assert lib.bitlinear_quant_forward_grouped_workspace_bytes(0, 64) == 0
+    WS = ctypes.c_void_p(C.value + (1 << 16))
+    G = (bl.Group * 2)()
+    for i in range(2):
+        G[i].packed, G[i].w_scale, G[i].N = C.value + i * 4096, D.value + 16 * i, 16
+        G[i].Y = Y.value + i * 4096
+    assert f(None, 2, 64, 0, None, 1e-5, G, 2, WS, nb, None) == bl.BL_ERR_NULL
+    assert f(A, 2, 64, 0x8, None, 1e-5, G, 2, WS, nb, None) == bl.BL_ERR_UNSUPPORTED
+    assert f(A, 2, 96, 0, None, 1e-5, G, 2, WS, nb, None) == bl.BL_ERR_SHAPE
+    assert f(A, -1, 64, 0, None, 1e-5, G, 2, WS, nb, None) == bl.BL_ERR_SHAPE
+    assert f(ctypes.c_void_p(A.value + 4), 2, 64, 0, None, 1e-5, G, 2, WS, nb, None) == bl.BL_ERR_ALIGN
+    assert f(A, 2, 64, 0, None, 1e-5, G, 2, WS, nb - 1, None) == bl.BL_ERR_WORKSPACE
+    assert f(A, 2, 64, 0, None, 1e-5, G, 2, None, nb, None) == bl.BL_ERR_WORKSPACE
+    assert f(A, 2, 64, 0, None, 1e-5, G, 0, WS, nb, None) == bl.BL_ERR_UNSUPPORTED
+    H = (bl.Group * 2)()
+    ctypes.memmove(H, G, ctypes.sizeof(H))
+    H[1].Y = Y.value + 64                                                  # over matrix 0's Y
+    assert f(A, 2, 64, 0, None, 1e-5, H, 2, WS, nb, None) == bl.BL_ERR_UNSUPPORTED
+    H[1].Y = A.value                                                       # over X
+    assert f(A, 2, 64, 0, None, 1e-5, H, 2, WS, nb, None) == bl.BL_ERR_UNSUPPORTED
+    H[1].Y = WS.value                                                      # over the workspace rows
+    assert f(A, 2, 64, 0, None, 1e-5, H, 2, WS, nb, None) == bl.BL_ERR_UNSUPPORTED
+    H[1].Y = ctypes.c_void_p(B.value).value                                # over the gain
+    assert f(A, 2, 64, bl.BL_QUANT_RMSNORM, B, 1e-5, H, 2, WS, nb, None) == bl.BL_ERR_UNSUPPORTED
+    assert f(WS, 2, 64, 0, None, 1e-5, G, 2, WS, nb, None) == bl.BL_ERR_UNSUPPORTED  # X over the workspace
+    assert f(A, 0, 64, 0, None, 1e-5, G, 2, None, 0, None) == bl.BL_OK     # no rows: checks only

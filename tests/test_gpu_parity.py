@@ -440,6 +440,61 @@ def test_forward_stationary(M, K, Ns):
         assert_y_close(host(out[i]["y"]), want, f"matrix {i} y")
 
 
+def _quant_grouped_cases():
+    # (M, K, row counts of the matrices, RMSNorm, gain): the launch that
+    # quantises its rows itself (up to 8 tokens, at least 512 tiles of 16
+    # rows, K <= 2560), with and without RMSNorm and gain, K with a partial
+    # last float4 group of the 256-thread quantiser and a partial chunk quad;
+    # then the two-step path (9 tokens, too few tiles, K above 2560)
+    return [(1, 2560, (2560, 6912, 6912), False, False), (8, 2560, (2560, 6912, 6912), False, False),
+            (3, 2560, (2560, 6912, 6912), True, True), (5, 576, (3000, 3001, 2999), True, False),
+            (7, 1088, (4100, 4099), True, True), (2, 64, (8200,), False, False),
+            (9, 2560, (2560, 6912, 6912), True, True), (4, 2560, (640, 640), False, False),
+            (8, 2624, (8200,), True, True)]
+
+
+@pytest.mark.parametrize("M,K,Ns,rms,gain", _quant_grouped_cases())
+def test_quant_forward_grouped(M, K, Ns, rms, gain):
+    """bitlinear_quant_forward_grouped: every output (y, acc, subln requant)
+    bit-identical to bitlinear_quant_act followed by
+    bitlinear_forward_grouped, with ReLU^2, residual, gating product and
+    subln epilogues; the quantised rows themselves against the oracle (R1
+    without RMSNorm, R3 with it)."""
+    log(f"[quant grouped] M={M} K={K} N={Ns} rms={rms} gain={gain}")
+    rng = np.random.default_rng(3500 + M + K + 2 * rms + gain)
+    X = synth.activations(rng, M, K, outliers=True)
+    G = synth.gains(rng, K) if gain else None
+    gdev = None if G is None else dev(G)
+    epis = [{"relu2": True, "subln": True}, {"residual": True}, {"mul": True}, {}]
+    mats = []
+    for i, N in enumerate(Ns):
+        p, s = gpu_pack(synth.weights(rng, N, K))
+        kw = epis[i % len(epis)]
+        d = {"packed": p, "w_scale": s, "want_acc": True, "relu2": kw.get("relu2", False),
+             "subln": kw.get("subln", False) and N % 64 == 0}
+        if d["subln"]:
+            d["norm_gain"] = dev(synth.gains(rng, N))
+        if kw.get("residual"):
+            d["residual"] = dev(synth.activations(rng, M, N))
+        if kw.get("mul"):
+            d["mul_by"] = dev(synth.activations(rng, M, N))
+        mats.append(d)
+    xq, xs, rs = bl.quant_act(dev(X), rmsnorm=rms, norm_gain=gdev)
+    want = bl.forward_grouped(xq, xs, rs, mats)
+    got = bl.quant_forward_grouped(dev(X), mats, rmsnorm=rms, norm_gain=gdev)
+    for i in range(len(Ns)):
+        assert set(got[i]) == set(want[i])
+        for key in want[i]:
+            assert_exact(host(got[i][key]), host(want[i][key]), f"matrix {i} {key}: fused vs two calls")
+    if rms:
+        check_requant(oracle.rmsnorm(X, G), host(xq), host(xs), host(rs), f"quant grouped M={M} K={K}")
+    else:
+        ref_q, ref_s, ref_r = oracle.quant_act(X)
+        assert_exact(host(xq), ref_q, "xq")
+        assert_exact(host(xs), ref_s, "scale")
+        assert_exact(host(rs), ref_r, "rowsum")
+
+
 def test_gemv_row_equals_gemm_row():
     """Token independence across kernels: M=1 (batched kernel, one token tile) equals
     row 0 of M=80 (tiled GEMM)."""
