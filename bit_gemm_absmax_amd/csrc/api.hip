@@ -800,7 +800,7 @@ int scratch_address(void** out) {
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return hip_status(e, "ffn_noalloc: hipGetDevice");
     if (dev < 0 || dev >= kMaxDevices)
-        return fail(BL_ERR_UNSUPPORTED, "ffn_noalloc: device %d beyond the %d this build tracks", dev, kMaxDevices);
+        return fail(BL_ERR_UNSUPPORTED, "ffn_noalloc: device %d beyond the %d devices the library tracks", dev, kMaxDevices);
     std::lock_guard<std::mutex> lock(g_scratch_mu);
     if (g_scratch_ptr[dev] == nullptr) {
         void* p = nullptr;

@@ -79,7 +79,7 @@ enum bl_status {
     BL_ERR_ALIGN = -3,       /* a pointer is not aligned as required */
     BL_ERR_WORKSPACE = -4,   /* workspace missing or smaller than required */
     BL_ERR_HIP = -5,         /* HIP runtime reported an error (launch, device) */
-    BL_ERR_UNSUPPORTED = -6  /* valid request this build does not implement */
+    BL_ERR_UNSUPPORTED = -6  /* valid request the library does not implement */
 };
 
 /* Static description of a status code (never NULL). */
