@@ -29,8 +29,8 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 constexpr int kXcds = 8;
 
 // Pipeline: k advances 128 per stage and NBUF (4) stages ring through LDS,
-// filled by direct global->LDS loads (global_load_lds_dwordx4) issued up to
-// four stages ahead, so L2/HBM latency overlaps the MFMAs.
+// filled by direct buffer->LDS loads (buffer_load_dwordx4 ... lds) issued
+// three stages ahead, so L2/HBM latency overlaps the MFMAs.
 // A DMA instruction writes 64 lanes x 16 bytes contiguously; the global
 // address each lane fetches is chosen so that:
 //   - activations: one instruction covers 8 rows x 128 bytes (whole cache
@@ -40,7 +40,6 @@ constexpr int kXcds = 8;
 //     stage, chunk-major, so a fragment read (word g of 16 rows) is one
 //     contiguous 256-byte span; in the packed layout (16-row tiles, chunk c
 //     of a tile's rows side by side) that is four 256-byte runs in memory.
-// Rows past M or N are clamped to the last row for loading (never stored).
 
 constexpr int kBK = 128;             // k per stage
 
