@@ -823,6 +823,40 @@ def test_forward_shape_sweep(i, M, K, N, epi):
     assert_exact(host(y2), host(out["y"]), "sweep quant_forward vs quant_act + forward")
 
 
+@pytest.mark.parametrize("M,K,N", [(512, 256, 512), (2304, 64, 6912)])
+def test_gemm_whole_tile_epilogues(M, K, N):
+    """The GEMM path's whole tiles store Y through LDS staging; the int32
+    accumulators are not requested here, so that path runs (asking for them
+    takes the element-wise one).  512 x 512 runs 256x160 tiles, the last one
+    partial; 2304 x 6912 runs 256x256 tiles, all whole.  Every epilogue:
+    plain, ReLU^2, residual add and gating product, alone and after ReLU^2;
+    Y within 1e-5 of the oracle."""
+    log(f"[gemm tiles] M={M} K={K} N={N}")
+    rng = np.random.default_rng(7300 + M)
+    X = synth.activations(rng, M, K)
+    W = synth.weights(rng, N, K)
+    A = synth.activations(rng, M, N)
+    p, s, q, gw = check_pack(W, "gemm tiles")
+    xq, xs, rs = bl.quant_act(dev(X))
+    oq, og, _ = oracle.quant_act(X)
+    assert_exact(host(xq), oq, "gemm tiles xq")
+    with oracle.parallel():
+        acc = oracle.int_matmul(oq, q)
+    base = oracle.dequant(acc, og, gw)
+    aux = dev(A)
+    for epi in ("none", "relu2", "residual", "mul", "relu2+residual", "relu2+mul"):
+        relu2 = epi.startswith("relu2")
+        res = aux if "residual" in epi else None
+        mul = aux if "mul" in epi else None
+        out = bl.forward(xq, xs, p, s, x_rowsum=rs, relu2=relu2, residual=res, mul_by=mul)
+        want = oracle.relu2(base.copy()) if relu2 else base.copy()
+        if res is not None:
+            want = oracle.add(A.copy(), want)
+        elif mul is not None:
+            want = oracle.mul(want, A)
+        assert_y_close(host(out["y"]), want, f"gemm tiles {epi}")
+
+
 def _ffn_sweep_cases(n=12, seed=6300):
     rng = np.random.default_rng(seed)
     out = []
