@@ -1194,12 +1194,15 @@ hipError_t go_decode_plan(const Plan& p, const float* X, int64_t M, int64_t K, b
 // longer rows go to the GEMM); token tiles 1, 2 or 4 (M = 33..48 runs a
 // zero tile) with 4, 3 or 2 ring stages (64, 96 or 128 KB of LDS); two
 // column tiles per workgroup once several token tiles share each operand
-// fragment, while that still leaves >= 128 workgroups.
+// fragment, while that still leaves >= 128 workgroups, and four at four
+// token tiles when that still gives every CU a workgroup (one workgroup per
+// CU fits the LDS, so a launch of more takes a second round, whose weight
+// stream starts only when the first round ends).
 static bool batch_shape(int64_t M, int64_t K, int64_t N, int& q, int& mt, int& ct) {
     const int64_t nq = (K / 64 + 3) / 4;
     q = (int)((nq + kBatchWaves - 1) / kBatchWaves);
     mt = M <= 16 ? 1 : M <= 32 ? 2 : 4;
-    ct = (mt >= 2 && (N + 31) / 32 >= 128) ? 2 : 1;
+    ct = (mt == 4 && (N + 63) / 64 >= cu_count()) ? 4 : (mt >= 2 && (N + 31) / 32 >= 128) ? 2 : 1;
     return M >= 1 && M <= 64 && K >= 64 && K <= 8192 && q >= 1 && q <= 8;
 }
 
@@ -1324,6 +1327,7 @@ static hipError_t go_batch_mats(const int8_t* Xq, const float* xs, const int32_t
         case 5: return go_batch_q<2, 2>(q, Xq, xs, rs, M, K, mats, s);
         case 8: return go_batch_q<4, 1>(q, Xq, xs, rs, M, K, mats, s);
         case 9: return go_batch_q<4, 2>(q, Xq, xs, rs, M, K, mats, s);
+        case 11: return go_batch_q<4, 4>(q, Xq, xs, rs, M, K, mats, s);
         default: return hipErrorInvalidValue;
     }
 }

@@ -393,10 +393,13 @@ def _stationary_cases():
     # (M, K, row counts of the matrices): at least 512 tiles of 16 rows, so the
     # launch copies all activations into LDS once per workgroup; ragged N, K
     # with a partial last chunk quad and K % 128 == 64 (unswizzled tail)
-    # (up to 32 tokens); beyond 32 tokens the same calls run k_batch
+    # (up to 32 tokens); beyond 32 tokens the same calls run k_batch, with
+    # four column tiles per workgroup once that still fills every CU (ragged
+    # matrices whose last workgroup has empty column tiles, K = 6912)
     return [(1, 2560, (2560, 6912, 6912)), (5, 576, (3000, 3001, 2999)), (16, 64, (8200,)),
             (17, 1088, (4100, 4099)), (31, 1344, (600, 7700, 5)), (32, 2560, (2560, 6912, 6912)),
-            (33, 2560, (2560, 6912, 6912)), (48, 192, (9000,)), (64, 2560, (2560, 6912, 6912))]
+            (33, 2560, (2560, 6912, 6912)), (48, 192, (9000,)), (64, 2560, (2560, 6912, 6912)),
+            (40, 1088, (4100, 4099, 8200)), (36, 6912, (16400,))]
 
 
 @pytest.mark.parametrize("M,K,Ns", _stationary_cases())
@@ -428,7 +431,8 @@ def test_forward_stationary(M, K, Ns):
     out = bl.forward_grouped(xq, xs, rs, mats) if len(Ns) > 1 else [bl.forward(
         xq, xs, mats[0]["packed"], mats[0]["w_scale"], x_rowsum=rs, want_acc=True, relu2=mats[0]["relu2"])]
     for i, (q, g, A, kw) in enumerate(refs):
-        acc = oracle.int_matmul(rq[0], q)
+        with oracle.parallel():
+            acc = oracle.int_matmul(rq[0], q)
         assert_exact(host(out[i]["acc"]), acc, f"matrix {i} acc")
         want = oracle.dequant(acc, rq[1], g)
         if kw.get("relu2"):
