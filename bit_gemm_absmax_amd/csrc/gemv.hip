@@ -947,7 +947,16 @@ __global__ __launch_bounds__(kStatWaves* kWave) void k_stat(const int8_t* __rest
         wrow_load<NVQ>(r0 < M ? sq.X + (int64_t)r0 * K : nullptr, K, v0);
         wrow_load<NVQ>(r1 < M ? sq.X + (int64_t)r1 * K : nullptr, K, v1);
         const bool has_gain = sq.rms && sq.gain != nullptr;
-        wrow_load<NVQ>(has_gain ? sq.gain : nullptr, K, gv);
+        // without a gain its loads are skipped, not sent out of range: every
+        // load instruction costs the CU's address unit the same time
+        if (has_gain) {
+            wrow_load<NVQ>(sq.gain, K, gv);
+        } else {
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int i = 0; i < NVQ; ++i) gv[u][i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        }
         __builtin_amdgcn_sched_barrier(0);
         stat_load_weights<QMAX>(T.W, T.n0, T.rows, K, C, nq, fr, fg, w);
         __builtin_amdgcn_sched_barrier(0);
@@ -958,9 +967,11 @@ __global__ __launch_bounds__(kStatWaves* kWave) void k_stat(const int8_t* __rest
         // overlaps the activation copy
         stat_load_weights<QMAX>(T.W, T.n0, T.rows, K, C, nq, fr, fg, w);
 
-        // ---- the activation copy: MT * 16 rows (rows past M read zeros)
+        // ---- the activation copy: MT * 16 rows (rows past M read zeros); one
+        // token tile copies only the instructions that hold rows below M (the
+        // rest of the tile is never stored from)
         const Rsrc rx = make_rsrc(Xq, (uint32_t)M * (uint32_t)K);
-        const int ninst = MT * 16 * K / 1024;
+        const int ninst = MT == 1 ? (M * K + 1023) / 1024 : MT * 16 * K / 1024;
         for (int i = wave; i < ninst; i += kStatWaves) {
             const uint32_t o = 1024u * (uint32_t)i + 16u * (uint32_t)lane;
             // r = o / K by a multiply-high with ceil(2^32 / K), then one correction
