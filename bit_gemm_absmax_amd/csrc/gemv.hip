@@ -412,8 +412,8 @@ __device__ __forceinline__ void wait_vm_n(int n) {
 // in the issue order of batch_body: (DMAs of quad j, weights of quad j) for
 // j < NS - 1, then the remaining weights; iteration j of the loop then adds
 // the DMAs of quad j + NS - 1.
-constexpr int batch_loads_after(int i, int Q, int NS, int MT, int CT) {
-    const int dma = 4 * MT;
+constexpr int batch_loads_after(int i, int Q, int NS, int MT, int CT, bool H8) {
+    const int dma = H8 ? 2 : 4 * MT;
     if (i <= NS - 2) {
         const int last_pro = NS - 2 < Q - 1 ? NS - 2 : Q - 1;
         const int rest = Q - (NS - 1) > 0 ? Q - (NS - 1) : 0;
@@ -423,7 +423,10 @@ constexpr int batch_loads_after(int i, int Q, int NS, int MT, int CT) {
     return (hi - i) * dma;
 }
 
-template <int MT, int CT, int NS, int Q>
+// H8 (one token tile, M <= 8): only the tile's first 8 rows are moved; the
+// other half of each stage is never written, and the operands read from it
+// feed only outputs of rows past M, which are never stored.
+template <int MT, int CT, int NS, int Q, bool H8>
 __device__ __forceinline__ void batch_body(Rsrc ra, const uint32_t (&voff)[MT][2], const Rsrc (&rw)[CT],
                                            const int (&rows)[CT], int wave, int fr, int fg, int C, int nq,
                                            int8_t* ring, const uint32_t (&rd)[4], v4i (&acc)[CT][MT]) {
@@ -444,7 +447,8 @@ __device__ __forceinline__ void batch_body(Rsrc ra, const uint32_t (&voff)[MT][2
         int8_t* st_ = ring + ((ii) % NS) * SB;                                                            \
         _Pragma("unroll") for (int t = 0; t < MT; ++t)                                                    \
         _Pragma("unroll") for (int j = 0; j < 4; ++j)                                                     \
-            dma16(ra, (lds_ptr)(st_ + t * kTileBytes + j * 1024), voff[t][j & 1], k0 + 128u * (uint32_t)(j >> 1)); \
+            if (!H8 || (j & 1) == 0)                                                                      \
+                dma16(ra, (lds_ptr)(st_ + t * kTileBytes + j * 1024), voff[t][j & 1], k0 + 128u * (uint32_t)(j >> 1)); \
     } while (0)
     // issue order (pinned: the waits below count loads): each of the first
     // NS - 1 quads' DMAs then its weights, then the other weights.  Loads
@@ -465,7 +469,7 @@ __device__ __forceinline__ void batch_body(Rsrc ra, const uint32_t (&voff)[MT][2
 #pragma unroll
     for (int i = 0; i < Q; ++i) {
         // quad i's activations have landed once only later loads are in flight
-        wait_vm_n(batch_loads_after(i, Q, NS, MT, CT));
+        wait_vm_n(batch_loads_after(i, Q, NS, MT, CT, H8));
         __builtin_amdgcn_sched_barrier(0);
         // all of quad i's operand fragments, then the DMA that refills the
         // stage read one step earlier (with every read in flight issued
@@ -517,7 +521,7 @@ struct BatchMats {
 // GATED (CT = 2, one matrix): the two column tiles are the same 16 output
 // rows of the up matrix (tile 0) and of the gate matrix Wg (tile 1), sharing
 // every activation fragment, and the output is ReLU^2(gate) * up.
-template <int MT, int CT, int NS, int QMAX, bool GATED = false>
+template <int MT, int CT, int NS, int QMAX, bool GATED = false, bool H8 = false>
 __global__ __launch_bounds__(kBatchWaves* kWave) void k_batch(const int8_t* __restrict__ Xq,
                                                                const float* __restrict__ x_scale,
                                                                const int32_t* __restrict__ x_rowsum, int M, int K,
@@ -525,6 +529,7 @@ __global__ __launch_bounds__(kBatchWaves* kWave) void k_batch(const int8_t* __re
                                                                const uint8_t* __restrict__ Wg,
                                                                const float* __restrict__ g_scale) {
     static_assert(!GATED || CT == 2, "a gated tile pairs one up and one gate tile");
+    static_assert(!H8 || MT == 1, "the half-tile copy is for one token tile");
     constexpr int NWV = kBatchWaves;
     constexpr int NT = NWV * kWave;
     constexpr int COLS = 16 * CT;                        // accumulated columns per workgroup
@@ -631,7 +636,7 @@ __global__ __launch_bounds__(kBatchWaves* kWave) void k_batch(const int8_t* __re
     for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
         for (int t = 0; t < MT; ++t) acc[ct][t] = v4i{0, 0, 0, 0};
-    batch_body<MT, CT, NS, QMAX>(ra, voff, rw, rows, wave, fr, fg, C, nq, ring, rd, acc);
+    batch_body<MT, CT, NS, QMAX, H8>(ra, voff, rw, rows, wave, fr, fg, C, nq, ring, rd, acc);
 
     // ---- per-wave partial tiles -> LDS (over the rings, once every wave is
     // done with its own) -> sum over the waves in index order
@@ -1236,8 +1241,12 @@ static hipError_t go_batch(const int8_t* Xq, const float* xs, const int32_t* rs,
         mats.m[i].wg0 = (int)blocks;
         blocks += (mats.m[i].N + cols - 1) / cols;
     }
-    hipLaunchKernelGGL((k_batch<MT, CT, NS, Q, G>), dim3((unsigned)blocks), dim3(kBatchWaves * kWave), 0, s, Xq, xs,
-                       rs, (int)M, (int)K, mats, gate, gate_scale);
+    if (MT == 1 && M <= 8)  // half the token tile: half the activation copy
+        hipLaunchKernelGGL((k_batch<MT, CT, NS, Q, G, MT == 1>), dim3((unsigned)blocks), dim3(kBatchWaves * kWave), 0,
+                           s, Xq, xs, rs, (int)M, (int)K, mats, gate, gate_scale);
+    else
+        hipLaunchKernelGGL((k_batch<MT, CT, NS, Q, G, false>), dim3((unsigned)blocks), dim3(kBatchWaves * kWave), 0,
+                           s, Xq, xs, rs, (int)M, (int)K, mats, gate, gate_scale);
     return hipGetLastError();
 }
 
