@@ -205,9 +205,12 @@ def run_forward(X, W, **kw):
     return out, ref, (xq, xs, rs, p, s, q, g)
 
 
-@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 8, 17, 40, 64, 65, 130])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 8, 9, 16, 17, 40, 64, 65, 130])
 @pytest.mark.parametrize("K,N", [(256, 512), (192, 100), (2560, 200), (6912, 72), (64, 96), (128, 130), (320, 160)])
 def test_forward_small(M, K, N):
+    """One BitLinear from int8 rows against the oracle: up to 8 tokens the
+    batched kernel copies half its token tile, 9..16 the whole tile, then
+    two and four token tiles, and the GEMM beyond 64 tokens."""
     log(f"[forward] M={M} K={K} N={N}")
     rng = np.random.default_rng(M * 31 + K + N)
     X = synth.activations(rng, M, K, outliers=True)
