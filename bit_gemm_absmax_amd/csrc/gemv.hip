@@ -977,6 +977,10 @@ __global__ __launch_bounds__(kStatWaves* kWave) void k_stat(const int8_t* __rest
         // rest of the tile is never stored from)
         const Rsrc rx = make_rsrc(Xq, (uint32_t)M * (uint32_t)K);
         const int ninst = MT == 1 ? (M * K + 1023) / 1024 : MT * 16 * K / 1024;
+        // (rows of whole groups of 16 chunks, as at K = 2560, take the swizzle
+        // without the per-lane test for a partial last group)
+        const bool whole16 = (nch & 15u) == 0u;
+#pragma unroll 4
         for (int i = wave; i < ninst; i += kStatWaves) {
             const uint32_t o = 1024u * (uint32_t)i + 16u * (uint32_t)lane;
             // r = o / K by a multiply-high with ceil(2^32 / K), then one correction
@@ -985,7 +989,8 @@ __global__ __launch_bounds__(kStatWaves* kWave) void k_stat(const int8_t* __rest
             if ((r + 1u) * (uint32_t)K <= o) ++r;
             const uint32_t j = (o - r * (uint32_t)K) / 16u;
             // the global chunk held by this LDS slot: the swizzle is its own inverse
-            dma16(rx, (lds_ptr)(act + 1024 * i), stat_slot(r, j, (uint32_t)K, nch), 0u);
+            const uint32_t src = whole16 ? r * (uint32_t)K + 16u * (j ^ (r & 15u)) : stat_slot(r, j, (uint32_t)K, nch);
+            dma16(rx, (lds_ptr)(act + 1024 * i), src, 0u);
         }
 
         // ---- the rows' scales and sums for this lane's outputs: acc[t][q] is
