@@ -504,7 +504,11 @@ int bitlinear_quant_forward_grouped(const float* X, int64_t M, int64_t K, uint32
     const bool rms = (quant_flags & BL_QUANT_RMSNORM) != 0;
     bl::GroupMat mats[BL_MAX_GROUPS];
     group_mats(groups, n_groups, mats);
-    if (bl::gemv_grouped_quant_supported(M, K, mats, n_groups)) {
+    // the one launch also needs every matrix within the skinny kernels' 32-bit
+    // output offsets (M * N < 2^29), as run_grouped's single launch does
+    bool fused = bl::gemv_grouped_quant_supported(M, K, mats, n_groups);
+    for (int32_t g = 0; g < n_groups; ++g) fused = fused && bl::gemv_supported(M, K, mats[g].N);
+    if (fused) {
         hipError_t e = bl::launch_gemv_grouped_quant(X, M, K, rms, rms ? norm_gain : nullptr, norm_eps, mats,
                                                      n_groups, stream);
         if (e != hipSuccess) return hip_status(e, "quant_forward_grouped: contraction");

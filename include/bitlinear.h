@@ -225,7 +225,8 @@ int bitlinear_forward(const int8_t* Xq, const float* x_scale,
  * one input, e.g. the attention block's q, k and v projections, whose
  * absmean scales are per tensor; "BitNetConfig": 20 heads, 5 key/value
  * heads).  Results are identical to one bitlinear_forward per matrix; for
- * M <= 64 and K <= 8192 the contractions of all matrices stream in one launch.
+ * M <= 64, K <= 8192 and M * N < 2^29 for every matrix the contractions of
+ * all matrices stream in one launch.
  *
  * Xq, x_scale, M, K   as in bitlinear_forward
  * x_rowsum   in  int32 [M], required here
@@ -286,7 +287,8 @@ int bitlinear_quant_forward(const float* X, int64_t M, int64_t K, uint32_t quant
  * Grouped fused quantise + BitLinear: bitlinear_quant_act followed by
  * bitlinear_forward_grouped on the quantised rows, with the same results
  * bit for bit.  For a few tokens (M <= 8) against many 16-row tiles in all
- * (at least 512, K <= 2560) it is one contraction launch in which every
+ * (at least 512, K <= 2560, M * N < 2^29 for every matrix) it is one
+ * contraction launch in which every
  * workgroup quantises the rows itself, exactly as the standalone quantiser
  * would; otherwise the rows are quantised into the workspace first.
  *

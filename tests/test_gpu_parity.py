@@ -161,7 +161,9 @@ def test_inplace_quant_forward_rejected():
 @pytest.mark.parametrize("M,K,rms,gain", [(4, 256, False, False), (1, 2560, False, False),
                                           (37, 6912, True, True), (3, 16384, True, False),
                                           (5, 64, False, False), (9, 2560, True, False),
-                                          (2, 8192, True, True), (2, 8256, False, False)])
+                                          (2, 8192, True, True), (2, 8256, False, False),
+                                          (2, 16448, True, False), (2, 32768, False, False),
+                                          (3, 32768, True, True)])
 def test_quant(M, K, rms, gain):
     log(f"[quant] M={M} K={K} rms={rms} gain={gain}")
     rng = np.random.default_rng(M * 1000 + K)
@@ -309,9 +311,12 @@ def test_forward_subln_requant(M, with_gain):
 @pytest.mark.parametrize("K,N,rms,gain,relu2,res", [(2560, 6912, False, False, True, False),
                                                      (6912, 2560, True, True, False, True),
                                                      (256, 512, True, False, False, False),
-                                                     (640, 37, False, False, True, True)])
+                                                     (640, 37, False, False, True, True),
+                                                     (32768, 96, True, True, True, True)])
 def test_quant_forward(M, K, N, rms, gain, relu2, res):
-    """Fused quantise + BitLinear (one launch for M <= 4) against the oracle."""
+    """Fused quantise + BitLinear (one launch for M <= 4) against the oracle;
+    at the widest supported row (K = 32768) the quantiser runs 1024 threads
+    per row and the contraction goes to the GEMM whatever M."""
     log(f"[quant_forward] M={M} K={K} N={N} rms={rms} gain={gain} relu2={relu2} res={res}")
     rng = np.random.default_rng(M * 7 + K + N)
     X = synth.activations(rng, M, K, outliers=True)
@@ -611,6 +616,24 @@ def test_ffn_block_small(M):
     # free running against the oracle stack (information, loose bound)
     ref = oracle.ffn_stack(h0, ol)
     assert np.abs(host(hs) - ref).max() <= 1e-3 * np.abs(ref).max()
+
+
+@pytest.mark.parametrize("M,H,F", [(1, 256, 32768), (5, 32768, 256), (70, 128, 32768)])
+def test_ffn_max_width(M, H, F):
+    """FFN layers at the widest supported rows (32768): the 1024-thread
+    quantiser on the intermediate row (subln) or on the hidden row (pre-norm),
+    the down projection's K = 32768 or its 32768 outputs, checked stage by
+    stage against the oracle; the stack call equals the staged calls."""
+    log(f"[ffn max width] M={M} H={H} F={F}")
+    rng = np.random.default_rng(980 + M)
+    gl, ol = to_gpu_layers(ffn_layers_np(rng, 2, H, F, gains=True))
+    h0 = synth.activations(rng, M, H, outliers=True)
+    h = h0
+    for l in range(2):
+        h, _ = layer_teacher_forced(h, gl[l], ol[l], M)
+    hs = dev(h0)
+    bl.FFNStack(gl, H, F, M, DEV)(hs)
+    assert_exact(host(hs), h, "ffn max width: stack vs staged calls")
 
 
 def test_ffn_no_prenorm_no_residual():
