@@ -50,10 +50,14 @@ def log(*a):
 
 
 def src_hash(*names):
+    """Hash of the kernel sources and of the compiler flags they are built
+    with (include paths left out: they differ between checkouts)."""
+    from bit_gemm_absmax_amd import build as _build
     h = hashlib.sha256()
     for n in names:
         with open(os.path.join(ROOT, "bit_gemm_absmax_amd", "csrc", n), "rb") as f:
             h.update(f.read())
+    h.update(" ".join(f for f in _build.FLAGS if not f.startswith("-I")).encode())
     return h.hexdigest()[:16]
 
 
@@ -67,8 +71,8 @@ DURATION_KERNELS = {
 }
 
 
-PROFILE_CMD = ("rocprofv3 --kernel-trace --stats -d {dir} -o bench -- python3 bench.py --steps 300 --warmup 20 "
-               "--no-cpu --no-shapes")
+PROFILE_CMD = ("rocprofv3 --kernel-trace --stats --output-format csv -d {dir} -o bench -- python3 bench.py "
+               "--steps 300 --warmup 20 --no-cpu --no-shapes")
 
 
 def durations_from(trace_dir):

@@ -31,11 +31,17 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # -ffp-contract=off: epilogue arithmetic must be separate IEEE operations.
 # -fhip-fp32-correctly-rounded-divide-sqrt: 127/gamma and W/gamma are IEEE divides.
 # -packed-fp32-ops: keep the compiler from emitting packed fp32 VALU ops.
+# -amdgpu-kernarg-preload-count: the first kernel arguments (as many as the
+#   free user SGPRs hold, 32 bytes here) are preloaded into SGPRs at wave
+#   launch, so a kernel's first loads need not wait for an argument fetch;
+#   firmware without the feature runs the compiler's fallback block that
+#   loads them as before.  Decode step at M=1 8.20 -> 7.67 us.
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     "-ffp-contract=off", "-fhip-fp32-correctly-rounded-divide-sqrt",
     "-fno-gpu-flush-denormals-to-zero",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
     "-Wall", "-Wno-unused-command-line-argument",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
