@@ -1190,6 +1190,24 @@ def test_ffn_persistent_small(H, F, L, pre, residual):
     assert_exact(host(ref), hs, "two launches per layer vs staged calls")
 
 
+def test_ffn_persistent_chunked():
+    """More layers than one persistent launch takes (48): the stack runs as
+    consecutive launches, each starting from the hidden state the previous one
+    stored, bit-identical to two launches per layer, on two calls in a row."""
+    log("[persistent] 50 layers (two launches)")
+    rng = np.random.default_rng(5300)
+    H, F, L = 256, 640, 50
+    gl, _ = to_gpu_layers(ffn_layers_np(rng, L, H, F, gains=True))
+    h0 = synth.activations(rng, 1, H, outliers=True)
+    ref = dev(h0)
+    bl.FFNStack(gl, H, F, 1, DEV)(ref)
+    stack = bl.FFNStack(gl, H, F, 1, DEV, persistent=True)
+    for rep in range(2):
+        h = dev(h0)
+        stack(h)
+        assert_exact(host(h), host(ref), f"persistent 50-layer stack vs two launches per layer (call {rep})")
+
+
 def test_ffn_persistent_model_stack():
     """The 30-layer stack at hidden 2560 / intermediate 6912 (seed 4) at one
     token through the persistent launch: bit-identical to the two-launch path

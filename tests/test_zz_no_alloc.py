@@ -42,20 +42,20 @@ def stream():
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
-def with_workspace(lib, arr, n, h):
+def with_workspace(lib, arr, n, h, flags=FLAGS):
     M = h.shape[0]
     nb = lib.bitnet_ffn_workspace_bytes(M, H, F)
     ws = torch.empty(nb, dtype=torch.uint8, device=DEV)
-    rc = lib.bitnet_ffn_forward(arr, n, ctypes.c_void_p(h.data_ptr()), M, H, F, FLAGS, 1e-5,
+    rc = lib.bitnet_ffn_forward(arr, n, ctypes.c_void_p(h.data_ptr()), M, H, F, flags, 1e-5,
                                 ctypes.c_void_p(ws.data_ptr()), nb, stream())
     assert rc == bl.BL_OK, lib.bitlinear_last_error()
     torch.cuda.synchronize()
     del ws
 
 
-def no_alloc(lib, arr, n, h):
+def no_alloc(lib, arr, n, h, flags=FLAGS):
     M = h.shape[0]
-    rc = lib.bitnet_ffn_forward_noalloc(arr, n, ctypes.c_void_p(h.data_ptr()), M, H, F, FLAGS, 1e-5, stream())
+    rc = lib.bitnet_ffn_forward_noalloc(arr, n, ctypes.c_void_p(h.data_ptr()), M, H, F, flags, 1e-5, stream())
     assert rc == bl.BL_OK, lib.bitlinear_last_error()
     torch.cuda.synchronize()
 
@@ -73,6 +73,25 @@ def test_noalloc_equals_workspace_entry(gated):
         with_workspace(lib, arr, len(layers), a)
         no_alloc(lib, arr, len(layers), b)
         assert torch.equal(a, b), f"M={M}: no-alloc entry differs from the workspace entry"
+        assert not torch.equal(b, h0)
+
+
+def test_noalloc_persistent_equals_workspace_entry():
+    """With BL_FFN_PERSISTENT (one token, every layer in one launch, its
+    descriptors and ready flags in the scratch): the no-alloc entry gives the
+    workspace entry's hidden state on two calls in a row."""
+    lib = bl.load()
+    rng = np.random.default_rng(8300)
+    layers = gpu_layers(rng, 3, False)
+    arr = bl.make_layers(layers, H, F)
+    flags = FLAGS | bl.BL_FFN_PERSISTENT
+    for rep in range(2):
+        print(f"[no-alloc] persistent call {rep}", flush=True)
+        h0 = torch.from_numpy(synth.activations(rng, 1, H, outliers=True)).to(DEV)
+        a, b = h0.clone(), h0.clone()
+        with_workspace(lib, arr, len(layers), a, flags)
+        no_alloc(lib, arr, len(layers), b, flags)
+        assert torch.equal(a, b), f"call {rep}: persistent no-alloc entry differs from the workspace entry"
         assert not torch.equal(b, h0)
 
 
